@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each pin is chosen so that a plausible slip in the oracle -- a dropped term, a
+wrong sign, an exchanged index or stride, a transposed operand, a wrong
+rounding rule -- fails at least one of them; ``test_pins_catch_planted_mistakes``
+plants such slips on the CPU and shows they are caught.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import bits, draw
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f64(bits_arr):
+    return oracle.bf16_bits_to_f64_array(bits_arr)
+
+
+def _bf16_bits_of(values):
+    """Exact bf16 bits of values that are representable in bf16 (checked)."""
+    t = torch.tensor(np.asarray(values, dtype=np.float32)).to(torch.bfloat16)
+    b = bits(t)
+    assert np.array_equal(_f64(b), np.asarray(values, dtype=np.float64)), "value not exact in bf16"
+    return b
+
+
+def _rowmajor_gemm(A_bits, B_bits, M, N, K, want_T=True):
+    C, T = oracle.gemm(A_bits, B_bits, 1, M, N, K, (K, 1, 0), (N, 1, 0), want_T=want_T)
+    return C[0], (T[0] if want_T else None)
+
+
+# ------------------------------------------------------------------ bf16 --
+
+def _read_pairs(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                a, b = line.split()
+                rows.append((a, b))
+    return rows
+
+
+def test_bf16_decode_golden():
+    for hexbits, expr in _read_pairs("bf16_decode.txt"):
+        want = float(eval(expr, {"__builtins__": {}}))
+        got = oracle.bf16_to_f64(int(hexbits, 16))
+        assert got == want and np.signbit(got) == np.signbit(want), (hexbits, got, want)
+
+
+def test_bf16_rne_golden():
+    for expr, hexbits in _read_pairs("bf16_rne.txt"):
+        x = float(eval(expr, {"__builtins__": {}}))
+        assert oracle.f64_to_bf16_rne(x) == int(hexbits, 16), (expr, hex(oracle.f64_to_bf16_rne(x)))
+
+
+def test_bf16_rne_matches_torch_conversion():
+    # torch's float32 -> bfloat16 cast is an independent round-to-nearest-even.
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(20000, generator=g) * torch.exp2(torch.randint(-20, 20, (20000,), generator=g).float())
+    # plant exact ties: bf16 value plus half an ulp
+    ties = (torch.randn(2000, generator=g).to(torch.bfloat16).float())
+    ties = ties + ties.abs() * 2.0 ** -8
+    x = torch.cat([x, ties])
+    want = bits(x.to(torch.bfloat16))
+    got = np.array([oracle.f64_to_bf16_rne(float(v)) for v in x.tolist()], dtype=np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_decode_vector_matches_scalar():
+    b = np.arange(0, 65536, 97, dtype=np.uint16)
+    b = b[((b >> 7) & 0xFF) != 0xFF]  # finite only
+    vec = _f64(b)
+    sca = np.array([oracle.bf16_to_f64(int(v)) for v in b])
+    assert np.array_equal(vec, sca)
+
+
+# ------------------------------------------------------- hand-worked GEMM --
+
+def _read_gemm_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "gemm_hand.txt")) as f:
+        lines = [l.strip() for l in f if l.strip() and not l.startswith("#")]
+    i = 0
+    while i < len(lines):
+        _, name, M, N, K = lines[i].split()
+        M, N, K = int(M), int(N), int(K)
+        i += 1
+        def take(r):
+            nonlocal i
+            m = np.array([[float(x) for x in lines[i + t].split()] for t in range(r)])
+            i += r
+            return m
+        A, B, C, T = take(M), take(K), take(M), take(M)
+        cases.append((name, A, B, C, T))
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_gemm_cases(), ids=lambda c: c[0])
+def test_gemm_hand_worked(case):
+    name, A, B, C, T = case
+    M, K = A.shape
+    N = B.shape[1]
+    Cg, Tg = _rowmajor_gemm(_bf16_bits_of(A), _bf16_bits_of(B), M, N, K)
+    assert np.array_equal(Cg, C) and np.array_equal(Tg, T)
+
+
+def test_sscore_hand_worked():
+    with open(os.path.join(GOLDEN, "sscore_hand.txt")) as f:
+        lines = [l.strip() for l in f if l.strip() and not l.startswith("#")]
+    blocks, cur = {}, None
+    for l in lines:
+        if l in ("Q", "K", "S", "T"):
+            cur = l
+            blocks[cur] = []
+        else:
+            blocks[cur].append([float(x) for x in l.split()])
+    Q, Kt, S, T = (np.array(blocks[k]) for k in "QKST")
+    Lq, d = Q.shape
+    Lk = Kt.shape[0]
+    Sg, Tg = oracle.sscore(_bf16_bits_of(Q), _bf16_bits_of(Kt), 1, Lq, Lk, d, (d, 1, Lq * d), (d, 1, Lk * d))
+    assert np.array_equal(Sg[0], S) and np.array_equal(Tg[0], T)
+
+
+# --------------------------------------------------------------- closed forms --
+
+@pytest.mark.parametrize("M,N", [(16, 7), (64, 64), (33, 100)])
+def test_identity_A_gives_B(M, N):
+    K = M
+    eye = _bf16_bits_of(np.eye(M))
+    B = bits(draw((K, N), "normal", 0, 1, 11))
+    C, T = _rowmajor_gemm(eye, B, M, N, K)
+    assert np.array_equal(C, _f64(B))
+    assert np.array_equal(T, np.abs(_f64(B)))
+
+
+@pytest.mark.parametrize("M,K", [(9, 16), (64, 64), (100, 33)])
+def test_identity_B_gives_A(M, K):
+    N = K
+    A = bits(draw((M, K), "uniform", -1, 1, 12))
+    C, _ = _rowmajor_gemm(A, _bf16_bits_of(np.eye(K)), M, N, K)
+    assert np.array_equal(C, _f64(A))
+
+
+@pytest.mark.parametrize("K", [1, 128, 512, 2048])
+def test_all_ones_gives_K(K):
+    M, N = 5, 6
+    C, T = _rowmajor_gemm(_bf16_bits_of(np.ones((M, K))), _bf16_bits_of(np.ones((K, N))), M, N, K)
+    assert np.all(C == K) and np.all(T == K)
+
+
+def test_rank1_closed_form():
+    M, N, K = 12, 10, 64
+    alpha = 2.0 ** np.arange(-3, M - 3)
+    beta = -(2.0 ** np.arange(-2, N - 2))
+    A = np.repeat(alpha[:, None], K, axis=1)
+    B = np.repeat(beta[None, :], K, axis=0)
+    C, T = _rowmajor_gemm(_bf16_bits_of(A), _bf16_bits_of(B), M, N, K)
+    assert np.array_equal(C, K * np.outer(alpha, beta))
+    assert np.array_equal(T, K * np.abs(np.outer(alpha, beta)))
+
+
+def test_integer_data_is_exact_against_integer_matmul():
+    # integer entries in [-4, 4]: every partial sum is an exact integer, so the
+    # oracle must equal numpy's int64 matmul (an independent exact routine).
+    M, N, K = 37, 29, 300
+    Ai = draw((M, K), "int", -4, 4, 21)
+    Bi = draw((K, N), "int", -4, 4, 22)
+    C, T = _rowmajor_gemm(bits(Ai), bits(Bi), M, N, K)
+    a = Ai.float().numpy().astype(np.int64)
+    b = Bi.float().numpy().astype(np.int64)
+    assert np.array_equal(C, (a @ b).astype(np.float64))
+    assert np.array_equal(T, (np.abs(a) @ np.abs(b)).astype(np.float64))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 16, 33])
+@pytest.mark.parametrize("N", [1, 3, 16, 33])
+@pytest.mark.parametrize("K", [1, 2, 7, 33])
+def test_brute_force_tiny_vs_numpy(M, N, K):
+    A = bits(draw((M, K), "normal", 0, 1, 1000 + M * 100 + K))
+    B = bits(draw((K, N), "uniform", -1, 1, 2000 + N * 100 + K))
+    C, T = _rowmajor_gemm(A, B, M, N, K)
+    a, b = _f64(A).reshape(M, K), _f64(B).reshape(K, N)
+    ref = a @ b                     # numpy float64 matmul: independent library routine
+    refT = np.abs(a) @ np.abs(b)
+    assert np.all(np.abs(C - ref) <= 1e-12 * refT + 1e-300)
+    assert np.all(np.abs(T - refT) <= 1e-12 * refT + 1e-300)
+
+
+def test_bilinearity():
+    M, N, K = 20, 24, 96
+    A1 = draw((M, K), "int", -3, 3, 31)
+    A2 = draw((M, K), "int", -3, 3, 32)
+    B = bits(draw((K, N), "normal", 0, 1, 33))
+    Asum = (A1.float() + A2.float()).to(torch.bfloat16)  # exact: small integers
+    C1, _ = _rowmajor_gemm(bits(A1), B, M, N, K)
+    C2, _ = _rowmajor_gemm(bits(A2), B, M, N, K)
+    Cs, Ts = _rowmajor_gemm(bits(Asum), B, M, N, K)
+    assert np.all(np.abs(Cs - (C1 + C2)) <= 1e-13 * (Ts + 1))
+
+
+def test_magnitude_sum_bounds_result():
+    M, N, K = 31, 17, 257
+    A = bits(draw((M, K), "normal", 0, 1, 41))
+    B = bits(draw((K, N), "normal", 0, 1, 42))
+    C, T = _rowmajor_gemm(A, B, M, N, K)
+    assert np.all(np.abs(C) <= T)
+    assert np.all(T > 0)
+
+
+# ------------------------------------------------------------------- layouts --
+
+def test_column_major_A_equals_materialized():
+    M, N, K = 48, 40, 72
+    At = draw((K, M), "uniform", -0.5, 0.5, 51)       # storage of a column-major A
+    B = bits(draw((K, N), "uniform", -0.5, 0.5, 52))
+    C_col, T_col = oracle.gemm(bits(At), B, 1, M, N, K, (1, M, 0), (N, 1, 0))
+    A_mat = bits(At.t().contiguous())
+    C_row, T_row = oracle.gemm(A_mat, B, 1, M, N, K, (K, 1, 0), (N, 1, 0))
+    assert np.array_equal(C_col, C_row) and np.array_equal(T_col, T_row)
+
+
+def test_k_major_B_equals_materialized():
+    M, N, K = 30, 50, 64
+    A = bits(draw((M, K), "normal", 0, 1, 61))
+    Bt = draw((N, K), "normal", 0, 1, 62)             # B[k, j] stored at j*K + k
+    C_t, _ = oracle.gemm(A, bits(Bt), 1, M, N, K, (K, 1, 0), (1, K, 0))
+    C_r, _ = oracle.gemm(A, bits(Bt.t().contiguous()), 1, M, N, K, (K, 1, 0), (N, 1, 0))
+    assert np.array_equal(C_t, C_r)
+
+
+def test_sscore_equals_gemm_with_materialized_transpose():
+    b, Lq, Lk, d = 3, 20, 24, 32
+    Q = draw((b, Lq, d), "normal", 0, 1, 71)
+    Kt = draw((b, Lk, d), "normal", 0, 1, 72)
+    S, T = oracle.sscore(bits(Q), bits(Kt), b, Lq, Lk, d, (d, 1, Lq * d), (d, 1, Lk * d))
+    KT = Kt.transpose(1, 2).contiguous()               # [b, d, Lk]
+    C, Tc = oracle.gemm(bits(Q), bits(KT), b, Lq, Lk, d, (d, 1, Lq * d), (Lk, 1, d * Lk))
+    assert np.array_equal(S, C) and np.array_equal(T, Tc)
+
+
+def test_sscore_symmetric_when_Q_equals_K():
+    b, L, d = 2, 33, 64
+    Q = bits(draw((b, L, d), "normal", 0, 1, 81))
+    S, _ = oracle.sscore(Q, Q, b, L, L, d, (d, 1, L * d), (d, 1, L * d))
+    assert np.array_equal(S, np.transpose(S, (0, 2, 1)))
+
+
+def test_batch_stride_zero_broadcasts():
+    b, M, N, K = 3, 8, 9, 16
+    A = draw((b, M, K), "normal", 0, 1, 91)
+    B = bits(draw((K, N), "normal", 0, 1, 92))
+    C, _ = oracle.gemm(bits(A), B, b, M, N, K, (K, 1, M * K), (N, 1, 0))
+    for i in range(b):
+        Ci, _ = oracle.gemm(bits(A[i].contiguous()), B, 1, M, N, K, (K, 1, 0), (N, 1, 0))
+        assert np.array_equal(C[i], Ci[0])
+
+
+def test_points_equal_full_product():
+    b, M, N, K = 2, 40, 36, 80
+    A = draw((b, M, K), "normal", 0, 1, 101)
+    B = draw((b, K, N), "normal", 0, 1, 102)
+    sa, sb = (K, 1, M * K), (N, 1, K * N)
+    C, T = oracle.gemm(bits(A), bits(B), b, M, N, K, sa, sb)
+    rng = np.random.default_rng(0)
+    pts = np.stack([rng.integers(0, b, 200), rng.integers(0, M, 200), rng.integers(0, N, 200)], 1)
+    Cp, Tp = oracle.gemm_points(bits(A), bits(B), pts, K, sa, sb, dims=(b, M, N))
+    assert np.array_equal(Cp, C[pts[:, 0], pts[:, 1], pts[:, 2]])
+    assert np.array_equal(Tp, T[pts[:, 0], pts[:, 1], pts[:, 2]])
+    Q = draw((b, M, K), "normal", 0, 1, 103)
+    Kt = draw((b, N, K), "normal", 0, 1, 104)
+    S, _ = oracle.sscore(bits(Q), bits(Kt), b, M, N, K, (K, 1, M * K), (K, 1, N * K))
+    Sp, _ = oracle.sscore_points(bits(Q), bits(Kt), pts, K, (K, 1, M * K), (K, 1, N * K))
+    assert np.array_equal(Sp, S[pts[:, 0], pts[:, 1], pts[:, 2]])
+
+
+def test_threads_do_not_change_result():
+    M, N, K = 50, 30, 100
+    A = bits(draw((M, K), "normal", 0, 1, 111))
+    B = bits(draw((K, N), "normal", 0, 1, 112))
+    C1, T1 = oracle.gemm(A, B, 1, M, N, K, (K, 1, 0), (N, 1, 0), nthreads=1)
+    C7, T7 = oracle.gemm(A, B, 1, M, N, K, (K, 1, 0), (N, 1, 0), nthreads=7)
+    assert np.array_equal(C1, C7) and np.array_equal(T1, T7)
+
+
+def test_view_outside_buffer_rejected():
+    A = np.zeros(10, dtype=np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm(A, A, 1, 4, 4, 4, (4, 1, 0), (4, 1, 0))
+
+
+# ---------------------------------------------------------------- tolerance --
+
+def test_check_accepts_and_rejects():
+    ref = np.array([1.0, -2.0, 0.0, 5.0])
+    T = np.array([10.0, 2.0, 0.0, 5.0])
+    bound = 1e-3 * T + 1e-5
+    ok = ref + 0.99 * bound
+    assert oracle.check(ok, ref, T)[0] == 0
+    bad = ref.copy()
+    bad[1] += 1.01 * bound[1]
+    assert oracle.check(bad, ref, T)[0] == 1
+    nan = ref.copy()
+    nan[2] = np.nan
+    assert oracle.check(nan, ref, T)[0] == 1
+    inf = ref.copy()
+    inf[3] = np.inf
+    assert oracle.check(inf, ref, T)[0] == 1
+
+
+# ----------------------------------------------------- tile fan-out bench --
+
+def test_tilecast_accounting_matches_printed_run():
+    with open(os.path.join(GOLDEN, "tilecast_accounting.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for consumers, iters, tile_bytes, group, expected in rows:
+        consumers, iters, tile_bytes, group = int(consumers), int(iters), int(tile_bytes), int(group)
+        # one fetch per group of `group` consumers when the fan-out is ideal
+        got = oracle.tilecast_bytes(consumers, iters, tile_bytes) / group
+        assert got == float(expected)
+    # the printed reduction for a cluster of 2 is 50.00 %
+    assert 1.0 - 1.0 / 2 == 0.5
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("grouped", [True, False])
+def test_tilecast_group_membership(group, grouped):
+    n = 256
+    groups = [oracle.tilecast_group(w, n, group, grouped) for w in range(n)]
+    assert sorted(set(groups)) == list(range(n // group))
+    for g in range(n // group):
+        members = [w for w in range(n) if groups[w] == g]
+        assert len(members) == group
+        if grouped:
+            assert len({w % 8 for w in members}) == 1          # one XCD
+        else:
+            assert members == list(range(members[0], members[0] + group))
+
+
+def test_tilecast_group_rejects_bad_sizes():
+    assert oracle.tilecast_group(0, 256, 3, True) == -1
+    assert oracle.tilecast_group(0, 256, 64, True) == -1       # 32 workgroups per XCD
+    assert oracle.tilecast_group(256, 256, 2, False) == -1
+
+
+def test_tilecast_checksum_brute_force():
+    rows, cols, tm, tn = 32, 48, 8, 16
+    buf = np.arange(rows * cols, dtype=np.uint64) * 2654435761 % 65536
+    buf = buf.astype(np.uint16)
+    consumers, group, iters, stride = 16, 2, 7, 8
+    for grouped in (False, True):
+        for w in range(consumers):
+            g = oracle.tilecast_group(w, consumers, group, grouped)
+            tot, last = 0, 0
+            for it in range(iters):
+                t = it * stride + g
+                c0 = (t % (cols // tn)) * tn
+                r0 = ((t // (cols // tn)) % (rows // tm)) * tm
+                tile = buf.reshape(rows, cols)[r0:r0 + tm, c0:c0 + tn].astype(np.uint64)
+                s = int((tile[:, 0::2] + (tile[:, 1::2] << 16)).sum()) % 2 ** 32
+                tot = (tot + s) % 2 ** 32
+                last = s
+            assert oracle.tilecast_checksum(buf, rows, cols, tm, tn, w, consumers, group, grouped,
+                                            iters, stride) == (tot, last)
+
+
+# --------------------------------------------- planted mistakes are caught --
+
+def test_pins_catch_planted_mistakes():
+    """Slips planted on the CPU (wrong strides / lengths / sign fed to the
+    oracle) are each caught by one of the pins above."""
+    M, N, K = 16, 16, 64
+    Ai = draw((M, K), "int", -4, 4, 121)
+    Bi = draw((K, N), "int", -4, 4, 122)
+    a = Ai.float().numpy().astype(np.int64)
+    b = Bi.float().numpy().astype(np.int64)
+    exact = (a @ b).astype(np.float64)
+    # transposed B operand (row/col strides exchanged)
+    C, _ = oracle.gemm(bits(Ai), bits(Bi), 1, M, N, K, (K, 1, 0), (1, N, 0))
+    assert not np.array_equal(C[0], exact)
+    # dropped last term of the k sum
+    C, _ = oracle.gemm(bits(Ai), bits(Bi), 1, M, N, K - 1, (K, 1, 0), (N, 1, 0))
+    assert not np.array_equal(C[0], exact)
+    # transposed A operand
+    C, _ = oracle.gemm(bits(Ai), bits(Bi), 1, M, N, K, (1, M, 0), (N, 1, 0))
+    assert not np.array_equal(C[0], exact)
+    # sign slip: -A
+    Cn, _ = oracle.gemm(bits((-Ai.float()).to(torch.bfloat16)), bits(Bi), 1, M, N, K, (K, 1, 0), (N, 1, 0))
+    assert not np.array_equal(Cn[0], exact)
