@@ -1,0 +1,258 @@
+"""Python binding of libattn_scores.so (include/attn_scores.h) for MI355X / gfx950.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the current
+stream; nothing here computes on the CPU, and there is no fallback path --
+if the library has not been built, every call raises.
+
+Low-level names mirror the C ABI (``gemm_create``, ``gemm_run``,
+``gemm_destroy``, ``gemm_plan_info``, ``gemm_plan_tile_of``, ``sscore_run``,
+``tilecast_run``, ``as_status_str``, ``as_last_error``) and take raw device
+pointers.  ``gemm``, ``sscore`` and ``tilecast`` are tensor conveniences that
+read shapes, strides and dtypes from torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_scores.so")
+
+AS_OK, AS_ERR_INVALID, AS_ERR_UNSUPPORTED, AS_ERR_HIP, AS_ERR_NOMEM = 0, 1, 2, 3, 4
+AS_BF16, AS_F32 = 0, 1
+AS_FLAG_NO_GROUPING = 0x1
+AS_FLAG_TILE_128 = 0x2
+AS_FLAG_TILE_256 = 0x4
+
+EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
+            "sscore_run", "tilecast_run", "as_status_str", "as_last_error")
+
+
+class Strides(ctypes.Structure):
+    """as_strides: element strides (row, col, batch)."""
+    _fields_ = [("row", ctypes.c_int64), ("col", ctypes.c_int64), ("batch", ctypes.c_int64)]
+
+
+class AsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_status_name(status), message))
+        self.status = status
+
+
+def _status_name(status: int) -> str:
+    return {0: "AS_OK", 1: "AS_ERR_INVALID", 2: "AS_ERR_UNSUPPORTED", 3: "AS_ERR_HIP",
+            4: "AS_ERR_NOMEM"}.get(status, "AS_UNKNOWN_STATUS")
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libattn_scores.so is not built (run __graft_entry__.build() or "
+                               "python attention_scores_amd/_build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, u32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
+        L.gemm_create.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i64, Strides, Strides, Strides,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, u32]
+        L.gemm_create.restype = ctypes.c_int
+        L.gemm_run.argtypes = [vp, vp, vp, vp, vp]
+        L.gemm_run.restype = ctypes.c_int
+        L.gemm_destroy.argtypes = [vp]
+        L.gemm_destroy.restype = ctypes.c_int
+        L.gemm_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                     ctypes.POINTER(i64)]
+        L.gemm_plan_info.restype = ctypes.c_int
+        L.gemm_plan_tile_of.argtypes = [vp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.gemm_plan_tile_of.restype = ctypes.c_int
+        L.sscore_run.argtypes = [vp, vp, vp, i64, i64, i64, i64, Strides, Strides, Strides,
+                                 ctypes.c_int, ctypes.c_int, vp]
+        L.sscore_run.restype = ctypes.c_int
+        L.tilecast_run.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
+        L.tilecast_run.restype = ctypes.c_int
+        L.as_status_str.argtypes = [ctypes.c_int]
+        L.as_status_str.restype = ctypes.c_char_p
+        L.as_last_error.argtypes = []
+        L.as_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != AS_OK:
+        raise AsError(status, as_last_error())
+
+
+def as_status_str(status: int) -> str:
+    return lib().as_status_str(status).decode()
+
+
+def as_last_error() -> str:
+    return lib().as_last_error().decode()
+
+
+# ------------------------------------------------------------- raw C ABI --
+
+def gemm_create(M: int, N: int, K: int, batch: int, a: Tuple[int, int, int], b: Tuple[int, int, int],
+                c: Tuple[int, int, int], a_t: int = AS_BF16, b_t: int = AS_BF16, c_t: int = AS_F32,
+                flags: int = 0) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().gemm_create(ctypes.byref(h), M, N, K, batch, Strides(*a), Strides(*b), Strides(*c),
+                             a_t, b_t, c_t, flags))
+    return h.value
+
+
+def gemm_run(plan: int, A: int, B: int, C: int, stream: int = 0) -> None:
+    _check(lib().gemm_run(plan, A, B, C, stream))
+
+
+def gemm_destroy(plan: int) -> None:
+    _check(lib().gemm_destroy(plan))
+
+
+def gemm_plan_info(plan: int):
+    tm, tn, tk, wg = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().gemm_plan_info(plan, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(tk), ctypes.byref(wg)))
+    return tm.value, tn.value, tk.value, wg.value
+
+
+def gemm_plan_tile_of(plan: int, workgroup: int):
+    b, r, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().gemm_plan_tile_of(plan, workgroup, ctypes.byref(b), ctypes.byref(r), ctypes.byref(c)))
+    return b.value, r.value, c.value
+
+
+def sscore_run(Q: int, K: int, S: int, batch: int, Lq: int, Lk: int, dim: int, q: Tuple[int, int, int],
+               k: Tuple[int, int, int], s: Tuple[int, int, int], qk_t: int = AS_BF16, s_t: int = AS_F32,
+               stream: int = 0) -> None:
+    _check(lib().sscore_run(Q, K, S, batch, Lq, Lk, dim, Strides(*q), Strides(*k), Strides(*s), qk_t, s_t, stream))
+
+
+def tilecast_run(buf: int, rows: int, cols: int, tile_m: int, tile_n: int, consumers: int, group: int,
+                 grouped: bool, iters: int, warmup: int, stride: int, out_checksum: int, stream: int = 0) -> None:
+    _check(lib().tilecast_run(buf, rows, cols, tile_m, tile_n, consumers, group, int(bool(grouped)), iters,
+                              warmup, stride, out_checksum, stream))
+
+
+# ---------------------------------------------------- torch conveniences --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return AS_BF16
+    if dt == torch.float32:
+        return AS_F32
+    raise AsError(AS_ERR_UNSUPPORTED, "dtype %s" % dt)
+
+
+def _stream_handle(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _strides3(t):
+    """(row, col, batch) element strides of a 2-D or 3-D tensor."""
+    if t.dim() == 2:
+        return (t.stride(0), t.stride(1), 0)
+    if t.dim() == 3:
+        return (t.stride(1), t.stride(2), t.stride(0))
+    raise AsError(AS_ERR_INVALID, "expected a 2-D or 3-D tensor")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise AsError(AS_ERR_INVALID, "tensors must be on the GPU")
+
+
+_plan_cache = {}
+_plan_cache_lock = threading.Lock()
+
+
+def plan_for(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags=0) -> int:
+    """Cached gemm_create for a shape/stride/dtype/flags key."""
+    key = (M, N, K, batch, tuple(sa), tuple(sb), tuple(sc), a_t, b_t, c_t, flags)
+    with _plan_cache_lock:
+        p = _plan_cache.get(key)
+        if p is None:
+            p = gemm_create(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags)
+            _plan_cache[key] = p
+        return p
+
+
+def gemm(A, B, out=None, out_dtype=None, flags: int = 0):
+    """C = A @ B for bf16 A [M,K] / [b,M,K] and B [K,N] / [b,K,N] (any unit-stride orientation)."""
+    torch = _torch()
+    _require_cuda(A, B)
+    batched = A.dim() == 3 or B.dim() == 3
+    M, K = A.shape[-2], A.shape[-1]
+    K2, N = B.shape[-2], B.shape[-1]
+    if K != K2:
+        raise AsError(AS_ERR_INVALID, "inner dimensions differ (%d vs %d)" % (K, K2))
+    batch = max(A.shape[0] if A.dim() == 3 else 1, B.shape[0] if B.dim() == 3 else 1)
+    for t in (A, B):
+        if t.dim() == 3 and t.shape[0] not in (1, batch):
+            raise AsError(AS_ERR_INVALID, "batch sizes differ")
+    sa, sb = list(_strides3(A)), list(_strides3(B))
+    if A.dim() == 3 and A.shape[0] == 1:
+        sa[2] = 0
+    if B.dim() == 3 and B.shape[0] == 1:
+        sb[2] = 0
+    if out is None:
+        od = out_dtype if out_dtype is not None else torch.float32
+        out = torch.empty((batch, M, N) if batched else (M, N), dtype=od, device=A.device)
+    _require_cuda(out)
+    sc = _strides3(out)
+    plan = plan_for(M, N, K, batch, sa, sb, sc, _dtype_code(A.dtype), _dtype_code(B.dtype),
+                    _dtype_code(out.dtype), flags)
+    gemm_run(plan, A.data_ptr(), B.data_ptr(), out.data_ptr(), _stream_handle(A))
+    return out
+
+
+def sscore(Q, K, out=None, out_dtype=None):
+    """S = Q @ K^T per slice: Q [b,Lq,d], K [b,Lk,d] bf16 -> S [b,Lq,Lk] (no scale, no softmax)."""
+    torch = _torch()
+    _require_cuda(Q, K)
+    if Q.dim() != 3 or K.dim() != 3:
+        raise AsError(AS_ERR_INVALID, "Q and K must be [batch, L, d]")
+    b, Lq, d = Q.shape
+    if K.shape[0] != b or K.shape[2] != d:
+        raise AsError(AS_ERR_INVALID, "Q and K shapes do not match")
+    Lk = K.shape[1]
+    if out is None:
+        od = out_dtype if out_dtype is not None else torch.float32
+        out = torch.empty((b, Lq, Lk), dtype=od, device=Q.device)
+    _require_cuda(out)
+    sscore_run(Q.data_ptr(), K.data_ptr(), out.data_ptr(), b, Lq, Lk, d, _strides3(Q), _strides3(K),
+               _strides3(out), _dtype_code(Q.dtype), _dtype_code(out.dtype), _stream_handle(Q))
+    return out
+
+
+def tilecast(buf, tile_m: int = 128, tile_n: int = 64, consumers: int = 256, group: int = 2,
+             grouped: bool = True, iters: int = 5000, warmup: int = 0, stride: int = 0, out=None):
+    """Run the tile fan-out microbenchmark over a 2-D bf16 CUDA tensor; returns the checksum tensor."""
+    torch = _torch()
+    _require_cuda(buf)
+    if buf.dim() != 2 or buf.stride(1) != 1 or buf.stride(0) != buf.shape[1]:
+        raise AsError(AS_ERR_INVALID, "buf must be a contiguous 2-D tensor")
+    if out is None:
+        out = torch.zeros(2 * consumers, dtype=torch.int32, device=buf.device)
+    tilecast_run(buf.data_ptr(), buf.shape[0], buf.shape[1], tile_m, tile_n, consumers, group, grouped,
+                 iters, warmup, stride, out.data_ptr(), _stream_handle(buf))
+    return out

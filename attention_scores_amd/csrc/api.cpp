@@ -1,0 +1,275 @@
+// api.cpp -- the C ABI (include/attn_scores.h): argument checks, planning,
+// plan registry, error reporting.  Every check runs before any HIP call.
+#include "attn_scores.h"
+
+#include <cinttypes>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_set>
+
+#include "internal.hpp"
+#include "schedule.hpp"
+
+struct as_gemm_plan {
+    asl::GemmDesc d;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+std::mutex g_plans_mu;
+std::unordered_set<const as_gemm_plan*>& plans() {
+    static std::unordered_set<const as_gemm_plan*> s;
+    return s;
+}
+
+as_status fail(as_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+as_status fail(as_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+as_status ok() {
+    g_last_error.clear();
+    return AS_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256;
+constexpr int64_t kBK = 64;
+
+// Rows of tiles per group: minimise the panels one XCD's share of the grid
+// touches (A row-panels + B column-panels), ties broken by the panels its
+// ~32 concurrently running workgroups touch.
+int choose_group_m(int64_t tiles, int64_t tiles_m, int64_t tiles_n) {
+    int64_t per_batch = tiles_m * tiles_n;
+    int64_t share = (tiles + asl::kXcds - 1) / asl::kXcds;
+    if (share > per_batch) share = per_batch;
+    int best = 1;
+    int64_t best_cost = INT64_MAX, best_tie = INT64_MAX;
+    for (int64_t gm = 1; gm <= tiles_m && gm <= 64; gm *= 2) {
+        int64_t cols = (share + gm - 1) / gm;
+        if (cols > tiles_n) cols = tiles_n;
+        int64_t cost = gm + cols;
+        int64_t ccols = (32 + gm - 1) / gm;
+        if (ccols > tiles_n) ccols = tiles_n;
+        int64_t tie = gm + ccols;
+        if (cost < best_cost || (cost == best_cost && tie < best_tie)) {
+            best = (int)gm;
+            best_cost = cost;
+            best_tie = tie;
+        }
+    }
+    return best;
+}
+
+as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t batch,
+                    as_strides a, as_strides b, as_strides c,
+                    as_dtype a_t, as_dtype b_t, as_dtype c_t, uint32_t flags) {
+    if (M <= 0 || N <= 0 || K <= 0 || batch <= 0)
+        return fail(AS_ERR_INVALID, "sizes must be positive (M=%" PRId64 " N=%" PRId64 " K=%" PRId64
+                    " batch=%" PRId64 ")", M, N, K, batch);
+    if (flags & ~kKnownFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    if ((flags & AS_FLAG_TILE_128) && (flags & AS_FLAG_TILE_256))
+        return fail(AS_ERR_INVALID, "AS_FLAG_TILE_128 and AS_FLAG_TILE_256 are exclusive");
+    for (as_dtype t : {a_t, b_t, c_t})
+        if (t != AS_BF16 && t != AS_F32) return fail(AS_ERR_INVALID, "unknown dtype %d", (int)t);
+    if (a_t != AS_BF16 || b_t != AS_BF16)
+        return fail(AS_ERR_UNSUPPORTED, "A and B must be bf16");
+    const int64_t sv[9] = {a.row, a.col, a.batch, b.row, b.col, b.batch, c.row, c.col, c.batch};
+    for (int64_t v : sv)
+        if (v < 0) return fail(AS_ERR_INVALID, "negative stride %" PRId64, v);
+
+    asl::GemmDesc d{};
+    d.M = M; d.N = N; d.K = K; d.batch = batch;
+    d.a_row = a.row; d.a_col = a.col; d.a_batch = a.batch;
+    d.b_row = b.row; d.b_col = b.col; d.b_batch = b.batch;
+    d.c_row = c.row; d.c_batch = c.batch;
+    d.c_bf16 = (c_t == AS_BF16);
+
+    // Operand orientation.
+    if (a.col == 1) d.a_kmajor = true;
+    else if (a.row == 1) d.a_kmajor = false;
+    else return fail(AS_ERR_UNSUPPORTED, "A needs a unit row or column stride");
+    if (b.row == 1 && b.col != 1) d.b_kmajor = true;
+    else if (b.col == 1) d.b_kmajor = false;
+    else return fail(AS_ERR_UNSUPPORTED, "B needs a unit row or column stride");
+    if (c.col != 1) return fail(AS_ERR_UNSUPPORTED, "C must have column stride 1");
+
+    const int64_t a_ld = d.a_kmajor ? a.row : a.col;
+    const int64_t b_ld = d.b_kmajor ? b.col : b.row;
+    if (a_ld % 8 || b_ld % 8)
+        return fail(AS_ERR_UNSUPPORTED, "leading strides must be multiples of 8 elements (A %" PRId64
+                    ", B %" PRId64 ")", a_ld, b_ld);
+    const int64_t c_align = d.c_bf16 ? 8 : 4;
+    if (c.row % c_align)
+        return fail(AS_ERR_UNSUPPORTED, "C row stride must be a multiple of %" PRId64 " elements", c_align);
+    if (M > 1 && c.row < N) return fail(AS_ERR_INVALID, "C rows overlap (row stride %" PRId64 " < N)", c.row);
+    if (batch > 1 && c.batch < M * c.row)
+        return fail(AS_ERR_INVALID, "C batches overlap (batch stride %" PRId64 ")", c.batch);
+
+    // Tile choice.
+    int tile;
+    if (flags & AS_FLAG_TILE_256) tile = 256;
+    else if (flags & AS_FLAG_TILE_128) tile = 128;
+    else if (M % 256 == 0 && N % 256 == 0 && batch * (M / 256) * (N / 256) >= 128) tile = 256;
+    else tile = 128;
+    if (M % tile || N % tile || K % kBK)
+        return fail(AS_ERR_UNSUPPORTED, "M and N must be multiples of the %dx%d tile and K of %" PRId64
+                    " (M=%" PRId64 " N=%" PRId64 " K=%" PRId64 ")", tile, tile, kBK, M, N, K);
+    // Per-lane 32-bit byte offsets inside one staged tile.
+    const int64_t a_span = (d.a_kmajor ? tile : kBK) * a_ld * 2;
+    const int64_t b_span = (d.b_kmajor ? tile : kBK) * b_ld * 2;
+    if (a_span >= (INT64_C(1) << 31) || b_span >= (INT64_C(1) << 31))
+        return fail(AS_ERR_UNSUPPORTED, "leading strides too large for 32-bit tile offsets");
+    if (K / kBK > INT32_MAX) return fail(AS_ERR_UNSUPPORTED, "K too large");
+
+    d.tile = tile;
+    d.tiles_m = M / tile;
+    d.tiles_n = N / tile;
+    if (d.tiles_m > INT32_MAX / d.tiles_n || d.tiles_m * d.tiles_n > INT32_MAX / batch)
+        return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
+    d.tiles = batch * d.tiles_m * d.tiles_n;
+    d.grouped = !(flags & AS_FLAG_NO_GROUPING);
+    d.group_m = choose_group_m(d.tiles, d.tiles_m, d.tiles_n);
+    *out = d;
+    return AS_OK;
+}
+
+bool plan_live(const as_gemm_plan* p) {
+    std::lock_guard<std::mutex> lk(g_plans_mu);
+    return p && plans().count(p);
+}
+
+as_status run_desc(const asl::GemmDesc& d, const void* A, const void* B, void* C, void* stream) {
+    if (!A || !B || !C) return fail(AS_ERR_INVALID, "null device pointer");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C))
+        return fail(AS_ERR_UNSUPPORTED, "device pointers must be 16-byte aligned");
+    int e = asl::launch_gemm(d, A, B, C, stream);
+    if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t batch,
+                      as_strides a, as_strides b, as_strides c,
+                      as_dtype a_t, as_dtype b_t, as_dtype c_t, uint32_t flags) {
+    if (!out) return fail(AS_ERR_INVALID, "null plan output pointer");
+    *out = nullptr;
+    asl::GemmDesc d;
+    as_status s = plan_desc(&d, M, N, K, batch, a, b, c, a_t, b_t, c_t, flags);
+    if (s != AS_OK) return s;
+    as_gemm_plan* p = new (std::nothrow) as_gemm_plan;
+    if (!p) return fail(AS_ERR_NOMEM, "out of host memory");
+    p->d = d;
+    {
+        std::lock_guard<std::mutex> lk(g_plans_mu);
+        plans().insert(p);
+    }
+    *out = p;
+    return ok();
+}
+
+as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream) {
+    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
+    return run_desc(plan->d, A, B, C, hip_stream);
+}
+
+as_status gemm_destroy(as_gemm_t plan) {
+    {
+        std::lock_guard<std::mutex> lk(g_plans_mu);
+        if (!plan || !plans().erase(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
+    }
+    delete plan;
+    return ok();
+}
+
+as_status gemm_plan_info(as_gemm_t plan, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,
+                         int64_t* workgroups) {
+    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
+    if (tile_m) *tile_m = plan->d.tile;
+    if (tile_n) *tile_n = plan->d.tile;
+    if (tile_k) *tile_k = (int32_t)kBK;
+    if (workgroups) *workgroups = plan->d.tiles;
+    return ok();
+}
+
+as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* batch, int64_t* tile_row,
+                            int64_t* tile_col) {
+    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
+    if (workgroup < 0 || workgroup >= plan->d.tiles || !batch || !tile_row || !tile_col)
+        return fail(AS_ERR_INVALID, "workgroup out of range or null output");
+    asl::tile_of_workgroup(plan->d, workgroup, batch, tile_row, tile_col);
+    return ok();
+}
+
+as_status sscore_run(const void* Q, const void* K, void* S,
+                     int64_t batch, int64_t Lq, int64_t Lk, int64_t dim,
+                     as_strides q, as_strides k, as_strides s,
+                     as_dtype qk_t, as_dtype s_t, void* hip_stream) {
+    if (q.col != 1 || k.col != 1 || s.col != 1) {
+        if (q.col < 0 || k.col < 0 || s.col < 0) return fail(AS_ERR_INVALID, "negative stride");
+        return fail(AS_ERR_UNSUPPORTED, "Q, K and S need column stride 1");
+    }
+    // S = Q . K^T: A = Q, B[d, j] = K[j, d] (row stride 1, column stride k.row).
+    as_strides a = {q.row, 1, q.batch};
+    as_strides b = {1, k.row, k.batch};
+    asl::GemmDesc d;
+    as_status st = plan_desc(&d, Lq, Lk, dim, batch, a, b, s, qk_t, qk_t, s_t, 0);
+    if (st != AS_OK) return st;
+    return run_desc(d, Q, K, S, hip_stream);
+}
+
+as_status tilecast_run(const void* buf, int64_t rows, int64_t cols, int32_t tile_m, int32_t tile_n,
+                       int32_t consumers, int32_t group, int32_t grouped, int64_t iters,
+                       int64_t warmup, int64_t stride, uint32_t* out_checksum, void* hip_stream) {
+    if (!buf || !out_checksum) return fail(AS_ERR_INVALID, "null pointer");
+    if (rows <= 0 || cols <= 0 || tile_m <= 0 || tile_n <= 0)
+        return fail(AS_ERR_INVALID, "sizes must be positive");
+    if (consumers <= 0 || consumers > 4096 || consumers % 8)
+        return fail(AS_ERR_INVALID, "consumers must be a positive multiple of 8, at most 4096");
+    if (group <= 0 || consumers % group) return fail(AS_ERR_INVALID, "group must divide consumers");
+    if (grouped && (consumers / 8) % group)
+        return fail(AS_ERR_INVALID, "grouped: group must divide consumers/8 (workgroups per XCD)");
+    if (iters < 0 || warmup < 0 || stride < 0) return fail(AS_ERR_INVALID, "negative iteration count or stride");
+    if (tile_n % 8) return fail(AS_ERR_UNSUPPORTED, "tile_n must be a multiple of 8");
+    if ((int64_t)tile_m * tile_n * 2 > 65536) return fail(AS_ERR_UNSUPPORTED, "tile larger than 64 KiB");
+    if (rows % tile_m || cols % tile_n) return fail(AS_ERR_UNSUPPORTED, "matrix not a multiple of the tile");
+    if (rows / tile_m > INT32_MAX || cols / tile_n > INT32_MAX) return fail(AS_ERR_UNSUPPORTED, "too many tiles");
+    if (!aligned16(buf)) return fail(AS_ERR_UNSUPPORTED, "buffer must be 16-byte aligned");
+    if (stride > 0 && (iters + warmup) > INT64_MAX / stride) return fail(AS_ERR_INVALID, "tile index overflow");
+    asl::TilecastDesc d{buf, rows, cols, tile_m, tile_n, consumers, group, grouped ? 1 : 0,
+                        iters + warmup, stride, out_checksum};
+    int e = asl::launch_tilecast(d, hip_stream);
+    if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
+    return ok();
+}
+
+const char* as_status_str(as_status s) {
+    switch (s) {
+        case AS_OK: return "AS_OK";
+        case AS_ERR_INVALID: return "AS_ERR_INVALID";
+        case AS_ERR_UNSUPPORTED: return "AS_ERR_UNSUPPORTED";
+        case AS_ERR_HIP: return "AS_ERR_HIP";
+        case AS_ERR_NOMEM: return "AS_ERR_NOMEM";
+    }
+    return "AS_UNKNOWN_STATUS";
+}
+
+const char* as_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// internal.hpp -- host-side interface between the C ABI (api.cpp) and the
+// kernel launchers (gemm.hip, tilecast.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <cstdint>
+
+namespace asl {
+
+// Everything a GEMM launch needs, fixed at plan time.  Strides are elements.
+struct GemmDesc {
+    int64_t M, N, K, batch;
+    int64_t a_row, a_col, a_batch;   // A[b,i,k]
+    int64_t b_row, b_col, b_batch;   // B[b,k,j]
+    int64_t c_row, c_batch;          // C[b,i,j], column stride 1
+    bool a_kmajor;                   // A[i, k..k+7] contiguous
+    bool b_kmajor;                   // B[k..k+7, j] contiguous
+    bool c_bf16;                     // output rounded to bf16 (else fp32)
+    int tile;                        // 256 or 128 (square output tile)
+    int group_m;                     // rows of tiles per group in the grouped order
+    bool grouped;                    // XCD-aware grouped order (false: identity)
+    int64_t tiles_m, tiles_n, tiles; // grid
+};
+
+// Launch the planned product.  Returns 0 or a hipError_t value.
+int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* stream);
+
+// Logical tile visited by hardware workgroup id h (the device remap, shared
+// with the kernels): writes batch, tile row and tile column.
+void tile_of_workgroup(const GemmDesc& d, int64_t h, int64_t* b, int64_t* tm, int64_t* tn);
+
+struct TilecastDesc {
+    const void* buf;
+    int64_t rows, cols;
+    int32_t tile_m, tile_n;
+    int32_t consumers, group, grouped;
+    int64_t iters, stride;
+    uint32_t* out;
+};
+
+int launch_tilecast(const TilecastDesc& d, void* stream);
+
+}  // namespace asl

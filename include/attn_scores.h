@@ -1,0 +1,179 @@
+/*
+ * attn_scores.h -- C ABI of the MI355X (gfx950) operand-reuse contraction library.
+ *
+ * Operations
+ *   gemm_*      C[b,i,j] = sum_k A[b,i,k] * B[b,k,j]          (beta = 0, no alpha)
+ *   sscore_run  S[b,i,j] = sum_d Q[b,i,d] * K[b,j,d]  = Q.K^T  (no scale, no softmax)
+ *   tilecast_run  tile fan-out microbenchmark
+ *
+ * Where the operations are defined:
+ *   - The GEMM over a tile grid whose rows share an A row-panel and whose
+ *     columns share a B column-panel: lesson 07 "Clusters, distributed shared
+ *     memory & cluster launch control", section "TMA multicast -- one load,
+ *     many CTAs".
+ *   - The attention scores S_i = Q_i K^T, computed by neighbouring workgroups
+ *     that consume the same key tile: "Hopper TMA Multicast" deep-dive,
+ *     Attention/GEMM reuse use-case, equation S_0 = Q_0 K^T, S_1 = Q_1 K^T.
+ *     The equation carries no scale and no softmax, and neither does sscore_run.
+ *   - The fan-out microbenchmark: same deep-dive, sections "Microbenchmark
+ *     source" (128x64 16-bit tiles, consumers loading tile
+ *     iteration*stride + group each iteration) and "run results" (hot-tile
+ *     and streaming scenarios).
+ *
+ * Numerics: A and B (Q and K) are bf16; products are accumulated in fp32 by
+ * v_mfma_f32_32x32x16_bf16; C is written as fp32, or rounded to bf16 with
+ * round-to-nearest-even.  Results are deterministic run to run (no atomics,
+ * no split-K).
+ *
+ * Layout conventions.  All strides are ELEMENT strides (not bytes).  A matrix
+ * X[b, r, c] lives at base + b*batch + r*row + c*col.  A batch stride of 0
+ * broadcasts one matrix to every batch entry.  For A (M x K) exactly one of
+ * row/col must be 1: col == 1 is "K-major" (row-major A), row == 1 is
+ * "M-major" (column-major A).  For B (K x N): row == 1 is "K-major" (B given
+ * as its transpose, like K in Q.K^T), col == 1 is "N-major" (row-major B).
+ * C must have col == 1.  The leading (non-unit) stride of every operand must
+ * be a multiple of 8 elements and every base pointer 16-byte aligned.
+ *
+ * Ownership.  The caller owns every device buffer; the library never
+ * allocates, frees or keeps user memory.  A plan (as_gemm_t) is host memory
+ * only; it may be destroyed as soon as gemm_run returns, because kernel
+ * arguments are captured by value at launch.  `hip_stream` is the caller's
+ * hipStream_t (NULL = the null stream); every run call is asynchronous on it
+ * and never synchronizes.  Calls are thread-safe; as_last_error() is
+ * per-thread.
+ *
+ * Errors.  Every entry point returns an as_status.  All argument checks
+ * happen before any HIP call, so invalid calls are rejected without a GPU:
+ *   AS_ERR_INVALID      null/negative/zero sizes, null pointers, an output
+ *                       whose rows or batches overlap, unknown flags or
+ *                       dtypes, a null or unknown plan
+ *   AS_ERR_UNSUPPORTED  a well-formed request the kernels do not cover
+ *                       (operand dtypes other than bf16, a contiguous stride
+ *                       other than 1, unaligned pointers or leading strides,
+ *                       M/N/K not multiples of the chosen tile)
+ *   AS_ERR_HIP          a HIP launch error (the text is in as_last_error())
+ *   AS_ERR_NOMEM        host allocation of a plan failed
+ * Nothing is ever computed silently wrong: an unsupported case is refused.
+ */
+#ifndef ATTN_SCORES_H
+#define ATTN_SCORES_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define AS_API __attribute__((visibility("default")))
+#else
+#define AS_API
+#endif
+
+typedef enum {
+    AS_OK = 0,
+    AS_ERR_INVALID = 1,
+    AS_ERR_UNSUPPORTED = 2,
+    AS_ERR_HIP = 3,
+    AS_ERR_NOMEM = 4
+} as_status;
+
+typedef enum { AS_BF16 = 0, AS_F32 = 1 } as_dtype;
+
+/* Element strides of X[b, r, c]. */
+typedef struct {
+    int64_t row;
+    int64_t col;
+    int64_t batch;
+} as_strides;
+
+/* gemm_create flags */
+#define AS_FLAG_NO_GROUPING 0x1u  /* ablation: workgroup id -> tile is the identity (row-major tile order) */
+#define AS_FLAG_TILE_128    0x2u  /* force 128x128 output tiles */
+#define AS_FLAG_TILE_256    0x4u  /* force 256x256 output tiles */
+
+typedef struct as_gemm_plan* as_gemm_t;
+
+/*
+ * Plan C = A.B for `batch` independent (M x K).(K x N) products.
+ *   out          receives the plan handle (host memory)
+ *   M, N, K      sizes, > 0
+ *   batch        number of products, > 0
+ *   a, b, c      element strides of A[b,i,k], B[b,k,j], C[b,i,j]
+ *   a_t, b_t     must be AS_BF16
+ *   c_t          AS_F32, or AS_BF16 (round-to-nearest-even)
+ *   flags        AS_FLAG_* bits
+ * Chooses the output tile (256x256 or 128x128, 4 waves), the workgroup
+ * grouping and the grid.  Makes no HIP call.
+ */
+AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t batch,
+                      as_strides a, as_strides b, as_strides c,
+                      as_dtype a_t, as_dtype b_t, as_dtype c_t, uint32_t flags);
+
+/* Launch the planned product on `hip_stream`.  A, B: device bf16; C: device
+ * fp32 or bf16 as planned.  Pointers must be 16-byte aligned. */
+AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream);
+
+/* Release a plan created by gemm_create (NULL or unknown -> AS_ERR_INVALID). */
+AS_API as_status gemm_destroy(as_gemm_t plan);
+
+/* Tile shape a plan chose (for reporting); returns AS_ERR_INVALID on a bad plan. */
+AS_API as_status gemm_plan_info(as_gemm_t plan, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,
+                         int64_t* workgroups);
+
+/* Output tile that hardware workgroup `workgroup` (0 <= workgroup <
+ * workgroups) computes under the plan's XCD-aware grouped order: batch
+ * index, tile row and tile column.  Host-only; for inspection and tests. */
+AS_API as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* batch, int64_t* tile_row,
+                            int64_t* tile_col);
+
+/*
+ * Attention scores S[b,i,j] = sum_d Q[b,i,d] * K[b,j,d] for b < batch,
+ * i < Lq, j < Lk, d < dim.  Q is [batch, Lq, dim], K is [batch, Lk, dim],
+ * S is [batch, Lq, Lk], each addressed by its own (row, col, batch) element
+ * strides with col == 1 for all three (the head dimension and the key index
+ * contiguous).  qk_t must be AS_BF16; s_t AS_F32 or AS_BF16.  This is the
+ * GEMM with A = Q and B = K^T, planned and launched in one call (same
+ * kernels, same errors).  Asynchronous on `hip_stream`.
+ */
+AS_API as_status sscore_run(const void* Q, const void* K, void* S,
+                     int64_t batch, int64_t Lq, int64_t Lk, int64_t dim,
+                     as_strides q, as_strides k, as_strides s,
+                     as_dtype qk_t, as_dtype s_t, void* hip_stream);
+
+/*
+ * Tile fan-out microbenchmark.  `consumers` workgroups (a multiple of 8, at
+ * most 4096) each load, once per iteration, one tile_m x tile_n tile of the
+ * bf16 row-major matrix `buf` (rows x cols, leading dimension cols) into
+ * LDS with 128-bit loads.  In iteration `it` the workgroups of group g load
+ * tile index it*stride + g, at tile row ((it*stride+g) div (cols/tile_n))
+ * mod (rows/tile_m) and tile column (it*stride+g) mod (cols/tile_n).
+ * Groups hold `group` workgroups:
+ *   grouped != 0  members run on one XCD: workgroup w runs on XCD w mod 8
+ *                 and is the (w div 8)-th there; `group` consecutive ones of
+ *                 an XCD form a group (so `group` must divide consumers/8);
+ *   grouped == 0  members are `group` consecutive workgroup ids.
+ * The launch runs warmup + iters iterations (it = 0 .. warmup+iters-1; the
+ * split only mirrors the deep-dive's kernel arguments).  out_checksum
+ * (device, 2*consumers uint32) receives, per workgroup w: [2w] the sum
+ * modulo 2^32 of every little-endian 32-bit word of every tile it loaded in
+ * all iterations, and [2w+1] the same sum over the tile held in its LDS at
+ * the end (the last one loaded).
+ * tile_n must be a multiple of 8, tile_m*tile_n*2 at most 65536 bytes, rows
+ * and cols multiples of tile_m and tile_n.  Asynchronous on `hip_stream`.
+ */
+AS_API as_status tilecast_run(const void* buf, int64_t rows, int64_t cols, int32_t tile_m, int32_t tile_n,
+                       int32_t consumers, int32_t group, int32_t grouped, int64_t iters,
+                       int64_t warmup, int64_t stride, uint32_t* out_checksum, void* hip_stream);
+
+/* Static text for a status code. */
+AS_API const char* as_status_str(as_status s);
+
+/* Text of the last error reported on the calling thread ("" if none). */
+AS_API const char* as_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SCORES_H */

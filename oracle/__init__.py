@@ -63,6 +63,8 @@ def _load():
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
     lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_f64_to_bf16_rne_array.argtypes = [dp, u16p, i64]
+    lib.oracle_f64_to_bf16_rne_array.restype = None
     lib.oracle_gemm.argtypes = [u16p, u16p, dp, dp, i64, i64, i64, i64] + [i64] * 6 + [i32]
     lib.oracle_gemm.restype = i32
     lib.oracle_gemm_points.argtypes = [u16p, u16p, ctypes.c_void_p, i64, dp, dp, i64] + [i64] * 6 + [i32]
@@ -109,6 +111,14 @@ def bf16_to_f64(bits) -> float:
 
 def f64_to_bf16_rne(x: float) -> int:
     return int(_load().oracle_f64_to_bf16_rne(float(x)))
+
+
+def f64_to_bf16_rne_array(x: np.ndarray) -> np.ndarray:
+    """Element-wise round-to-nearest-even of doubles to bf16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_f64_to_bf16_rne_array(_ptr(x), _ptr(out), x.size)
+    return out
 
 
 def bf16_bits_to_f64_array(bits: np.ndarray) -> np.ndarray:

@@ -301,3 +301,8 @@ uint32_t oracle_tilecast_checksum(const uint16_t* buf, int64_t rows, int64_t col
     if (last_sum) *last_sum = last;
     return total;
 }
+
+/* Element-wise oracle_f64_to_bf16_rne over an array (n values). */
+void oracle_f64_to_bf16_rne_array(const double* x, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16_rne(x[i]);
+}

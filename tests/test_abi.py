@@ -1,0 +1,232 @@
+"""C-ABI checks that need no GPU: exports, status codes, argument validation,
+plan registry and the workgroup -> tile schedule (host replica of the device map)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_scores_amd as asl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_scores.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"AS_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+def test_header_declares_binding_names():
+    assert _declared_functions() == sorted(asl.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = asl.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    # and nothing else is exported with C linkage beyond the header's names
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", asl.LIB_PATH], capture_output=True, text=True).stdout
+    text_syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert text_syms == set(_declared_functions())
+
+
+def test_status_strings():
+    assert asl.as_status_str(0) == "AS_OK"
+    assert asl.as_status_str(1) == "AS_ERR_INVALID"
+    assert asl.as_status_str(2) == "AS_ERR_UNSUPPORTED"
+    assert asl.as_status_str(3) == "AS_ERR_HIP"
+    assert asl.as_status_str(4) == "AS_ERR_NOMEM"
+    assert asl.as_status_str(99) == "AS_UNKNOWN_STATUS"
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except asl.AsError as e:
+        return e.status
+    return asl.AS_OK
+
+
+RM = lambda r, c: (c, 1, 0)   # row-major r x c
+
+
+@pytest.mark.parametrize("M,N,K,batch", [(0, 512, 512, 1), (512, -1, 512, 1), (512, 512, 0, 1), (512, 512, 512, 0)])
+def test_create_rejects_bad_sizes(M, N, K, batch):
+    st = _status(asl.gemm_create, M, N, K, batch, (max(K, 8), 1, 0), (max(N, 8), 1, 0), (max(N, 8), 1, 0))
+    assert st == asl.AS_ERR_INVALID
+
+
+def test_create_rejects_bad_flags_and_dtypes():
+    args = (512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512))
+    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, asl.AS_F32, 0x100) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, asl.AS_F32,
+                   asl.AS_FLAG_TILE_128 | asl.AS_FLAG_TILE_256) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, 7, 0) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_create, *args, asl.AS_F32, asl.AS_BF16, asl.AS_F32, 0) == asl.AS_ERR_UNSUPPORTED
+    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_F32, asl.AS_F32, 0) == asl.AS_ERR_UNSUPPORTED
+
+
+def test_create_rejects_bad_strides():
+    base = dict(M=512, N=512, K=512, batch=1)
+    mk = lambda a, b, c, batch=1: _status(asl.gemm_create, 512, 512, 512, batch, a, b, c)
+    assert mk((-512, 1, 0), RM(512, 512), RM(512, 512)) == asl.AS_ERR_INVALID        # negative
+    assert mk((512, 2, 0), RM(512, 512), RM(512, 512)) == asl.AS_ERR_UNSUPPORTED      # no unit stride
+    assert mk((516, 1, 0), RM(512, 512), RM(512, 512)) == asl.AS_ERR_UNSUPPORTED      # ld % 8
+    assert mk(RM(512, 512), (512, 2, 0), RM(512, 512)) == asl.AS_ERR_UNSUPPORTED
+    assert mk(RM(512, 512), RM(512, 512), (512, 2, 0)) == asl.AS_ERR_UNSUPPORTED      # C col stride
+    assert mk(RM(512, 512), RM(512, 512), (256, 1, 0)) == asl.AS_ERR_INVALID          # C rows overlap
+    assert mk(RM(512, 512), RM(512, 512), (512, 1, 0), batch=2) == asl.AS_ERR_INVALID  # C batches overlap
+    assert mk(RM(512, 512), RM(512, 512), (514, 1, 0)) == asl.AS_ERR_UNSUPPORTED      # C row alignment
+    del base
+
+
+@pytest.mark.parametrize("M,N,K", [(500, 512, 512), (512, 520, 512), (512, 512, 96), (384, 384, 100)])
+def test_create_refuses_ragged_shapes(M, N, K):
+    st = _status(asl.gemm_create, M, N, K, 1, (K + (-K) % 8, 1, 0), (N + (-N) % 8, 1, 0), (N + (-N) % 8, 1, 0))
+    assert st == asl.AS_ERR_UNSUPPORTED
+    assert "multiple" in asl.as_last_error()
+
+
+def test_create_refuses_huge_leading_stride():
+    # 256 rows of a K-major tile at ld = 2^23 elements overflow 32-bit offsets
+    st = _status(asl.gemm_create, 8192, 8192, 8192, 1, (1 << 23, 1, 0), RM(8192, 8192), RM(8192, 8192))
+    assert st == asl.AS_ERR_UNSUPPORTED
+
+
+def test_plan_registry_and_run_argument_checks():
+    p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512))
+    assert asl.gemm_plan_info(p) == (128, 128, 64, 16)
+    assert _status(asl.gemm_run, p, 0, 0, 0) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_run, p, 16, 32, 0) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_run, p, 8, 16, 32) == asl.AS_ERR_UNSUPPORTED          # misaligned
+    assert _status(asl.gemm_run, p + 8, 16, 32, 48) == asl.AS_ERR_INVALID         # unknown plan
+    assert _status(asl.gemm_run, 0, 16, 32, 48) == asl.AS_ERR_INVALID
+    asl.gemm_destroy(p)
+    assert _status(asl.gemm_destroy, p) == asl.AS_ERR_INVALID                     # double destroy
+    assert _status(asl.gemm_run, p, 16, 32, 48) == asl.AS_ERR_INVALID             # destroyed plan
+    assert _status(asl.gemm_destroy, 0) == asl.AS_ERR_INVALID
+    L = asl.lib()
+    assert L.gemm_create(None, 512, 512, 512, 1, asl.Strides(512, 1, 0), asl.Strides(512, 1, 0),
+                         asl.Strides(512, 1, 0), 0, 0, 1, 0) == asl.AS_ERR_INVALID
+
+
+def test_last_error_is_per_call():
+    _status(asl.gemm_create, 0, 1, 1, 1, (8, 1, 0), (8, 1, 0), (8, 1, 0))
+    assert "positive" in asl.as_last_error()
+    p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512))
+    assert asl.as_last_error() == ""
+    asl.gemm_destroy(p)
+
+
+def test_tile_choice():
+    p = asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192), c_t=asl.AS_BF16)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024)
+    asl.gemm_destroy(p)
+    p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512), flags=asl.AS_FLAG_TILE_256)
+    assert asl.gemm_plan_info(p)[0] == 256
+    asl.gemm_destroy(p)
+    p = asl.gemm_create(65536, 256, 4096, 1, RM(65536, 4096), RM(4096, 256), RM(65536, 256))
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 256)
+    asl.gemm_destroy(p)
+
+
+SHAPES = [  # (M, N, K, batch, flags)
+    (8192, 8192, 8192, 1, 0),
+    (2048, 2048, 128, 32, 0),
+    (65536, 256, 4096, 1, 0),
+    (16384, 8192, 2048, 1, 0),
+    (640, 384, 64, 1, 0),          # 15 tiles: not a multiple of the 8 XCDs
+    (512, 512, 512, 3, asl.AS_FLAG_TILE_128),
+    (1024, 768, 256, 5, 0),
+    (8192, 8192, 8192, 1, asl.AS_FLAG_NO_GROUPING),
+]
+
+
+@pytest.mark.parametrize("M,N,K,batch,flags", SHAPES)
+def test_schedule_is_a_bijection(M, N, K, batch, flags):
+    p = asl.gemm_create(M, N, K, batch, (K, 1, M * K), (N, 1, K * N), (N, 1, M * N), flags=flags)
+    tm, tn, _, wg = asl.gemm_plan_info(p)
+    tiles_m, tiles_n = M // tm, N // tn
+    assert wg == batch * tiles_m * tiles_n
+    seen = set()
+    for h in range(wg):
+        b, r, c = asl.gemm_plan_tile_of(p, h)
+        assert 0 <= b < batch and 0 <= r < tiles_m and 0 <= c < tiles_n
+        seen.add((b, r, c))
+    assert len(seen) == wg
+    assert _status(asl.gemm_plan_tile_of, p, wg) == asl.AS_ERR_INVALID
+    asl.gemm_destroy(p)
+
+
+def _xcd_panels(p, wg):
+    """Distinct (batch, tile row) and (batch, tile col) panels each XCD touches."""
+    rows = [set() for _ in range(8)]
+    cols = [set() for _ in range(8)]
+    for h in range(wg):
+        b, r, c = asl.gemm_plan_tile_of(p, h)
+        rows[h % 8].add((b, r))
+        cols[h % 8].add((b, c))
+    return [len(r) for r in rows], [len(c) for c in cols]
+
+
+def test_grouping_concentrates_panels_per_xcd():
+    # 8192^3 with 256^2 tiles: each XCD runs 128 tiles.  Grouped, an XCD's
+    # tiles span at most 24 panels (8 A + 16 B); in row-major identity order
+    # the 128 tiles of an XCD are spread over every row and column.
+    mk = lambda flags: asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192),
+                                       c_t=asl.AS_BF16, flags=flags)
+    g, u = mk(0), mk(asl.AS_FLAG_NO_GROUPING)
+    gr, gc = _xcd_panels(g, 1024)
+    ur, uc = _xcd_panels(u, 1024)
+    assert max(a + b for a, b in zip(gr, gc)) <= 24
+    assert min(a + b for a, b in zip(ur, uc)) >= 32 + 4
+    asl.gemm_destroy(g)
+    asl.gemm_destroy(u)
+
+
+def test_attention_scores_share_whole_slices_per_xcd():
+    # 32 slices of 2048x2048 scores, 64 tiles per slice: every XCD computes 4
+    # whole slices, so each slice's Q and K are fetched by one XCD only.
+    p = asl.gemm_create(2048, 2048, 128, 32, (128, 1, 2048 * 128), (1, 128, 2048 * 128), (2048, 1, 2048 * 2048))
+    slices = [set() for _ in range(8)]
+    for h in range(2048):
+        b, _, _ = asl.gemm_plan_tile_of(p, h)
+        slices[h % 8].add(b)
+    assert all(len(s) == 4 for s in slices)
+    assert len(set().union(*slices)) == 32
+    asl.gemm_destroy(p)
+
+
+def test_sscore_argument_checks():
+    q = (128, 1, 2048 * 128)
+    s = (2048, 1, 2048 * 2048)
+    assert _status(asl.sscore_run, 16, 32, 48, 32, 2048, 2048, 128, (128, 2, 0), q, s) == asl.AS_ERR_UNSUPPORTED
+    assert _status(asl.sscore_run, 16, 32, 48, 0, 2048, 2048, 128, q, q, s) == asl.AS_ERR_INVALID
+    assert _status(asl.sscore_run, 0, 32, 48, 32, 2048, 2048, 128, q, q, s) == asl.AS_ERR_INVALID
+    assert _status(asl.sscore_run, 16, 32, 48, 32, 2048, 2048, 100, (100, 1, 0), (100, 1, 0), s) \
+        == asl.AS_ERR_UNSUPPORTED
+    assert _status(asl.sscore_run, 16, 32, 48, 32, 2048, 2048, 128, q, q, s, asl.AS_F32) == asl.AS_ERR_UNSUPPORTED
+
+
+def test_tilecast_argument_checks():
+    ok = dict(buf=16, rows=4096, cols=4096, tile_m=128, tile_n=64, consumers=256, group=2, grouped=True,
+              iters=10, warmup=0, stride=0, out_checksum=32)
+
+    def st(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(asl.tilecast_run, *a.values())
+
+    assert st(buf=0) == asl.AS_ERR_INVALID
+    assert st(out_checksum=0) == asl.AS_ERR_INVALID
+    assert st(consumers=100) == asl.AS_ERR_INVALID
+    assert st(consumers=8192) == asl.AS_ERR_INVALID
+    assert st(group=3) == asl.AS_ERR_INVALID
+    assert st(group=64) == asl.AS_ERR_INVALID              # grouped: 32 workgroups per XCD
+    assert st(iters=-1) == asl.AS_ERR_INVALID
+    assert st(tile_n=60) == asl.AS_ERR_UNSUPPORTED
+    assert st(tile_m=1024) == asl.AS_ERR_UNSUPPORTED       # 128 KiB tile
+    assert st(rows=4000) == asl.AS_ERR_UNSUPPORTED
+    assert st(buf=24) == asl.AS_ERR_UNSUPPORTED

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: bit-exact where the arithmetic is exact (integer-valued data, identity
+operands, checksums); otherwise |C_gpu - C_ref| <= 1e-3 * sum_k|a*b| + 1e-5
+per element.  Full checks at sizes the oracle finishes in seconds (several
+tiles, odd tile counts); at the full workload sizes, seeded samples of output
+elements that the oracle computes one by one, plus the tile corners.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_scores_amd as asl
+import oracle
+from workloads import WORKLOADS, bits, draw, operands, sample_points
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    asl.lib()  # fails loudly if the HIP library is missing
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def _decode(out: torch.Tensor) -> np.ndarray:
+    return out.detach().float().double().cpu().numpy() if out.dtype == torch.bfloat16 else \
+        out.detach().double().cpu().numpy()
+
+
+def _run_gemm(A, B, M, N, K, batch, sa, sb, out_dtype, flags=0):
+    """Plan + run through the raw C ABI; A, B are CPU bf16 storage tensors."""
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((batch, M, N), dtype=out_dtype, device=DEV)
+    sc = (N, 1, M * N)
+    plan = asl.gemm_create(M, N, K, batch, sa, sb, sc, asl.AS_BF16, asl.AS_BF16,
+                           asl.AS_BF16 if out_dtype == torch.bfloat16 else asl.AS_F32, flags)
+    try:
+        asl.gemm_run(plan, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        asl.gemm_destroy(plan)
+    return C
+
+
+def _layout(M, N, K, batch, a_k, b_k):
+    """Storage shapes and (row, col, batch) strides for A [M,K] and B [K,N]."""
+    if a_k:
+        a_shape, sa = (batch, M, K), (K, 1, M * K)
+    else:
+        a_shape, sa = (batch, K, M), (1, M, M * K)
+    if b_k:
+        b_shape, sb = (batch, N, K), (1, K, N * K)
+    else:
+        b_shape, sb = (batch, K, N), (N, 1, K * N)
+    return a_shape, sa, b_shape, sb
+
+
+# ------------------------------------------------------- exact integer pins --
+
+LAYOUTS = [(ak, bk) for ak in (True, False) for bk in (True, False)]
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("a_k,b_k", LAYOUTS, ids=lambda v: str(v))
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_integer_data_bit_exact(tile, a_k, b_k, out):
+    # integers in [-4, 4]: every fp32 partial sum is exact in any order, so the
+    # fp32 output must equal the oracle exactly and the bf16 output must be its
+    # round-to-nearest-even.  512 x 768 x 320: several tiles, 5 K steps (odd).
+    M, N, K, batch = 512, 768, 320, 2
+    _say("int exact tile=%d a_k=%s b_k=%s out=%s" % (tile, a_k, b_k, out))
+    a_shape, sa, b_shape, sb = _layout(M, N, K, batch, a_k, b_k)
+    A = draw(a_shape, "int", -4, 4, 11 + tile)
+    B = draw(b_shape, "int", -4, 4, 12 + tile)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    flags = asl.AS_FLAG_TILE_256 if tile == 256 else asl.AS_FLAG_TILE_128
+    C = _run_gemm(A, B, M, N, K, batch, sa, sb, od, flags)
+    Cref, _ = oracle.gemm(bits(A), bits(B), batch, M, N, K, sa, sb, want_T=False)
+    if out == "f32":
+        assert np.array_equal(_decode(C), Cref)
+    else:
+        want = oracle.f64_to_bf16_rne_array(Cref)
+        assert np.array_equal(bits(C), want)
+
+
+def test_identity_operand_bit_exact():
+    M = N = K = 512
+    for b_k in (True, False):
+        _say("identity A, b_k=%s" % b_k)
+        a_shape, sa, b_shape, sb = _layout(M, N, K, 1, True, b_k)
+        A = torch.eye(M, dtype=torch.bfloat16).reshape(a_shape)
+        B = draw(b_shape, "normal", 0, 1, 31)
+        C = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32)
+        Bv = B[0] if not b_k else B[0].t()
+        assert torch.equal(C[0].cpu(), Bv.float())
+
+
+def test_odd_tile_count_and_single_k_step():
+    # 640 x 384 with 128 tiles = 15 workgroups (not a multiple of the 8 XCDs), K = 64.
+    M, N, K = 640, 384, 64
+    _say("odd tile count")
+    a_shape, sa, b_shape, sb = _layout(M, N, K, 1, True, False)
+    A = draw(a_shape, "int", -4, 4, 41)
+    B = draw(b_shape, "int", -4, 4, 42)
+    C = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32)
+    Cref, _ = oracle.gemm(bits(A), bits(B), 1, M, N, K, sa, sb, want_T=False)
+    assert np.array_equal(_decode(C), Cref)
+
+
+def test_batch_broadcast_of_B():
+    M, N, K, batch = 256, 256, 128, 3
+    _say("batch broadcast")
+    A = draw((batch, M, K), "int", -4, 4, 51)
+    B = draw((K, N), "int", -4, 4, 52)
+    sa, sb = (K, 1, M * K), (N, 1, 0)
+    C = _run_gemm(A, B, M, N, K, batch, sa, sb, torch.float32)
+    Cref, _ = oracle.gemm(bits(A), bits(B), batch, M, N, K, sa, sb, want_T=False)
+    assert np.array_equal(_decode(C), Cref)
+
+
+# -------------------------------------------------- workloads, full checks --
+
+def _check_full(C, Cref, T):
+    nfail, util = oracle.check(_decode(C).reshape(Cref.shape), Cref, T)
+    assert nfail == 0, "%d elements outside tolerance (max util %.3g)" % (nfail, util)
+    return util
+
+
+def test_gemm512_full():
+    w = WORKLOADS["gemm512"]
+    _say(w.name)
+    A, B = operands(w)
+    C = _run_gemm(A, B, w.M, w.N, w.K, 1, w.a_strides(), w.b_strides(), torch.float32)
+    Cref, T = oracle.gemm(bits(A), bits(B), 1, w.M, w.N, w.K, w.a_strides(), w.b_strides())
+    _check_full(C, Cref, T)
+
+
+@pytest.mark.parametrize("name,M,N,K,batch", [
+    ("gemm8192", 1024, 1024, 1024, 1),
+    ("gemm65536x256x4096", 4096, 256, 1024, 1),
+    ("gemm16384x8192x2048_colA", 1024, 512, 512, 1),
+])
+def test_workload_distribution_reduced_full(name, M, N, K, batch):
+    """Same layouts, value distribution and output type as the full workload, at an oracle-sized shape."""
+    w = WORKLOADS[name]
+    _say("%s reduced %dx%dx%d" % (name, M, N, K))
+    a_k = w.a_major == "row"
+    a_shape, sa, b_shape, sb = _layout(M, N, K, batch, a_k, False)
+    A = draw(a_shape, w.dist, w.lo, w.hi, w.seeds[0] + 1000)
+    B = draw(b_shape, w.dist, w.lo, w.hi, w.seeds[1] + 1000)
+    od = torch.bfloat16 if w.out == "bf16" else torch.float32
+    C = _run_gemm(A, B, M, N, K, batch, sa, sb, od)
+    Cref, T = oracle.gemm(bits(A), bits(B), batch, M, N, K, sa, sb)
+    _check_full(C, Cref, T)
+
+
+@pytest.mark.parametrize("batch,Lq,Lk,d", [(4, 512, 512, 128), (3, 768, 512, 128), (2, 256, 384, 64)])
+def test_sscore_reduced_full(batch, Lq, Lk, d):
+    _say("sscore %dx%dx%dx%d" % (batch, Lq, Lk, d))
+    Q = draw((batch, Lq, d), "normal", 0, 1, 201 + Lq)
+    K = draw((batch, Lk, d), "normal", 0, 1, 202 + Lk)
+    S = asl.sscore(Q.to(DEV), K.to(DEV))
+    torch.cuda.synchronize()
+    Sref, T = oracle.sscore(bits(Q), bits(K), batch, Lq, Lk, d, (d, 1, Lq * d), (d, 1, Lk * d))
+    _check_full(S, Sref, T)
+
+
+def test_sscore_symmetric_when_Q_is_K():
+    b, L, d = 2, 512, 128
+    _say("sscore symmetry")
+    Q = draw((b, L, d), "normal", 0, 1, 211).to(DEV)
+    S = asl.sscore(Q, Q)
+    torch.cuda.synchronize()
+    Sref, T = oracle.sscore(bits(Q), bits(Q), b, L, L, d, (d, 1, L * d), (d, 1, L * d))
+    _check_full(S, Sref, T)
+    s = _decode(S)
+    assert np.all(np.abs(s - np.transpose(s, (0, 2, 1))) <= 2 * (1e-3 * T + 1e-5))
+
+
+# ------------------------------------------------ full sizes, sampled checks --
+
+N_SAMPLES = 4000
+
+
+def _sampled_gemm(w, flags=0, out=None):
+    A, B = operands(w)
+    od = torch.bfloat16 if w.out == "bf16" else torch.float32
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((w.batch, w.M, w.N), dtype=od, device=DEV)
+    plan = asl.gemm_create(w.M, w.N, w.K, w.batch, w.a_strides(), w.b_strides(), (w.N, 1, w.M * w.N),
+                           asl.AS_BF16, asl.AS_BF16, asl.AS_BF16 if w.out == "bf16" else asl.AS_F32, flags)
+    try:
+        asl.gemm_run(plan, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        asl.gemm_destroy(plan)
+    pts = sample_points(w.batch, w.M, w.N, N_SAMPLES, seed=w.seeds[0] * 7)
+    idx = torch.from_numpy(pts).to(DEV)
+    got = _decode(C[idx[:, 0], idx[:, 1], idx[:, 2]])
+    Cref, T = oracle.gemm_points(bits(A), bits(B), pts, w.K, w.a_strides(), w.b_strides(),
+                                 dims=(w.batch, w.M, w.N))
+    nfail, util = oracle.check(got, Cref, T)
+    assert nfail == 0, "%d sampled elements outside tolerance (max util %.3g)" % (nfail, util)
+    return C
+
+
+@pytest.mark.parametrize("name", ["gemm8192", "gemm65536x256x4096", "gemm16384x8192x2048_colA"])
+def test_full_size_sampled(name):
+    w = WORKLOADS[name]
+    _say("%s full size, sampled" % name)
+    _sampled_gemm(w)
+
+
+def test_sscore_full_size_sampled_and_deterministic():
+    w = WORKLOADS["sscore32x2048"]
+    _say("sscore full size")
+    Q, K = operands(w)
+    Qd, Kd = Q.to(DEV), K.to(DEV)
+    S1 = asl.sscore(Qd, Kd)
+    S2 = asl.sscore(Qd, Kd)
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S2)
+    pts = sample_points(w.batch, w.M, w.N, N_SAMPLES, seed=w.seeds[0] * 7)
+    idx = torch.from_numpy(pts).to(DEV)
+    got = _decode(S1[idx[:, 0], idx[:, 1], idx[:, 2]])
+    Sref, T = oracle.sscore_points(bits(Q), bits(K), pts, w.K, w.a_strides(), w.b_strides())
+    nfail, util = oracle.check(got, Sref, T)
+    assert nfail == 0, "%d sampled elements outside tolerance (max util %.3g)" % (nfail, util)
+
+
+def test_grouping_ablation_is_bitwise_identical():
+    # The schedule changes which workgroup computes a tile, never the
+    # arithmetic of the tile: grouped and identity orders agree bit for bit.
+    M = N = K = 2048
+    _say("grouping ablation")
+    A = draw((M, K), "uniform", -1, 1, 61)
+    B = draw((K, N), "uniform", -1, 1, 62)
+    sa, sb = (K, 1, 0), (N, 1, 0)
+    C1 = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.bfloat16, 0)
+    C2 = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.bfloat16, asl.AS_FLAG_NO_GROUPING)
+    assert torch.equal(C1, C2)
+
+
+# ------------------------------------------------------ tile fan-out bench --
+
+@pytest.mark.parametrize("group", [1, 2, 8, 32])
+@pytest.mark.parametrize("grouped", [True, False])
+@pytest.mark.parametrize("streaming", [False, True])
+def test_tilecast_checksums(group, grouped, streaming):
+    rows, cols, tm, tn, consumers, iters = 4096, 4096, 128, 64, 256, 12
+    _say("tilecast G=%d grouped=%s streaming=%s" % (group, grouped, streaming))
+    g = torch.Generator().manual_seed(601)
+    buf = torch.randint(-32768, 32768, (rows, cols), generator=g, dtype=torch.int32).to(torch.int16)
+    stride = consumers // group if streaming else 0
+    out = asl.tilecast(buf.to(DEV).view(torch.bfloat16), tm, tn, consumers, group, grouped, iters, 0, stride)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32).reshape(consumers, 2)
+    b = buf.numpy().view(np.uint16)
+    for w in range(consumers):
+        tot, last = oracle.tilecast_checksum(b, rows, cols, tm, tn, w, consumers, group, grouped, iters, stride)
+        assert (int(got[w, 0]), int(got[w, 1])) == (tot, last), w
