@@ -47,7 +47,7 @@ as_status ok() {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256;
-constexpr int64_t kBK = 64;
+constexpr int64_t kBK = asl::kTileK;
 
 // Rows of tiles per group: minimise the panels one XCD's share of the grid
 // touches (A row-panels + B column-panels), ties broken by the panels its

@@ -51,7 +51,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) i16x8 lds_i16x8_t;
 
-constexpr int kBK = 64;        // K per pipeline step
+constexpr int kBK = kTileK;    // K per pipeline stage (two k16 MFMA substeps)
 constexpr int kWaves = 4;      // 2 x 2
 constexpr int kThreads = 64 * kWaves;
 
@@ -66,15 +66,17 @@ struct KArgs {
     int64_t a_ld, a_bs;   // A: stride of the non-contiguous index, batch stride
     int64_t b_ld, b_bs;
     int64_t c_ld, c_bs;
-    int32_t ktiles;       // K / 64
+    int32_t ktiles;       // K / kBK
     int32_t tiles, tiles_m, tiles_n, group_m, grouped;
 };
 
-// Swizzle of a K-contiguous tile (rows of 64 k = 8 chunks of 16 B): chunk c
-// of row r is stored in slot c ^ swz_k(r).  Any 8 aligned consecutive rows
-// read at one chunk index hit 8 distinct slots, and any 16 hit 16 distinct
-// 16-byte bank groups of a 256-byte bank line.
-__device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Swizzle of a K-contiguous tile (rows of 32 k = 4 chunks of 16 B): chunk c
+// of row r is stored in slot c ^ swz_k(r).  A fragment read touches one
+// chunk index in 32 consecutive rows; with this XOR any 8 consecutive rows
+// fall in 8 distinct 16-byte bank groups of a 128-byte bank line and any 16
+// in 16 distinct groups of a 256-byte line (rows with equal r mod 4 get
+// distinct slots).
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 
 // Swizzle of an MN-contiguous tile (rows are k, CH chunks of 16 B per row):
 // chunk c of row k is stored in slot c ^ swz_mn(k).  The transposing reads
@@ -83,11 +85,17 @@ __device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 template <int CH>
 __device__ __forceinline__ int swz_mn(int k) { return ((k & 3) << 2) & (CH - 1); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kRsrcWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 
-// One operand tile of R (M or N extent) x 64 (K) bf16 per pipeline stage.
+// s_waitcnt immediate for the gfx9 family: vmcnt <= vm (6 bits, split
+// [3:0] and [15:14]), lgkmcnt <= lgkm (4 bits [11:8]), expcnt unconstrained.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
+}
+
+// One operand tile of R (M or N extent) x 32 (K) bf16 per pipeline stage.
 template <int R, bool KMAJ>
 struct OperandTile {
     static constexpr int kBytes = R * kBK * 2;
@@ -100,7 +108,7 @@ struct OperandTile {
     __device__ static uint32_t src_offset(int w, int i, int lane, int64_t ld) {
         int p = (w * kLoadsPerWave + i) * 64 + lane;      // destination chunk index
         if constexpr (KMAJ) {
-            int r = p >> 3, s = p & 7;
+            int r = p >> 2, s = p & 3;
             int c = s ^ swz_k(r);
             return (uint32_t)(((int64_t)r * ld + c * 8) * 2);
         } else {
@@ -110,13 +118,13 @@ struct OperandTile {
         }
     }
 
-    // Fragment for MFMA operand rows/columns [mn0, mn0+32) and k16 step j:
-    // lane l receives 8 consecutive k of row/column mn0 + l%32.
+    // Fragment for MFMA operand rows/columns [mn0, mn0+32) and k16 substep j
+    // (0 or 1): lane l receives 8 consecutive k of row/column mn0 + l%32.
     __device__ static bf16x8 frag(const char* lds, int mn0, int j, int lane) {
         if constexpr (KMAJ) {
             int r = mn0 + (lane & 31);
             int c = 2 * j + (lane >> 5);
-            const lds_i16x8_t* p = (const lds_i16x8_t*)(lds + r * 128 + ((c ^ swz_k(r)) << 4));
+            const lds_i16x8_t* p = (const lds_i16x8_t*)(lds + r * 64 + ((c ^ swz_k(r)) << 4));
             i16x8 v = *p;
             return __builtin_bit_cast(bf16x8, v);
         } else {
@@ -135,25 +143,102 @@ struct OperandTile {
     }
 };
 
-// Request the K step `kt` tiles of A and B into LDS stage `stage`: wave w
-// fills its own 1 KiB rows of the stage, one buffer_load ... lds per KiB.
-template <class OpA, class OpB>
-__device__ __forceinline__ void issue_loads(char* smem, int stage_bytes, int stage, int w,
-                                            const uint16_t* a_src, const uint16_t* b_src,
-                                            const uint32_t* aoff, const uint32_t* boff) {
-    __amdgpu_buffer_rsrc_t ra = make_rsrc(a_src);
-    __amdgpu_buffer_rsrc_t rb = make_rsrc(b_src);
-    char* sa = smem + stage * stage_bytes + w * OpA::kLoadsPerWave * 1024;
-    char* sb = smem + stage * stage_bytes + OpA::kBytes + w * OpB::kLoadsPerWave * 1024;
-#pragma unroll
-    for (int i = 0; i < OpA::kLoadsPerWave; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + i * 1024), 16, aoff[i], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < OpB::kLoadsPerWave; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + i * 1024), 16, boff[i], 0, 0, 0);
+// One 16-byte-per-lane global -> LDS load: lane l's bytes at rsrc base +
+// voff land at LDS address m0 + 16*l.  Issued as inline assembly so that the
+// compiler does not insert its own (conservative) vmcnt waits before later
+// LDS reads; the kernel orders these loads explicitly (s_waitcnt vmcnt + s_barrier).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
-template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// The per-stage global -> LDS loads of one wave: kLoadsPerWave for A then
+// for B, each filling one 1 KiB row of the wave's part of the stage.  With
+// `live` false the resources have no valid range: the loads fetch nothing
+// and only keep the per-stage load count uniform (the buffer is dead).
+template <class OpA, class OpB>
+struct StageLoads {
+    static constexpr int kCount = OpA::kLoadsPerWave + OpB::kLoadsPerWave;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t sa, sb;   // LDS byte addresses of this wave's first A / B row in the stage
+
+    __device__ void setup(const char* dst, int w, const uint16_t* a_src, const uint16_t* b_src, bool live) {
+        ra = make_rsrc(a_src, live ? 0x7fffffff : 0);
+        rb = make_rsrc(b_src, live ? 0x7fffffff : 0);
+        sa = lds_u32(dst + w * OpA::kLoadsPerWave * 1024);
+        sb = lds_u32(dst + OpA::kBytes + w * OpB::kLoadsPerWave * 1024);
+    }
+    __device__ void issue(int i, const uint32_t* aoff, const uint32_t* boff) const {
+        if (i < OpA::kLoadsPerWave) lds_dma16(ra, aoff[i], sa + i * 1024);
+        else lds_dma16(rb, boff[i - OpA::kLoadsPerWave], sb + (i - OpA::kLoadsPerWave) * 1024);
+    }
+};
+
+template <int TM, int TN>
+struct Frags {
+    bf16x8 a[TM];
+    bf16x8 b[TN];
+};
+
+// Fragment unit u of a substep: u < TM is A tile u, else B tile u - TM.
+template <class OpA, class OpB, int TM, int TN>
+__device__ __forceinline__ void read_unit(Frags<TM, TN>& f, int u, const char* stage, int j, int m0, int n0,
+                                          int lane) {
+    if (u < TM) f.a[u] = OpA::frag(stage, m0 + 32 * u, j, lane);
+    else f.b[u - TM] = OpB::frag(stage + OpA::kBytes, n0 + 32 * (u - TM), j, lane);
+}
+
+// One k16 substep: TM*TN MFMAs on fragments `f`; woven between them, the
+// reads of the next fragment set `g` (stage `rd`, substep `j`) and, when
+// `loads` is set, this wave's global -> LDS loads of a future stage.  The
+// scheduling barriers keep that order, so every MFMA has independent work
+// issued next to it and no read waits on a load issued in the same substep.
+template <class OpA, class OpB, int TM, int TN, bool LOADS>
+__device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, TN>& f, Frags<TM, TN>& g,
+                                        const char* rd, int j, int m0, int n0, int lane,
+                                        const StageLoads<OpA, OpB>& ld, const uint32_t* aoff,
+                                        const uint32_t* boff) {
+    constexpr int kMfma = TM * TN;
+    constexpr int kUnits = TM + TN;
+    constexpr int kLoads = StageLoads<OpA, OpB>::kCount;
+#pragma unroll
+    for (int t = 0; t < kMfma; ++t) {
+        const int mi = t / TN, ni = t % TN;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+        if constexpr (LOADS) {
+            if (t < kLoads) ld.issue(t, aoff, boff);
+        }
+        if (t < kUnits) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (LOADS) {
+#pragma unroll
+        for (int t = kMfma; t < kLoads; ++t) ld.issue(t, aoff, boff);
+    }
+#pragma unroll
+    for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
+}
+
+// Pipeline (S LDS buffers, stage kt lives in buffer kt mod S):
+//   prologue  request stages 0..S-1; wait for stage 0; barrier; read the
+//             substep-0 fragments of stage 0.
+//   step kt   substep 0: MFMAs on the substep-0 fragments while the
+//                        substep-1 fragments of stage kt are read;
+//             sync:      this wave's loads of stage kt+1 have landed
+//                        (vmcnt <= the loads of stages kt+2..kt+S-1), its
+//                        LDS reads are done, then a workgroup barrier: every
+//                        wave's part of stage kt+1 is in LDS and nobody
+//                        reads buffer kt mod S any more;
+//             substep 1: request stage kt+S into buffer kt mod S, read the
+//                        substep-0 fragments of stage kt+1, MFMAs on the
+//                        substep-1 fragments.
+// A stage is requested S-1 steps before it is consumed.  Every step issues
+// the same number of loads (stages past the end fetch nothing), so the wait
+// count is a constant.
+template <int TILE, int S, bool A_K, bool B_K, bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     constexpr int WT = TILE / 2;         // wave tile
     constexpr int TM = WT / 32;          // MFMA tiles per wave along M
@@ -161,16 +246,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     using OpA = OperandTile<TILE, A_K>;
     using OpB = OperandTile<TILE, B_K>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+    constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
+    static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
+    __shared__ __attribute__((aligned(1024))) char smem[S * kStage];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = w >> 1, wn = w & 1;
+    const int m0 = wm * WT, n0 = wn * WT;
 
     int bb, tm, tn;
     remap_tile<int>(blockIdx.x, a.tiles, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
 
-    // Tile origins and per-step advance (elements).
+    // Tile origins and per-stage advance (elements).
     const uint16_t* a0 = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE);
     const uint16_t* b0 = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE);
     const int64_t a_step = A_K ? kBK : (int64_t)kBK * a.a_ld;
@@ -182,45 +270,47 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
 #pragma unroll
     for (int i = 0; i < OpB::kLoadsPerWave; ++i) boff[i] = OpB::src_offset(w, i, lane, a.b_ld);
 
-
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    issue_loads<OpA, OpB>(smem, kStage, 0, w, a0, b0, aoff, boff);
+    const int KT = a.ktiles;
+    StageLoads<OpA, OpB> ld;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        ld.setup(smem + s * kStage, w, a0 + (int64_t)s * a_step, b0 + (int64_t)s * b_step, s < KT);
+#pragma unroll
+        for (int i = 0; i < L; ++i) ld.issue(i, aoff, boff);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
+    asm volatile("s_barrier" ::: "memory");
 
-    for (int kt = 0; kt < a.ktiles; ++kt) {
-        const int stage = kt & 1;
-        __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of step kt have landed
-        __syncthreads();                   // ... and every other wave's
+    Frags<TM, TN> f0, f1;
+#pragma unroll
+    for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB>(f0, u, smem, 0, m0, n0, lane);
 
-        const char* sa = smem + stage * kStage;
-        const char* sb = sa + OpA::kBytes;
-        bf16x8 af[TM][4], bfr[TN][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) af[i][j] = OpA::frag(sa, wm * WT + 32 * i, j, lane);
-#pragma unroll
-            for (int i = 0; i < TN; ++i) bfr[i][j] = OpB::frag(sb, wn * WT + 32 * i, j, lane);
-        }
-        // All fragment reads of this stage are issued before the next stage's
-        // loads, so no read waits on them.
+    int cur = 0;                                  // buffer of stage kt
+    const uint16_t* a_next = a0 + (int64_t)S * a_step;
+    const uint16_t* b_next = b0 + (int64_t)S * b_step;
+    for (int kt = 0; kt < KT; ++kt) {
+        char* st = smem + cur * kStage;
+        const int nxt = (cur + 1 == S) ? 0 : cur + 1;
+        // substep 0: MFMAs on f0, read f1 = substep 1 of stage kt
+        substep<OpA, OpB, TM, TN, false>(acc, f0, f1, st, 1, m0, n0, lane, ld, aoff, boff);
+        // stage kt+1 landed everywhere; nobody reads buffer `cur` any more
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < a.ktiles)
-            issue_loads<OpA, OpB>(smem, kStage, stage ^ 1, w, a0 + (int64_t)(kt + 1) * a_step,
-                                  b0 + (int64_t)(kt + 1) * b_step, aoff, boff);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 2), 0));
+        asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi][j], bfr[ni][j], acc[mi][ni], 0, 0, 0);
+        // substep 1: MFMAs on f1, read f0 = substep 0 of stage kt+1, load stage kt+S into `cur`
+        ld.setup(st, w, a_next, b_next, kt + S < KT);
+        substep<OpA, OpB, TM, TN, true>(acc, f1, f0, smem + nxt * kStage, 0, m0, n0, lane, ld, aoff, boff);
+        __builtin_amdgcn_sched_barrier(0);
+        a_next += a_step;
+        b_next += b_step;
+        cur = nxt;
     }
 
     // Epilogue: element e of lane l of MFMA tile (mi, ni) is
@@ -252,9 +342,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     }
 }
 
+constexpr int kStages = 4;
+
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
 int launch_t(const GemmDesc& d, const KArgs& k, hipStream_t s) {
-    gemm_kernel<TILE, A_K, B_K, OUT_BF16><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
+    gemm_kernel<TILE, kStages, A_K, B_K, OUT_BF16><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
     return (int)hipGetLastError();
 }
 

@@ -6,6 +6,9 @@
 
 namespace asl {
 
+// K extent of one pipeline stage; K must be a multiple of it.
+constexpr int kTileK = 32;
+
 // Everything a GEMM launch needs, fixed at plan time.  Strides are elements.
 struct GemmDesc {
     int64_t M, N, K, batch;
