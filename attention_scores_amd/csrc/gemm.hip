@@ -51,7 +51,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) i16x8 lds_i16x8_t;
 
-constexpr int kBK = kTileK;    // K per pipeline stage (two k16 MFMA substeps)
 constexpr int kWaves = 4;      // 2 x 2
 constexpr int kThreads = 64 * kWaves;
 
@@ -66,17 +65,22 @@ struct KArgs {
     int64_t a_ld, a_bs;   // A: stride of the non-contiguous index, batch stride
     int64_t b_ld, b_bs;
     int64_t c_ld, c_bs;
-    int32_t ktiles;       // K / kBK
+    int32_t ktiles;       // K / BK (stages)
     int32_t tiles, tiles_m, tiles_n, group_m, grouped;
 };
 
-// Swizzle of a K-contiguous tile (rows of 32 k = 4 chunks of 16 B): chunk c
-// of row r is stored in slot c ^ swz_k(r).  A fragment read touches one
-// chunk index in 32 consecutive rows; with this XOR any 8 consecutive rows
-// fall in 8 distinct 16-byte bank groups of a 128-byte bank line and any 16
-// in 16 distinct groups of a 256-byte line (rows with equal r mod 4 get
-// distinct slots).
-__device__ __forceinline__ int swz_k(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+// Swizzle of a K-contiguous tile (rows of BK k = CHR chunks of 16 B): chunk
+// c of row r is stored in slot c ^ swz_k<CHR>(r).  A fragment read touches
+// one chunk index in 32 consecutive rows; with these XORs any 8 consecutive
+// rows fall in 8 distinct 16-byte bank groups of a 128-byte bank line and
+// any 16 in 16 distinct groups of a 256-byte line.
+//   CHR = 4 (64-byte rows): rows with equal r mod 4 get distinct slots;
+//   CHR = 8 (128-byte rows): rows with equal r mod 2 get distinct slots.
+template <int CHR>
+__device__ __forceinline__ int swz_k(int r) {
+    if constexpr (CHR == 4) return ((r >> 2) ^ (r >> 1)) & 3;
+    else return (r & 7) ^ ((r >> 3) & 1);
+}
 
 // Swizzle of an MN-contiguous tile (rows are k, CH chunks of 16 B per row):
 // chunk c of row k is stored in slot c ^ swz_mn(k).  The transposing reads
@@ -95,10 +99,11 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
     return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
 }
 
-// One operand tile of R (M or N extent) x 32 (K) bf16 per pipeline stage.
-template <int R, bool KMAJ>
+// One operand tile of R (M or N extent) x BK (K) bf16 per pipeline stage.
+template <int R, bool KMAJ, int BK>
 struct OperandTile {
-    static constexpr int kBytes = R * kBK * 2;
+    static constexpr int kBytes = R * BK * 2;
+    static constexpr int kCHR = BK / 8;                              // chunks per row (K-major)
     static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;   // 1 KiB per wave-wide load
     static constexpr int kCH = R / 8;                                // chunks per row (MN-major)
 
@@ -108,8 +113,8 @@ struct OperandTile {
     __device__ static uint32_t src_offset(int w, int i, int lane, int64_t ld) {
         int p = (w * kLoadsPerWave + i) * 64 + lane;      // destination chunk index
         if constexpr (KMAJ) {
-            int r = p >> 2, s = p & 3;
-            int c = s ^ swz_k(r);
+            int r = p / kCHR, s = p % kCHR;
+            int c = s ^ swz_k<kCHR>(r);
             return (uint32_t)(((int64_t)r * ld + c * 8) * 2);
         } else {
             int k = p / kCH, s = p % kCH;
@@ -119,12 +124,12 @@ struct OperandTile {
     }
 
     // Fragment for MFMA operand rows/columns [mn0, mn0+32) and k16 substep j
-    // (0 or 1): lane l receives 8 consecutive k of row/column mn0 + l%32.
+    // (< BK/16): lane l receives 8 consecutive k of row/column mn0 + l%32.
     __device__ static bf16x8 frag(const char* lds, int mn0, int j, int lane) {
         if constexpr (KMAJ) {
             int r = mn0 + (lane & 31);
             int c = 2 * j + (lane >> 5);
-            const lds_i16x8_t* p = (const lds_i16x8_t*)(lds + r * 64 + ((c ^ swz_k(r)) << 4));
+            const lds_i16x8_t* p = (const lds_i16x8_t*)(lds + r * (BK * 2) + ((c ^ swz_k<kCHR>(r)) << 4));
             i16x8 v = *p;
             return __builtin_bit_cast(bf16x8, v);
         } else {
@@ -191,11 +196,12 @@ __device__ __forceinline__ void read_unit(Frags<TM, TN>& f, int u, const char* s
     else f.b[u - TM] = OpB::frag(stage + OpA::kBytes, n0 + 32 * (u - TM), j, lane);
 }
 
-// One k16 substep: TM*TN MFMAs on fragments `f`; woven between them, the
-// reads of the next fragment set `g` (stage `rd`, substep `j`) and, when
-// `loads` is set, this wave's global -> LDS loads of a future stage.  The
-// scheduling barriers keep that order, so every MFMA has independent work
-// issued next to it and no read waits on a load issued in the same substep.
+// One k16 substep: TM*TN MFMAs on fragments `f`; woven between them, one
+// fragment unit of the next set `g` (stage `rd`, substep `j`) per MFMA and,
+// when `LOADS` is set, one of this wave's global -> LDS loads of a future
+// stage per MFMA.  Scheduling barriers keep that order, so every MFMA has
+// independent work issued next to it and the LDS sees a steady stream of
+// requests rather than bursts.
 template <class OpA, class OpB, int TM, int TN, bool LOADS>
 __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, TN>& f, Frags<TM, TN>& g,
                                         const char* rd, int j, int m0, int n0, int lane,
@@ -222,29 +228,32 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, T
     for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
 }
 
-// Pipeline (S LDS buffers, stage kt lives in buffer kt mod S):
+// Pipeline (S LDS buffers, stage kt lives in buffer kt mod S; a stage is
+// BK deep in K, NS = BK/16 MFMA substeps):
 //   prologue  request stages 0..S-1; wait for stage 0; barrier; read the
 //             substep-0 fragments of stage 0.
-//   step kt   substep 0: MFMAs on the substep-0 fragments while the
-//                        substep-1 fragments of stage kt are read;
+//   step kt   substeps 0..NS-2: MFMAs on the current fragments while the
+//                        next substep's fragments of stage kt are read;
 //             sync:      this wave's loads of stage kt+1 have landed
 //                        (vmcnt <= the loads of stages kt+2..kt+S-1), its
 //                        LDS reads are done, then a workgroup barrier: every
 //                        wave's part of stage kt+1 is in LDS and nobody
 //                        reads buffer kt mod S any more;
-//             substep 1: request stage kt+S into buffer kt mod S, read the
-//                        substep-0 fragments of stage kt+1, MFMAs on the
-//                        substep-1 fragments.
+//             substep NS-1: request stage kt+S into buffer kt mod S, read
+//                        the substep-0 fragments of stage kt+1, MFMAs on the
+//                        last fragments of stage kt.
 // A stage is requested S-1 steps before it is consumed.  Every step issues
 // the same number of loads (stages past the end fetch nothing), so the wait
 // count is a constant.
-template <int TILE, int S, bool A_K, bool B_K, bool OUT_BF16>
+template <int TILE, int BK, int S, bool A_K, bool B_K, bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     constexpr int WT = TILE / 2;         // wave tile
     constexpr int TM = WT / 32;          // MFMA tiles per wave along M
     constexpr int TN = WT / 32;          // ... along N
-    using OpA = OperandTile<TILE, A_K>;
-    using OpB = OperandTile<TILE, B_K>;
+    constexpr int NS = BK / 16;          // k16 substeps per stage
+    static_assert(NS % 2 == 0, "fragment sets alternate; NS must be even");
+    using OpA = OperandTile<TILE, A_K, BK>;
+    using OpB = OperandTile<TILE, B_K, BK>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
@@ -261,8 +270,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     // Tile origins and per-stage advance (elements).
     const uint16_t* a0 = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE);
     const uint16_t* b0 = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE);
-    const int64_t a_step = A_K ? kBK : (int64_t)kBK * a.a_ld;
-    const int64_t b_step = B_K ? kBK : (int64_t)kBK * a.b_ld;
+    const int64_t a_step = A_K ? BK : (int64_t)BK * a.a_ld;
+    const int64_t b_step = B_K ? BK : (int64_t)BK * a.b_ld;
 
     uint32_t aoff[OpA::kLoadsPerWave], boff[OpB::kLoadsPerWave];
 #pragma unroll
@@ -287,9 +296,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
     asm volatile("s_barrier" ::: "memory");
 
-    Frags<TM, TN> f0, f1;
+    Frags<TM, TN> f[2];
 #pragma unroll
-    for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB>(f0, u, smem, 0, m0, n0, lane);
+    for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB>(f[0], u, smem, 0, m0, n0, lane);
 
     int cur = 0;                                  // buffer of stage kt
     const uint16_t* a_next = a0 + (int64_t)S * a_step;
@@ -297,16 +306,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     for (int kt = 0; kt < KT; ++kt) {
         char* st = smem + cur * kStage;
         const int nxt = (cur + 1 == S) ? 0 : cur + 1;
-        // substep 0: MFMAs on f0, read f1 = substep 1 of stage kt
-        substep<OpA, OpB, TM, TN, false>(acc, f0, f1, st, 1, m0, n0, lane, ld, aoff, boff);
+#pragma unroll
+        for (int j = 0; j + 1 < NS; ++j)
+            substep<OpA, OpB, TM, TN, false>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, aoff, boff);
         // stage kt+1 landed everywhere; nobody reads buffer `cur` any more
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 2), 0));
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        // substep 1: MFMAs on f1, read f0 = substep 0 of stage kt+1, load stage kt+S into `cur`
         ld.setup(st, w, a_next, b_next, kt + S < KT);
-        substep<OpA, OpB, TM, TN, true>(acc, f1, f0, smem + nxt * kStage, 0, m0, n0, lane, ld, aoff, boff);
+        substep<OpA, OpB, TM, TN, true>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
+                                        aoff, boff);
         __builtin_amdgcn_sched_barrier(0);
         a_next += a_step;
         b_next += b_step;
@@ -342,11 +352,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     }
 }
 
-constexpr int kStages = 4;
+// Stage depth and ring length: 2 x 64 KiB of LDS for the 256 tile.  A
+// 64-deep stage reads whole 128-byte lines of K-contiguous operands.
+constexpr int kBK = 64;
+constexpr int kStages = 2;
 
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
-int launch_t(const GemmDesc& d, const KArgs& k, hipStream_t s) {
-    gemm_kernel<TILE, kStages, A_K, B_K, OUT_BF16><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
+int launch_t(const GemmDesc& d, KArgs k, hipStream_t s) {
+    k.ktiles = (int32_t)(d.K / kBK);
+    gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
     return (int)hipGetLastError();
 }
 
@@ -388,7 +402,6 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
     k.b_bs = d.b_batch;
     k.c_ld = d.c_row;
     k.c_bs = d.c_batch;
-    k.ktiles = (int32_t)(d.K / kBK);
     k.tiles = (int32_t)d.tiles;
     k.tiles_m = (int32_t)d.tiles_m;
     k.tiles_n = (int32_t)d.tiles_n;

@@ -7,7 +7,7 @@
 namespace asl {
 
 // K extent of one pipeline stage; K must be a multiple of it.
-constexpr int kTileK = 32;
+constexpr int kTileK = 64;
 
 // Everything a GEMM launch needs, fixed at plan time.  Strides are elements.
 struct GemmDesc {

@@ -1,0 +1,283 @@
+"""Benchmark: bf16 GEMM C = A.B at M = N = K = 8192 on one MI355X.
+
+One step = one pass of the hot path over the 8192^3 workload: the planned
+(XCD-grouped) GEMM kernel -- LDS staging, MFMA inner loop and epilogue in one
+launch -- on inputs already resident in HBM.  Plan creation happens once,
+before the timed region.
+
+Prints ONE JSON line with the metric, the kernel's roofline position (HIP
+events on the launch stream; algorithmic flops = 2*M*N*K per launch; peak =
+2.5 PFLOP/s dense bf16), the HBM traffic from the committed rocprofv3 counter
+summary when it was taken on the current kernel source, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+  python bench.py --workload NAME      other workloads (reported, not the headline)
+  python bench.py --tilecast           tile fan-out microbenchmark (JSON lines)
+  python bench.py --profile            short run for rocprofv3 (GEMM + a copy kernel of known size)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+HEADLINE = "gemm8192"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm8192.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_scores_amd", "csrc", f)
+                  for f in ("gemm.hip", "schedule.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return {"read_bytes": float(vals["hbm_read_bytes_per_launch"]),
+                "write_bytes": float(vals["hbm_write_bytes_per_launch"]),
+                "scale": float(vals["copy_scale_factor"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def _gpu_inputs(w, dev):
+    import torch
+    from workloads import operands
+    A, B = operands(w)
+    return A.to(dev), B.to(dev)
+
+
+def _plan(asl, w, flags=0):
+    c_t = asl.AS_BF16 if w.out == "bf16" else asl.AS_F32
+    return asl.gemm_create(w.M, w.N, w.K, w.batch, w.a_strides(), w.b_strides(), (w.N, 1, w.M * w.N),
+                           asl.AS_BF16, asl.AS_BF16, c_t, flags)
+
+
+def time_workload(w, steps, warmup, flags=0):
+    """(wall ms per step, event ms per launch, plan info) for workload w."""
+    import torch
+    import attention_scores_amd as asl
+    dev = torch.device("cuda:0")
+    A, B = _gpu_inputs(w, dev)
+    od = torch.bfloat16 if w.out == "bf16" else torch.float32
+    C = torch.empty((w.batch, w.M, w.N), dtype=od, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    a, b, c = A.data_ptr(), B.data_ptr(), C.data_ptr()
+    if w.kind == "sscore":
+        s_t = asl.AS_BF16 if w.out == "bf16" else asl.AS_F32
+        sq, sk, ss = w.a_strides(), w.b_strides(), (w.N, 1, w.M * w.N)
+        # the plan sscore_run makes internally, for reporting only
+        plan = asl.gemm_create(w.M, w.N, w.K, w.batch, sq, (1, sk[0], sk[2]), ss, asl.AS_BF16, asl.AS_BF16, s_t)
+        info = asl.gemm_plan_info(plan)
+        asl.gemm_destroy(plan)
+
+        def run():
+            asl.sscore_run(a, b, c, w.batch, w.M, w.N, w.K, sq, sk, ss, asl.AS_BF16, s_t, sh)
+    else:
+        plan = _plan(asl, w, flags)
+        info = asl.gemm_plan_info(plan)
+
+        def run():
+            asl.gemm_run(plan, a, b, c, sh)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if w.kind != "sscore":
+        asl.gemm_destroy(plan)
+    wall_ms = (t1 - t0) * 1e3 / steps
+    ev_ms = ev0.elapsed_time(ev1) / steps
+    del A, B, C
+    return wall_ms, ev_ms, info
+
+
+def cpu_baseline(w, target_s=15.0):
+    """The oracle, as it stands, on a bounded row sample of workload w."""
+    import numpy as np
+    import oracle
+    from workloads import bits, operands
+    A, B = operands(w)
+    a, b = bits(A), bits(B)
+    threads = min(16, os.cpu_count() or 1)
+    sa, sb = w.a_strides(), w.b_strides()
+
+    def rows_job(r0, nrows):
+        # rows r0 .. r0+nrows-1 of C: a row-major A slice is a contiguous block
+        if w.a_major != "row":
+            raise ValueError("row sampling needs a row-major A")
+        sub = a.reshape(w.M, w.K)[r0:r0 + nrows]
+        t = time.perf_counter()
+        oracle.gemm(sub, b, 1, nrows, w.N, w.K, sa, sb, want_T=True, nthreads=threads)
+        return time.perf_counter() - t
+
+    probe_rows = threads
+    t_probe = rows_job(0, probe_rows)
+    nrows = max(threads, int(probe_rows * target_s / max(t_probe, 1e-3)) // threads * threads)
+    nrows = min(nrows, w.M - probe_rows)
+    t_main = rows_job(probe_rows, nrows)
+    total_rows = probe_rows + nrows
+    secs = t_probe + t_main
+    flop = 2.0 * total_rows * w.N * w.K
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d output rows of the %dx%dx%d product (fp64 oracle incl. the sum|a*b| pass), "
+                      "%.1f s" % (total_rows, w.M, w.M, w.N, w.K, secs)}
+
+
+def tilecast_report(iters=5000):
+    """Fan-out microbenchmark: grouped vs ungrouped, hot-tile and streaming."""
+    import torch
+    import attention_scores_amd as asl
+    dev = torch.device("cuda:0")
+    lines = []
+    for rows, cols, label in ((4096, 4096, "32MiB"), (32768, 16384, "1GiB")):
+        buf = torch.randint(-32768, 32768, (rows, cols), dtype=torch.int16, device=dev).view(torch.bfloat16)
+        tile_bytes = 128 * 64 * 2
+        for stride_kind in ("hot", "stream"):
+            for group in (1, 2, 4, 8, 16, 32):
+                for grouped in (True, False):
+                    if group == 1 and not grouped:
+                        continue
+                    stride = 0 if stride_kind == "hot" else 256 // group
+                    out = torch.zeros(512, dtype=torch.int32, device=dev)
+                    asl.tilecast(buf, 128, 64, 256, group, grouped, 50, 0, stride, out)
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    asl.tilecast(buf, 128, 64, 256, group, grouped, iters, 0, stride, out)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms = e0.elapsed_time(e1)
+                    delivered = 256 * iters * tile_bytes
+                    lines.append({"bench": "tilecast", "matrix": label, "scenario": stride_kind, "group": group,
+                                  "grouped": grouped, "ms": ms, "delivered_GBps": delivered / ms / 1e6,
+                                  "consumers": 256, "iters": iters, "tile": "128x64 bf16"})
+        del buf
+    return lines
+
+
+def profile_run(steps):
+    """Short run for counter collection: the headline GEMM, then a copy kernel of known size."""
+    import torch
+    from workloads import WORKLOADS
+    w = WORKLOADS[HEADLINE]
+    time_workload(w, steps, 1)
+    n = 1 << 29                                  # 1 GiB of bf16 read, 1 GiB written
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": "done", "gemm_launches": steps + 1, "copy_bytes_each_way": 2 * n,
+                      "copy_launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tilecast", action="store_true")
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--flags", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path; "
+              "got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_scores_amd as asl
+    from workloads import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    asl.lib()
+
+    if args.profile:
+        profile_run(max(1, args.steps))
+        return
+    if args.tilecast:
+        for line in tilecast_report():
+            print(json.dumps(line))
+        return
+
+    w = WORKLOADS[args.workload]
+    wall_ms, ev_ms, info = time_workload(w, args.steps, args.warmup, args.flags)
+    flop = w.flop
+    value = flop / (wall_ms * 1e-3) / 1e12
+    achieved = flop / (ev_ms * 1e-3) / 1e12
+    traffic = read_traffic() if w.name == HEADLINE else None
+    compulsory_read = w.bytes_a + w.bytes_b
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": (traffic["read_bytes"] + traffic["write_bytes"]) if traffic else None,
+                "kernel_ms": round(ev_ms, 4)}
+    if w.name != HEADLINE and w.flop / (w.bytes_a + w.bytes_b + w.bytes_c) < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        gbs = (w.bytes_a + w.bytes_b + w.bytes_c) / (ev_ms * 1e-3) / 1e9
+        roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    out = {
+        "metric": "bf16 GEMM TFLOP/s at 8192^3 (MFMA util %); HBM bytes read / compulsory bytes",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, %s)" % w.dist,
+        "config": {"workload": w.description, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
+                   "tile": "%dx%dx%d" % (info[0], info[1], info[2]), "workgroups": info[3],
+                   "grouping": "none" if args.flags & asl.AS_FLAG_NO_GROUPING else "xcd-grouped"},
+        "roofline": roofline,
+        "mfma_util": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "hbm_read_over_compulsory": (round(traffic["read_bytes"] / compulsory_read, 3) if traffic else None),
+    }
+    if not args.no_cpu_baseline and w.a_major == "row" and w.kind == "gemm":
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -97,7 +97,7 @@ def test_create_refuses_huge_leading_stride():
 
 def test_plan_registry_and_run_argument_checks():
     p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512))
-    assert asl.gemm_plan_info(p) == (128, 128, 32, 16)
+    assert asl.gemm_plan_info(p) == (128, 128, 64, 16)
     assert _status(asl.gemm_run, p, 0, 0, 0) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_run, p, 16, 32, 0) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_run, p, 8, 16, 32) == asl.AS_ERR_UNSUPPORTED          # misaligned
@@ -122,13 +122,13 @@ def test_last_error_is_per_call():
 
 def test_tile_choice():
     p = asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192), c_t=asl.AS_BF16)
-    assert asl.gemm_plan_info(p) == (256, 256, 32, 1024)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024)
     asl.gemm_destroy(p)
     p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512), flags=asl.AS_FLAG_TILE_256)
     assert asl.gemm_plan_info(p)[0] == 256
     asl.gemm_destroy(p)
     p = asl.gemm_create(65536, 256, 4096, 1, RM(65536, 4096), RM(4096, 256), RM(65536, 256))
-    assert asl.gemm_plan_info(p) == (256, 256, 32, 256)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 256)
     asl.gemm_destroy(p)
 
 
