@@ -123,7 +123,11 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     int tile;
     if (flags & AS_FLAG_TILE_256) tile = 256;
     else if (flags & AS_FLAG_TILE_128) tile = 128;
-    else if (M % 256 == 0 && N % 256 == 0 && batch * (M / 256) * (N / 256) >= 128) tile = 256;
+    // 256x256 tiles when K is deep enough to amortise the epilogue and the
+    // grid still fills most CUs; otherwise 128x128 tiles, whose 64 KiB of
+    // LDS lets two workgroups share a CU so one's stores overlap the other's
+    // loads (store-bound shapes such as attention scores with a short K).
+    else if (M % 256 == 0 && N % 256 == 0 && K >= 512 && batch * (M / 256) * (N / 256) >= 128) tile = 256;
     else tile = 128;
     if (M % tile || N % tile || K % kBK)
         return fail(AS_ERR_UNSUPPORTED, "M and N must be multiples of the %dx%d tile and K of %" PRId64

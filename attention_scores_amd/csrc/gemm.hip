@@ -47,9 +47,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) i16x8 lds_i16x8_t;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
 
 constexpr int kWaves = 4;      // 2 x 2
 constexpr int kThreads = 64 * kWaves;
@@ -89,8 +91,15 @@ __device__ __forceinline__ int swz_k(int r) {
 template <int CH>
 __device__ __forceinline__ int swz_mn(int k) { return ((k & 3) << 2) & (CH - 1); }
 
+// Buffer resource over `bytes` bytes at `base`.  The operands are wave
+// uniform by construction; readfirstlane makes that visible to the compiler
+// so the descriptor lives in SGPRs (the loads take it as a scalar operand).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void* q = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 
 // s_waitcnt immediate for the gfx9 family: vmcnt <= vm (6 bits, split
@@ -228,6 +237,61 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, T
     for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
 }
 
+// LDS bytes each wave uses for staging its epilogue chunk (fits 4 waves in
+// the 128 KiB the 256 tile holds, and 4 in the 64 KiB of the 128 tile).
+constexpr int kEpiRegion = 16384 + 1024;
+
+// Write a wave's (WT x WT) accumulator quadrant to C (row r0.., column c0..)
+// through LDS, 32 rows at a time; see the kernel's epilogue note.  The chunk
+// is staged as fp32 in either case; a bf16 result is rounded (to nearest
+// even) right before its store, eight elements per lane.
+template <int TILE, bool OUT_BF16>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[TILE / 64][TILE / 64], char* region, void* Cv,
+                                         int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane) {
+    constexpr int WT = TILE / 2, TM = WT / 32, TN = WT / 32;
+    constexpr int ROWB = WT * 4;                     // bytes of one staged fp32 row
+    // Row stride with padding: rows r and r+4 (the two halves of one wave
+    // write) start 128 bytes apart modulo 256, so the writes are conflict free.
+    constexpr int STRIDE = ROWB + 32;
+    static_assert(32 * STRIDE <= kEpiRegion, "epilogue chunk exceeds the wave's LDS region");
+    constexpr int ELEMS = OUT_BF16 ? 8 : 4;          // elements per lane per store (16 bytes out)
+    constexpr int PPR = WT / ELEMS;                  // pieces per row
+    constexpr int PIECES = 32 * PPR;
+    const int lr = 4 * (lane >> 5), lc = lane & 31;
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 8 * (e >> 2) + lr + (e & 3), col = 32 * ni + lc;
+                *(__attribute__((address_space(3))) float*)(lds_void_t*)(region + row * STRIDE + col * 4) =
+                    acc[mi][ni][e];
+            }
+#pragma unroll
+        for (int q = 0; q < PIECES / 64; ++q) {
+            const int piece = q * 64 + lane;
+            const int row = piece / PPR, cp = piece % PPR;
+            const char* src = region + row * STRIDE + cp * ELEMS * 4;
+            const int64_t gi = c_off + (r0 + 32 * mi + row) * ldc + c0 + cp * ELEMS;
+            if constexpr (OUT_BF16) {
+                const f32x4 lo = *(const lds_f32x4_t*)(lds_void_t*)src;
+                const f32x4 hi = *(const lds_f32x4_t*)(lds_void_t*)(src + 16);
+                bf16x8 o;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    o[k] = (__bf16)lo[k];
+                    o[k + 4] = (__bf16)hi[k];
+                }
+                __builtin_nontemporal_store(__builtin_bit_cast(i16x8, o), (i16x8*)((__bf16*)Cv + gi));
+            } else {
+                const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)src;
+                __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
+            }
+        }
+    }
+}
+
 // Pipeline (S LDS buffers, stage kt lives in buffer kt mod S; a stage is
 // BK deep in K, NS = BK/16 MFMA substeps):
 //   prologue  request stages 0..S-1; wait for stage 0; barrier; read the
@@ -323,33 +387,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
         cur = nxt;
     }
 
-    // Epilogue: element e of lane l of MFMA tile (mi, ni) is
-    // C[row0 + 32*mi + 8*(e/4) + 4*(l/32) + e%4][col0 + 32*ni + l%32].
-    const int64_t row0 = (int64_t)tm * TILE + wm * WT + 4 * (lane >> 5);
-    const int64_t col0 = (int64_t)tn * TILE + wn * WT + (lane & 31);
-    if constexpr (OUT_BF16) {
-        __bf16* c = (__bf16*)a.C + bb * a.c_bs;
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    int64_t r = row0 + 32 * mi + 8 * (e >> 2) + (e & 3);
-                    c[r * a.c_ld + col0 + 32 * ni] = (__bf16)acc[mi][ni][e];
-                }
-    } else {
-        float* c = (float*)a.C + bb * a.c_bs;
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    int64_t r = row0 + 32 * mi + 8 * (e >> 2) + (e & 3);
-                    c[r * a.c_ld + col0 + 32 * ni] = acc[mi][ni][e];
-                }
-    }
+    // Epilogue.  Element e of lane l of MFMA tile (mi, ni) is
+    // C[32*mi + 8*(e/4) + 4*(l/32) + e%4][32*ni + l%32] of the wave's
+    // quadrant: a lane holds 4 consecutive rows of one column, so direct
+    // stores would write 32 contiguous elements per row.  Instead each wave
+    // stages 32-row chunks of its quadrant in its own LDS region (row-major,
+    // padded so the writes are conflict free) and writes every row back as
+    // contiguous 16-byte pieces: 512-byte (fp32) or 256-byte (bf16) runs per
+    // row.  The stores are non-temporal: C is written once and not re-read,
+    // so it should not push A and B out of L2.
+    // Dead loads issued past the last stage may still be landing in LDS, and
+    // other waves may still read the last stage: drain and sync first.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    asm volatile("s_barrier" ::: "memory");
+    epilogue<TILE, OUT_BF16>(acc, smem + w * kEpiRegion, a.C, bb * a.c_bs, (int64_t)tm * TILE + m0,
+                             (int64_t)tn * TILE + n0, a.c_ld, lane);
 }
 
 // Stage depth and ring length: 2 x 64 KiB of LDS for the 256 tile.  A

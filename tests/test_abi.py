@@ -187,11 +187,13 @@ def test_grouping_concentrates_panels_per_xcd():
 
 
 def test_attention_scores_share_whole_slices_per_xcd():
-    # 32 slices of 2048x2048 scores, 64 tiles per slice: every XCD computes 4
-    # whole slices, so each slice's Q and K are fetched by one XCD only.
+    # 32 slices of 2048x2048 scores, 256 tiles of 128x128 per slice: every
+    # XCD computes 4 whole slices, so each slice's Q and K are fetched by one
+    # XCD only.
     p = asl.gemm_create(2048, 2048, 128, 32, (128, 1, 2048 * 128), (1, 128, 2048 * 128), (2048, 1, 2048 * 2048))
+    assert asl.gemm_plan_info(p) == (128, 128, 64, 8192)
     slices = [set() for _ in range(8)]
-    for h in range(2048):
+    for h in range(8192):
         b, _, _ = asl.gemm_plan_tile_of(p, h)
         slices[h % 8].add(b)
     assert all(len(s) == 4 for s in slices)
