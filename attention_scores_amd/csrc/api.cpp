@@ -8,6 +8,8 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <set>
+#include <utility>
 #include <string>
 #include <unordered_set>
 
@@ -49,26 +51,41 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256;
 constexpr int64_t kBK = asl::kTileK;
 
-// Rows of tiles per group: minimise the panels one XCD's share of the grid
-// touches (A row-panels + B column-panels), ties broken by the panels its
-// ~32 concurrently running workgroups touch.
-int choose_group_m(int64_t tiles, int64_t tiles_m, int64_t tiles_n) {
-    int64_t per_batch = tiles_m * tiles_n;
-    int64_t share = (tiles + asl::kXcds - 1) / asl::kXcds;
-    if (share > per_batch) share = per_batch;
+// Rows of tiles per group.  The cost of a candidate is the operand-panel
+// traffic one XCD's L2 would take from memory, estimated on XCD 0's share
+// of the grid: its tiles run 32 at a time (one workgroup per CU); a wave of
+// 32 fetches every A row-panel and B column-panel it touches, unless the
+// whole share's panels fit in the 4 MiB L2 together, in which case each is
+// fetched once.  Ties go to the smaller group.
+int choose_group_m(int64_t tiles, int64_t tiles_m, int64_t tiles_n, int64_t tile, int64_t K) {
+    constexpr int64_t kCusPerXcd = 32;
+    constexpr int64_t kL2Bytes = INT64_C(4) << 20;
+    const int64_t panel_bytes = tile * K * 2;
+    const int64_t q = tiles / asl::kXcds, r = tiles % asl::kXcds;
+    const int64_t share = q + (r > 0 ? 1 : 0);           // XCD 0's tiles: logical [0, share)
     int best = 1;
-    int64_t best_cost = INT64_MAX, best_tie = INT64_MAX;
+    int64_t best_cost = INT64_MAX;
     for (int64_t gm = 1; gm <= tiles_m && gm <= 64; gm *= 2) {
-        int64_t cols = (share + gm - 1) / gm;
-        if (cols > tiles_n) cols = tiles_n;
-        int64_t cost = gm + cols;
-        int64_t ccols = (32 + gm - 1) / gm;
-        if (ccols > tiles_n) ccols = tiles_n;
-        int64_t tie = gm + ccols;
-        if (cost < best_cost || (cost == best_cost && tie < best_tie)) {
+        std::set<std::pair<int64_t, int64_t>> all_a, all_b, wave_a, wave_b;
+        int64_t per_wave = 0;
+        for (int64_t L = 0; L < share; ++L) {
+            int64_t bb, tm, tn;
+            asl::remap_tile<int64_t>(L * asl::kXcds, tiles, tiles_m, tiles_n, gm, true, bb, tm, tn);
+            all_a.insert({bb, tm});
+            all_b.insert({bb, tn});
+            wave_a.insert({bb, tm});
+            wave_b.insert({bb, tn});
+            if ((L + 1) % kCusPerXcd == 0 || L + 1 == share) {
+                per_wave += (int64_t)(wave_a.size() + wave_b.size());
+                wave_a.clear();
+                wave_b.clear();
+            }
+        }
+        const int64_t whole = (int64_t)(all_a.size() + all_b.size());
+        const int64_t cost = (whole * panel_bytes <= kL2Bytes) ? whole : per_wave;
+        if (cost < best_cost) {
             best = (int)gm;
             best_cost = cost;
-            best_tie = tie;
         }
     }
     return best;
@@ -146,7 +163,7 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
     d.tiles = batch * d.tiles_m * d.tiles_n;
     d.grouped = !(flags & AS_FLAG_NO_GROUPING);
-    d.group_m = choose_group_m(d.tiles, d.tiles_m, d.tiles_n);
+    d.group_m = choose_group_m(d.tiles, d.tiles_m, d.tiles_n, tile, K);
     *out = d;
     return AS_OK;
 }

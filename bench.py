@@ -189,11 +189,11 @@ def tilecast_report(iters=5000):
     return lines
 
 
-def profile_run(steps):
-    """Short run for counter collection: the headline GEMM, then a copy kernel of known size."""
+def profile_run(steps, name=HEADLINE):
+    """Short run for counter collection: one workload, then a copy kernel of known size."""
     import torch
     from workloads import WORKLOADS
-    w = WORKLOADS[HEADLINE]
+    w = WORKLOADS[name]
     time_workload(w, steps, 1)
     n = 1 << 29                                  # 1 GiB of bf16 read, 1 GiB written
     src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
@@ -232,7 +232,7 @@ def main():
     asl.lib()
 
     if args.profile:
-        profile_run(max(1, args.steps))
+        profile_run(max(1, args.steps), args.workload)
         return
     if args.tilecast:
         for line in tilecast_report():

@@ -160,30 +160,42 @@ def test_schedule_is_a_bijection(M, N, K, batch, flags):
     asl.gemm_destroy(p)
 
 
-def _xcd_panels(p, wg):
-    """Distinct (batch, tile row) and (batch, tile col) panels each XCD touches."""
-    rows = [set() for _ in range(8)]
-    cols = [set() for _ in range(8)]
-    for h in range(wg):
-        b, r, c = asl.gemm_plan_tile_of(p, h)
-        rows[h % 8].add((b, r))
-        cols[h % 8].add((b, c))
-    return [len(r) for r in rows], [len(c) for c in cols]
+def _wave_panels(p, wg, cus_per_xcd=32):
+    """Largest number of (batch, tile row) + (batch, tile col) panels that the
+    workgroups of one XCD running together (32 consecutive slots) touch."""
+    worst = 0
+    for x in range(8):
+        hs = list(range(x, wg, 8))
+        for w0 in range(0, len(hs), cus_per_xcd):
+            rows, cols = set(), set()
+            for h in hs[w0:w0 + cus_per_xcd]:
+                b, r, c = asl.gemm_plan_tile_of(p, h)
+                rows.add((b, r))
+                cols.add((b, c))
+            worst = max(worst, len(rows) + len(cols))
+    return worst
 
 
-def test_grouping_concentrates_panels_per_xcd():
-    # 8192^3 with 256^2 tiles: each XCD runs 128 tiles.  Grouped, an XCD's
-    # tiles span at most 24 panels (8 A + 16 B); in row-major identity order
-    # the 128 tiles of an XCD are spread over every row and column.
-    mk = lambda flags: asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192),
-                                       c_t=asl.AS_BF16, flags=flags)
-    g, u = mk(0), mk(asl.AS_FLAG_NO_GROUPING)
-    gr, gc = _xcd_panels(g, 1024)
-    ur, uc = _xcd_panels(u, 1024)
-    assert max(a + b for a, b in zip(gr, gc)) <= 24
-    assert min(a + b for a, b in zip(ur, uc)) >= 32 + 4
-    asl.gemm_destroy(g)
-    asl.gemm_destroy(u)
+@pytest.mark.parametrize("M,N,K,sa", [(8192, 8192, 8192, (8192, 1, 0)), (16384, 8192, 2048, (1, 16384, 0))])
+def test_concurrent_tiles_touch_few_panels(M, N, K, sa):
+    # 32 tiles that run at once on an XCD can touch as few as 4 A + 8 B (or
+    # 8 + 4) panels; the plan's group size must reach that minimum.
+    p = asl.gemm_create(M, N, K, 1, sa, (N, 1, 0), (N, 1, 0), c_t=asl.AS_BF16)
+    assert asl.gemm_plan_info(p)[0] == 256
+    assert _wave_panels(p, asl.gemm_plan_info(p)[3]) <= 12
+    asl.gemm_destroy(p)
+
+
+def test_grouping_keeps_slices_on_one_xcd_identity_spreads_them():
+    args = (2048, 2048, 128, 32, (128, 1, 2048 * 128), (1, 128, 2048 * 128), (2048, 1, 2048 * 2048))
+    for flags, want in ((0, 4), (asl.AS_FLAG_NO_GROUPING, 32)):
+        p = asl.gemm_create(*args, flags=flags)
+        wg = asl.gemm_plan_info(p)[3]
+        per_xcd = [set() for _ in range(8)]
+        for h in range(wg):
+            per_xcd[h % 8].add(asl.gemm_plan_tile_of(p, h)[0])
+        assert all(len(sl) == want for sl in per_xcd), (flags, [len(sl) for sl in per_xcd])
+        asl.gemm_destroy(p)
 
 
 def test_attention_scores_share_whole_slices_per_xcd():
