@@ -26,6 +26,7 @@ AS_BF16, AS_F32 = 0, 1
 AS_FLAG_NO_GROUPING = 0x1
 AS_FLAG_TILE_128 = 0x2
 AS_FLAG_TILE_256 = 0x4
+AS_FLAG_PERSISTENT = 0x8
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
             "sscore_run", "tilecast_run", "as_status_str", "as_last_error")
@@ -72,7 +73,7 @@ def lib() -> ctypes.CDLL:
         L.gemm_destroy.argtypes = [vp]
         L.gemm_destroy.restype = ctypes.c_int
         L.gemm_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32),
-                                     ctypes.POINTER(i64)]
+                                     ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.gemm_plan_info.restype = ctypes.c_int
         L.gemm_plan_tile_of.argtypes = [vp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.gemm_plan_tile_of.restype = ctypes.c_int
@@ -122,14 +123,18 @@ def gemm_destroy(plan: int) -> None:
 
 
 def gemm_plan_info(plan: int):
-    tm, tn, tk, wg = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
-    _check(lib().gemm_plan_info(plan, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(tk), ctypes.byref(wg)))
-    return tm.value, tn.value, tk.value, wg.value
+    """(tile_m, tile_n, tile_k, tiles, workgroups) the plan chose."""
+    tm, tn, tk = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    nt, wg = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().gemm_plan_info(plan, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(tk), ctypes.byref(nt),
+                                ctypes.byref(wg)))
+    return tm.value, tn.value, tk.value, nt.value, wg.value
 
 
-def gemm_plan_tile_of(plan: int, workgroup: int):
+def gemm_plan_tile_of(plan: int, slot: int):
+    """(batch, tile row, tile column) computed in execution slot `slot` (runs on XCD slot % 8)."""
     b, r, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    _check(lib().gemm_plan_tile_of(plan, workgroup, ctypes.byref(b), ctypes.byref(r), ctypes.byref(c)))
+    _check(lib().gemm_plan_tile_of(plan, slot, ctypes.byref(b), ctypes.byref(r), ctypes.byref(c)))
     return b.value, r.value, c.value
 
 

@@ -8,7 +8,8 @@
 #include <cstring>
 #include <mutex>
 #include <new>
-#include <set>
+#include <vector>
+#include <algorithm>
 #include <utility>
 #include <string>
 #include <unordered_set>
@@ -48,40 +49,45 @@ as_status ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256;
+constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 | AS_FLAG_PERSISTENT;
 constexpr int64_t kBK = asl::kTileK;
+constexpr int64_t kCus = 256;   // MI355X compute units
 
 // Rows of tiles per group.  The cost of a candidate is the operand-panel
 // traffic one XCD's L2 would take from memory, estimated on XCD 0's share
 // of the grid: its tiles run 32 at a time (one workgroup per CU); a wave of
 // 32 fetches every A row-panel and B column-panel it touches, unless the
 // whole share's panels fit in the 4 MiB L2 together, in which case each is
-// fetched once.  Ties go to the smaller group.
+// fetched once.  Ties go to the smaller group.  Panels are counted with
+// stamp arrays (the logical order is batch-major, so a panel (b, row) is new
+// to the share when its row was last stamped with an earlier batch), which
+// keeps the simulation linear in the share.
 int choose_group_m(int64_t tiles, int64_t tiles_m, int64_t tiles_n, int64_t tile, int64_t K) {
     constexpr int64_t kCusPerXcd = 32;
     constexpr int64_t kL2Bytes = INT64_C(4) << 20;
     const int64_t panel_bytes = tile * K * 2;
     const int64_t q = tiles / asl::kXcds, r = tiles % asl::kXcds;
     const int64_t share = q + (r > 0 ? 1 : 0);           // XCD 0's tiles: logical [0, share)
+    std::vector<int64_t> all_a(tiles_m), all_b(tiles_n), wave_a(tiles_m), wave_b(tiles_n);
     int best = 1;
     int64_t best_cost = INT64_MAX;
     for (int64_t gm = 1; gm <= tiles_m && gm <= 64; gm *= 2) {
-        std::set<std::pair<int64_t, int64_t>> all_a, all_b, wave_a, wave_b;
-        int64_t per_wave = 0;
+        std::fill(all_a.begin(), all_a.end(), -1);
+        std::fill(all_b.begin(), all_b.end(), -1);
+        std::fill(wave_a.begin(), wave_a.end(), -1);
+        std::fill(wave_b.begin(), wave_b.end(), -1);
+        int64_t whole = 0, per_wave = 0;
         for (int64_t L = 0; L < share; ++L) {
             int64_t bb, tm, tn;
-            asl::remap_tile<int64_t>(L * asl::kXcds, tiles, tiles_m, tiles_n, gm, true, bb, tm, tn);
-            all_a.insert({bb, tm});
-            all_b.insert({bb, tn});
-            wave_a.insert({bb, tm});
-            wave_b.insert({bb, tn});
-            if ((L + 1) % kCusPerXcd == 0 || L + 1 == share) {
-                per_wave += (int64_t)(wave_a.size() + wave_b.size());
-                wave_a.clear();
-                wave_b.clear();
-            }
+            asl::logical_tile<int64_t>(L, tiles_m, tiles_n, gm, true, bb, tm, tn);
+            // (wave, batch) stamp; a wave spans at most a few batches and L
+            // only grows, so equal stamps mean the same panel of this wave.
+            const int64_t ws = (L / kCusPerXcd) * (share + 1) + bb;
+            if (all_a[tm] != bb) { all_a[tm] = bb; ++whole; }
+            if (all_b[tn] != bb) { all_b[tn] = bb; ++whole; }
+            if (wave_a[tm] != ws) { wave_a[tm] = ws; ++per_wave; }
+            if (wave_b[tn] != ws) { wave_b[tn] = ws; ++per_wave; }
         }
-        const int64_t whole = (int64_t)(all_a.size() + all_b.size());
         const int64_t cost = (whole * panel_bytes <= kL2Bytes) ? whole : per_wave;
         if (cost < best_cost) {
             best = (int)gm;
@@ -163,6 +169,12 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
     d.tiles = batch * d.tiles_m * d.tiles_n;
     d.grouped = !(flags & AS_FLAG_NO_GROUPING);
+    // One workgroup per tile, or with AS_FLAG_PERSISTENT as many as stay
+    // resident (one per CU for the 256 tile's 145 KiB of LDS, two for the
+    // 128 tile), each walking its XCD's tiles with the LDS ring streaming
+    // across tile boundaries.
+    const int64_t resident = (tile == 256 ? 1 : 2) * kCus;
+    d.grid = (flags & AS_FLAG_PERSISTENT) && d.tiles > resident ? resident : d.tiles;
     d.group_m = choose_group_m(d.tiles, d.tiles_m, d.tiles_n, tile, K);
     *out = d;
     return AS_OK;
@@ -219,13 +231,14 @@ as_status gemm_destroy(as_gemm_t plan) {
     return ok();
 }
 
-as_status gemm_plan_info(as_gemm_t plan, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,
+as_status gemm_plan_info(as_gemm_t plan, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k, int64_t* tiles,
                          int64_t* workgroups) {
     if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
     if (tile_m) *tile_m = plan->d.tile;
     if (tile_n) *tile_n = plan->d.tile;
     if (tile_k) *tile_k = (int32_t)kBK;
-    if (workgroups) *workgroups = plan->d.tiles;
+    if (tiles) *tiles = plan->d.tiles;
+    if (workgroups) *workgroups = plan->d.grid;
     return ok();
 }
 
@@ -233,8 +246,9 @@ as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* batch, i
                             int64_t* tile_col) {
     if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
     if (workgroup < 0 || workgroup >= plan->d.tiles || !batch || !tile_row || !tile_col)
-        return fail(AS_ERR_INVALID, "workgroup out of range or null output");
-    asl::tile_of_workgroup(plan->d, workgroup, batch, tile_row, tile_col);
+        return fail(AS_ERR_INVALID, "execution slot out of range or null output");
+    if (!asl::tile_of_slot(plan->d, workgroup, batch, tile_row, tile_col))
+        return fail(AS_ERR_INVALID, "execution slot %" PRId64 " is empty", workgroup);
     return ok();
 }
 
@@ -249,9 +263,26 @@ as_status sscore_run(const void* Q, const void* K, void* S,
     // S = Q . K^T: A = Q, B[d, j] = K[j, d] (row stride 1, column stride k.row).
     as_strides a = {q.row, 1, q.batch};
     as_strides b = {1, k.row, k.batch};
+    // Plans depend only on the sizes, strides and types: a few recent ones
+    // are kept per thread, so a loop of calls plans once.
+    struct Cached {
+        int64_t key[14];
+        asl::GemmDesc d;
+    };
+    thread_local Cached cache[8];
+    thread_local int cached = 0, next_slot = 0;
+    const int64_t key[14] = {batch, Lq, Lk, dim, q.row, q.col, q.batch, k.row, k.col, k.batch,
+                             s.row, s.batch, (int64_t)qk_t, (int64_t)s_t};
+    for (int i = 0; i < cached; ++i)
+        if (std::memcmp(cache[i].key, key, sizeof key) == 0) return run_desc(cache[i].d, Q, K, S, hip_stream);
     asl::GemmDesc d;
     as_status st = plan_desc(&d, Lq, Lk, dim, batch, a, b, s, qk_t, qk_t, s_t, 0);
     if (st != AS_OK) return st;
+    Cached& slot = cache[next_slot];
+    std::memcpy(slot.key, key, sizeof key);
+    slot.d = d;
+    next_slot = (next_slot + 1) % 8;
+    if (cached < 8) ++cached;
     return run_desc(d, Q, K, S, hip_stream);
 }
 

@@ -237,75 +237,128 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, T
     for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
 }
 
-// LDS bytes each wave uses for staging its epilogue chunk (fits 4 waves in
-// the 128 KiB the 256 tile holds, and 4 in the 64 KiB of the 128 tile).
-constexpr int kEpiRegion = 16384 + 1024;
+// Epilogue staging region of one wave: ROWS rows of the wave's quadrant as
+// fp32 with a padded row stride (rows r and r+4 -- the two halves of one wave
+// write -- start 128 bytes apart modulo 256, so the writes are conflict
+// free).  A tile followed by another tile of the same workgroup stages 8 rows
+// at a time in a region past the LDS ring, so the next tile's stages can
+// stream in meanwhile; a workgroup's last tile stages 32 rows at a time in
+// the then idle ring (fewer LDS round trips per tile).
+template <int TILE, int ROWS>
+struct EpiRegion {
+    static constexpr int kStride = (TILE / 2) * 4 + 32;
+    static constexpr int kBytes = ROWS * kStride;
+};
 
 // Write a wave's (WT x WT) accumulator quadrant to C (row r0.., column c0..)
-// through LDS, 32 rows at a time; see the kernel's epilogue note.  The chunk
-// is staged as fp32 in either case; a bf16 result is rounded (to nearest
-// even) right before its store, eight elements per lane.
-template <int TILE, bool OUT_BF16>
+// through its LDS region, ROWS rows at a time.  Element e of lane l of MFMA
+// tile (mi, ni) is row 32*mi + 8*(e/4) + 4*(l/32) + e%4, column 32*ni + l%32
+// of the quadrant: a lane holds 4 consecutive rows of one column, so direct
+// stores would write only 32 contiguous elements per row.  Staged, every row
+// goes out as contiguous 16-byte pieces: 512-byte (fp32) or 256-byte (bf16,
+// rounded to nearest even right before its store) runs.  The stores are
+// non-temporal: C is written once and not re-read, so it should not push A
+// and B out of L2.
+template <int TILE, int ROWS, bool OUT_BF16>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TILE / 64][TILE / 64], char* region, void* Cv,
                                          int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane) {
     constexpr int WT = TILE / 2, TM = WT / 32, TN = WT / 32;
-    constexpr int ROWB = WT * 4;                     // bytes of one staged fp32 row
-    // Row stride with padding: rows r and r+4 (the two halves of one wave
-    // write) start 128 bytes apart modulo 256, so the writes are conflict free.
-    constexpr int STRIDE = ROWB + 32;
-    static_assert(32 * STRIDE <= kEpiRegion, "epilogue chunk exceeds the wave's LDS region");
+    constexpr int STRIDE = EpiRegion<TILE, ROWS>::kStride;
     constexpr int ELEMS = OUT_BF16 ? 8 : 4;          // elements per lane per store (16 bytes out)
     constexpr int PPR = WT / ELEMS;                  // pieces per row
-    constexpr int PIECES = 32 * PPR;
+    constexpr int PIECES = ROWS * PPR;
+    constexpr int H = 32 / ROWS;                     // chunks per MFMA row block
+    static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "chunks are whole 8-row groups of a row block");
+    static_assert(PIECES % 64 == 0, "epilogue pieces must fill whole wave stores");
     const int lr = 4 * (lane >> 5), lc = lane & 31;
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni)
+        for (int h = 0; h < H; ++h) {            // rows ROWS*h .. ROWS*h+ROWS-1 of MFMA row block mi
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = 8 * (e >> 2) + lr + (e & 3), col = 32 * ni + lc;
-                *(__attribute__((address_space(3))) float*)(lds_void_t*)(region + row * STRIDE + col * 4) =
-                    acc[mi][ni][e];
-            }
+            for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-        for (int q = 0; q < PIECES / 64; ++q) {
-            const int piece = q * 64 + lane;
-            const int row = piece / PPR, cp = piece % PPR;
-            const char* src = region + row * STRIDE + cp * ELEMS * 4;
-            const int64_t gi = c_off + (r0 + 32 * mi + row) * ldc + c0 + cp * ELEMS;
-            if constexpr (OUT_BF16) {
-                const f32x4 lo = *(const lds_f32x4_t*)(lds_void_t*)src;
-                const f32x4 hi = *(const lds_f32x4_t*)(lds_void_t*)(src + 16);
-                bf16x8 o;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    o[k] = (__bf16)lo[k];
-                    o[k + 4] = (__bf16)hi[k];
+                for (int e = (ROWS / 8) * 4 * h; e < (ROWS / 8) * 4 * (h + 1); ++e) {
+                    const int row = 8 * (e >> 2) - ROWS * h + lr + (e & 3), col = 32 * ni + lc;
+                    *(__attribute__((address_space(3))) float*)(lds_void_t*)(region + row * STRIDE + col * 4) =
+                        acc[mi][ni][e];
                 }
-                __builtin_nontemporal_store(__builtin_bit_cast(i16x8, o), (i16x8*)((__bf16*)Cv + gi));
-            } else {
-                const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)src;
-                __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
+#pragma unroll
+            for (int q = 0; q < PIECES / 64; ++q) {
+                const int piece = q * 64 + lane;
+                const int row = piece / PPR, cp = piece % PPR;
+                const char* src = region + row * STRIDE + cp * ELEMS * 4;
+                const int64_t gi = c_off + (r0 + 32 * mi + ROWS * h + row) * ldc + c0 + cp * ELEMS;
+                if constexpr (OUT_BF16) {
+                    const f32x4 lo = *(const lds_f32x4_t*)(lds_void_t*)src;
+                    const f32x4 hi = *(const lds_f32x4_t*)(lds_void_t*)(src + 16);
+                    bf16x8 o;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        o[k] = (__bf16)lo[k];
+                        o[k + 4] = (__bf16)hi[k];
+                    }
+                    __builtin_nontemporal_store(__builtin_bit_cast(i16x8, o), (i16x8*)((__bf16*)Cv + gi));
+                } else {
+                    const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)src;
+                    __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
+                }
             }
         }
     }
 }
 
-// Pipeline (S LDS buffers, stage kt lives in buffer kt mod S; a stage is
-// BK deep in K, NS = BK/16 MFMA substeps):
+// Cursor over the stream of stages a workgroup loads: tile t (logical),
+// stage k of it, and the global origins of that stage's A and B tiles.
+template <int TILE, int BK, bool A_K, bool B_K>
+struct StageCursor {
+    const KArgs& a;
+    int t, k, stride, end;
+    int64_t a_step, b_step;
+    const uint16_t *pa, *pb;
+
+    __device__ StageCursor(const KArgs& args, int first, int stride_, int end_)
+        : a(args), t(first), k(0), stride(stride_), end(end_) {
+        a_step = A_K ? BK : (int64_t)BK * a.a_ld;
+        b_step = B_K ? BK : (int64_t)BK * a.b_ld;
+        origins();
+    }
+    __device__ bool live() const { return t < end; }
+    __device__ void origins() {
+        int bb, tm, tn;
+        logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
+        pa = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE);
+        pb = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE);
+    }
+    __device__ void advance() {
+        if (++k == a.ktiles) {
+            k = 0;
+            t += stride;
+            if (t < end) origins();
+        } else {
+            pa += a_step;
+            pb += b_step;
+        }
+    }
+};
+
+// Pipeline (S LDS buffers; a stage is BK deep in K, NS = BK/16 MFMA
+// substeps).  The stages of all the tiles a workgroup visits form one
+// stream; stream stage g lives in buffer g mod S.
 //   prologue  request stages 0..S-1; wait for stage 0; barrier; read the
 //             substep-0 fragments of stage 0.
-//   step kt   substeps 0..NS-2: MFMAs on the current fragments while the
-//                        next substep's fragments of stage kt are read;
-//             sync:      this wave's loads of stage kt+1 have landed
-//                        (vmcnt <= the loads of stages kt+2..kt+S-1), its
+//   step g    substeps 0..NS-2: MFMAs on the current fragments while the
+//                        next substep's fragments of stage g are read;
+//             sync:      this wave's loads of stage g+1 have landed
+//                        (vmcnt <= the loads of stages g+2..g+S-1), its
 //                        LDS reads are done, then a workgroup barrier: every
-//                        wave's part of stage kt+1 is in LDS and nobody
-//                        reads buffer kt mod S any more;
-//             substep NS-1: request stage kt+S into buffer kt mod S, read
-//                        the substep-0 fragments of stage kt+1, MFMAs on the
-//                        last fragments of stage kt.
+//                        wave's part of stage g+1 is in LDS and nobody
+//                        reads buffer g mod S any more;
+//             substep NS-1: request stage g+S into buffer g mod S, read the
+//                        substep-0 fragments of stage g+1, MFMAs on the
+//                        last fragments of stage g.
+// After a tile's last step its accumulators go out through the wave's own
+// epilogue region while the next tile's first stages are already landing.
 // A stage is requested S-1 steps before it is consumed.  Every step issues
 // the same number of loads (stages past the end fetch nothing), so the wait
 // count is a constant.
@@ -321,41 +374,37 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
-    __shared__ __attribute__((aligned(1024))) char smem[S * kStage];
+    using Epi8 = EpiRegion<TILE, 8>;
+    using Epi32 = EpiRegion<TILE, 32>;
+    static_assert(kWaves * Epi32::kBytes <= S * kStage, "last-tile epilogue must fit in the ring");
+    __shared__ __attribute__((aligned(1024))) char smem[S * kStage + kWaves * Epi8::kBytes];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = w >> 1, wn = w & 1;
     const int m0 = wm * WT, n0 = wn * WT;
+    char* const epi = smem + S * kStage + w * Epi8::kBytes;
 
-    int bb, tm, tn;
-    remap_tile<int>(blockIdx.x, a.tiles, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
+    // The logical tiles this workgroup visits: first, first + stride, ... < end.
+    int first, stride, end;
+    tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, a.grouped != 0, first, stride, end);
+    if (first >= end) return;
 
-    // Tile origins and per-stage advance (elements).
-    const uint16_t* a0 = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE);
-    const uint16_t* b0 = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE);
-    const int64_t a_step = A_K ? BK : (int64_t)BK * a.a_ld;
-    const int64_t b_step = B_K ? BK : (int64_t)BK * a.b_ld;
-
+    StageCursor<TILE, BK, A_K, B_K> cur_ld(a, first, stride, end);
     uint32_t aoff[OpA::kLoadsPerWave], boff[OpB::kLoadsPerWave];
 #pragma unroll
     for (int i = 0; i < OpA::kLoadsPerWave; ++i) aoff[i] = OpA::src_offset(w, i, lane, a.a_ld);
 #pragma unroll
     for (int i = 0; i < OpB::kLoadsPerWave; ++i) boff[i] = OpB::src_offset(w, i, lane, a.b_ld);
 
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-
     const int KT = a.ktiles;
     StageLoads<OpA, OpB> ld;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        ld.setup(smem + s * kStage, w, a0 + (int64_t)s * a_step, b0 + (int64_t)s * b_step, s < KT);
+        ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.live());
 #pragma unroll
         for (int i = 0; i < L; ++i) ld.issue(i, aoff, boff);
+        cur_ld.advance();
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
     asm volatile("s_barrier" ::: "memory");
@@ -364,44 +413,49 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
 #pragma unroll
     for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB>(f[0], u, smem, 0, m0, n0, lane);
 
-    int cur = 0;                                  // buffer of stage kt
-    const uint16_t* a_next = a0 + (int64_t)S * a_step;
-    const uint16_t* b_next = b0 + (int64_t)S * b_step;
-    for (int kt = 0; kt < KT; ++kt) {
-        char* st = smem + cur * kStage;
-        const int nxt = (cur + 1 == S) ? 0 : cur + 1;
+    int cur = 0;                                  // buffer of the current stage
+    for (int t = first; t < end; t += stride) {
+        f32x16 acc[TM][TN];
 #pragma unroll
-        for (int j = 0; j + 1 < NS; ++j)
-            substep<OpA, OpB, TM, TN, false>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, aoff, boff);
-        // stage kt+1 landed everywhere; nobody reads buffer `cur` any more
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 2), 0));
-        asm volatile("s_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        ld.setup(st, w, a_next, b_next, kt + S < KT);
-        substep<OpA, OpB, TM, TN, true>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
-                                        aoff, boff);
-        __builtin_amdgcn_sched_barrier(0);
-        a_next += a_step;
-        b_next += b_step;
-        cur = nxt;
-    }
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    // Epilogue.  Element e of lane l of MFMA tile (mi, ni) is
-    // C[32*mi + 8*(e/4) + 4*(l/32) + e%4][32*ni + l%32] of the wave's
-    // quadrant: a lane holds 4 consecutive rows of one column, so direct
-    // stores would write 32 contiguous elements per row.  Instead each wave
-    // stages 32-row chunks of its quadrant in its own LDS region (row-major,
-    // padded so the writes are conflict free) and writes every row back as
-    // contiguous 16-byte pieces: 512-byte (fp32) or 256-byte (bf16) runs per
-    // row.  The stores are non-temporal: C is written once and not re-read,
-    // so it should not push A and B out of L2.
-    // Dead loads issued past the last stage may still be landing in LDS, and
-    // other waves may still read the last stage: drain and sync first.
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-    asm volatile("s_barrier" ::: "memory");
-    epilogue<TILE, OUT_BF16>(acc, smem + w * kEpiRegion, a.C, bb * a.c_bs, (int64_t)tm * TILE + m0,
-                             (int64_t)tn * TILE + n0, a.c_ld, lane);
+        for (int kt = 0; kt < KT; ++kt) {
+            char* st = smem + cur * kStage;
+            const int nxt = (cur + 1 == S) ? 0 : cur + 1;
+#pragma unroll
+            for (int j = 0; j + 1 < NS; ++j)
+                substep<OpA, OpB, TM, TN, false>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, aoff,
+                                                 boff);
+            // the next stage landed everywhere; nobody reads buffer `cur` any more
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 2), 0));
+            asm volatile("s_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.live());
+            substep<OpA, OpB, TM, TN, true>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
+                                            aoff, boff);
+            __builtin_amdgcn_sched_barrier(0);
+            cur_ld.advance();
+            cur = nxt;
+        }
+
+        int bb, tm, tn;
+        logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
+        const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
+        if (t + stride < end) {
+            epilogue<TILE, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, lane);
+        } else {
+            // Last tile: only loads past the end (which fetch nothing but
+            // still complete into LDS) are outstanding.  Once they have
+            // landed and every wave is done reading the last stage, the ring
+            // is free for 32-row staging.
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            asm volatile("s_barrier" ::: "memory");
+            epilogue<TILE, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, lane);
+        }
+    }
 }
 
 // Stage depth and ring length: 2 x 64 KiB of LDS for the 256 tile.  A
@@ -412,7 +466,7 @@ constexpr int kStages = 2;
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
 int launch_t(const GemmDesc& d, KArgs k, hipStream_t s) {
     k.ktiles = (int32_t)(d.K / kBK);
-    gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
+    gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16><<<dim3((unsigned)d.grid), dim3(kThreads), 0, s>>>(k);
     return (int)hipGetLastError();
 }
 
@@ -433,12 +487,14 @@ int launch_tile(const GemmDesc& d, const KArgs& k, hipStream_t s) {
 
 }  // namespace kern
 
-void tile_of_workgroup(const GemmDesc& d, int64_t h, int64_t* b, int64_t* tm, int64_t* tn) {
+bool tile_of_slot(const GemmDesc& d, int64_t i, int64_t* b, int64_t* tm, int64_t* tn) {
     int64_t bb, m, n;
-    remap_tile<int64_t>(h, d.tiles, d.tiles_m, d.tiles_n, d.group_m, d.grouped, bb, m, n);
+    if (!asl::tile_of_slot<int64_t>(i, d.grid, d.tiles, d.tiles_m, d.tiles_n, d.group_m, d.grouped, bb, m, n))
+        return false;
     *b = bb;
     *tm = m;
     *tn = n;
+    return true;
 }
 
 using namespace kern;

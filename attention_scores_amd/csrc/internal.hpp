@@ -21,15 +21,16 @@ struct GemmDesc {
     int tile;                        // 256 or 128 (square output tile)
     int group_m;                     // rows of tiles per group in the grouped order
     bool grouped;                    // XCD-aware grouped order (false: identity)
-    int64_t tiles_m, tiles_n, tiles; // grid
+    int64_t tiles_m, tiles_n, tiles; // output tiles
+    int64_t grid;                    // workgroups launched (tiles, or fewer: persistent)
 };
 
 // Launch the planned product.  Returns 0 or a hipError_t value.
 int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* stream);
 
-// Logical tile visited by hardware workgroup id h (the device remap, shared
-// with the kernels): writes batch, tile row and tile column.
-void tile_of_workgroup(const GemmDesc& d, int64_t h, int64_t* b, int64_t* tm, int64_t* tn);
+// Tile computed in execution slot i (round i div grid of workgroup i mod
+// grid; the device schedule, shared with the kernels).  False if empty.
+bool tile_of_slot(const GemmDesc& d, int64_t i, int64_t* b, int64_t* tm, int64_t* tn);
 
 struct TilecastDesc {
     const void* buf;

@@ -268,7 +268,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded, %s)" % w.dist,
         "config": {"workload": w.description, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
-                   "tile": "%dx%dx%d" % (info[0], info[1], info[2]), "workgroups": info[3],
+                   "tile": "%dx%dx%d" % (info[0], info[1], info[2]), "tiles": info[3], "workgroups": info[4],
                    "grouping": "none" if args.flags & asl.AS_FLAG_NO_GROUPING else "xcd-grouped"},
         "roofline": roofline,
         "mfma_util": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -91,6 +91,7 @@ typedef struct {
 #define AS_FLAG_NO_GROUPING 0x1u  /* ablation: workgroup id -> tile is the identity (row-major tile order) */
 #define AS_FLAG_TILE_128    0x2u  /* force 128x128 output tiles */
 #define AS_FLAG_TILE_256    0x4u  /* force 256x256 output tiles */
+#define AS_FLAG_PERSISTENT  0x8u  /* launch only as many workgroups as stay resident; each walks several tiles */
 
 typedef struct as_gemm_plan* as_gemm_t;
 
@@ -104,7 +105,7 @@ typedef struct as_gemm_plan* as_gemm_t;
  *   c_t          AS_F32, or AS_BF16 (round-to-nearest-even)
  *   flags        AS_FLAG_* bits
  * Chooses the output tile (256x256 or 128x128, 4 waves), the workgroup
- * grouping and the grid.  Makes no HIP call.
+ * grouping and the (persistent) grid.  Makes no HIP call.
  */
 AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t batch,
                       as_strides a, as_strides b, as_strides c,
@@ -117,15 +118,20 @@ AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C,
 /* Release a plan created by gemm_create (NULL or unknown -> AS_ERR_INVALID). */
 AS_API as_status gemm_destroy(as_gemm_t plan);
 
-/* Tile shape a plan chose (for reporting); returns AS_ERR_INVALID on a bad plan. */
+/* What a plan chose (for reporting): output tile shape and K stage depth,
+ * the number of output tiles, and the number of workgroups launched (equal
+ * to the tiles, or fewer when the grid is persistent and each workgroup walks
+ * several tiles).  Any output pointer may be NULL.  AS_ERR_INVALID on a bad
+ * plan. */
 AS_API as_status gemm_plan_info(as_gemm_t plan, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,
-                         int64_t* workgroups);
+                                int64_t* tiles, int64_t* workgroups);
 
-/* Output tile that hardware workgroup `workgroup` (0 <= workgroup <
- * workgroups) computes under the plan's XCD-aware grouped order: batch
- * index, tile row and tile column.  Host-only; for inspection and tests. */
-AS_API as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* batch, int64_t* tile_row,
-                            int64_t* tile_col);
+/* Output tile computed in execution slot `slot` (0 <= slot < tiles): slot
+ * i is round i div W of hardware workgroup i mod W (W = workgroups), which
+ * runs on XCD i mod 8.  Writes batch index, tile row and tile column under
+ * the plan's XCD-aware grouped order.  Host-only; for inspection and tests. */
+AS_API as_status gemm_plan_tile_of(as_gemm_t plan, int64_t slot, int64_t* batch, int64_t* tile_row,
+                                   int64_t* tile_col);
 
 /*
  * Attention scores S[b,i,j] = sum_d Q[b,i,d] * K[b,j,d] for b < batch,
@@ -134,7 +140,9 @@ AS_API as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* b
  * strides with col == 1 for all three (the head dimension and the key index
  * contiguous).  qk_t must be AS_BF16; s_t AS_F32 or AS_BF16.  This is the
  * GEMM with A = Q and B = K^T, planned and launched in one call (same
- * kernels, same errors).  Asynchronous on `hip_stream`.
+ * kernels, same errors).  The plans of the last 8 distinct size/stride/type
+ * combinations are kept per calling thread (host memory only), so a loop of
+ * calls plans once.  Asynchronous on `hip_stream`.
  */
 AS_API as_status sscore_run(const void* Q, const void* K, void* S,
                      int64_t batch, int64_t Lq, int64_t Lk, int64_t dim,

@@ -97,7 +97,7 @@ def test_create_refuses_huge_leading_stride():
 
 def test_plan_registry_and_run_argument_checks():
     p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512))
-    assert asl.gemm_plan_info(p) == (128, 128, 64, 16)
+    assert asl.gemm_plan_info(p) == (128, 128, 64, 16, 16)
     assert _status(asl.gemm_run, p, 0, 0, 0) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_run, p, 16, 32, 0) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_run, p, 8, 16, 32) == asl.AS_ERR_UNSUPPORTED          # misaligned
@@ -122,13 +122,17 @@ def test_last_error_is_per_call():
 
 def test_tile_choice():
     p = asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192), c_t=asl.AS_BF16)
-    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024, 1024)
+    asl.gemm_destroy(p)
+    p = asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192), c_t=asl.AS_BF16,
+                        flags=asl.AS_FLAG_PERSISTENT)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024, 256)   # one workgroup per CU
     asl.gemm_destroy(p)
     p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512), flags=asl.AS_FLAG_TILE_256)
     assert asl.gemm_plan_info(p)[0] == 256
     asl.gemm_destroy(p)
     p = asl.gemm_create(65536, 256, 4096, 1, RM(65536, 4096), RM(4096, 256), RM(65536, 256))
-    assert asl.gemm_plan_info(p) == (256, 256, 64, 256)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 256, 256)
     asl.gemm_destroy(p)
 
 
@@ -140,6 +144,10 @@ SHAPES = [  # (M, N, K, batch, flags)
     (640, 384, 64, 1, 0),          # 15 tiles: not a multiple of the 8 XCDs
     (512, 512, 512, 3, asl.AS_FLAG_TILE_128),
     (1024, 768, 256, 5, 0),
+    (8192, 8192, 8256 - 64, 1, asl.AS_FLAG_PERSISTENT),   # 1024 tiles over 256 workgroups
+    (4096, 6144, 1024, 3, asl.AS_FLAG_PERSISTENT),        # 1152 tiles over 256 (not a multiple)
+    (2048, 2048, 128, 7, asl.AS_FLAG_PERSISTENT),         # 1792 tiles of 128 over 512 workgroups
+    (640, 384, 64, 1, asl.AS_FLAG_PERSISTENT),            # fewer tiles than workgroups
     (8192, 8192, 8192, 1, asl.AS_FLAG_NO_GROUPING),
 ]
 
@@ -147,9 +155,10 @@ SHAPES = [  # (M, N, K, batch, flags)
 @pytest.mark.parametrize("M,N,K,batch,flags", SHAPES)
 def test_schedule_is_a_bijection(M, N, K, batch, flags):
     p = asl.gemm_create(M, N, K, batch, (K, 1, M * K), (N, 1, K * N), (N, 1, M * N), flags=flags)
-    tm, tn, _, wg = asl.gemm_plan_info(p)
+    tm, tn, _, wg, grid = asl.gemm_plan_info(p)
     tiles_m, tiles_n = M // tm, N // tn
     assert wg == batch * tiles_m * tiles_n
+    assert grid == (min(wg, 256 if tm == 256 else 512) if flags & asl.AS_FLAG_PERSISTENT else wg)
     seen = set()
     for h in range(wg):
         b, r, c = asl.gemm_plan_tile_of(p, h)
@@ -203,7 +212,7 @@ def test_attention_scores_share_whole_slices_per_xcd():
     # XCD computes 4 whole slices, so each slice's Q and K are fetched by one
     # XCD only.
     p = asl.gemm_create(2048, 2048, 128, 32, (128, 1, 2048 * 128), (1, 128, 2048 * 128), (2048, 1, 2048 * 2048))
-    assert asl.gemm_plan_info(p) == (128, 128, 64, 8192)
+    assert asl.gemm_plan_info(p) == (128, 128, 64, 8192, 8192)
     slices = [set() for _ in range(8)]
     for h in range(8192):
         b, _, _ = asl.gemm_plan_tile_of(p, h)

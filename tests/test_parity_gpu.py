@@ -267,3 +267,57 @@ def test_tilecast_checksums(group, grouped, streaming):
     for w in range(consumers):
         tot, last = oracle.tilecast_checksum(b, rows, cols, tm, tn, w, consumers, group, grouped, iters, stride)
         assert (int(got[w, 0]), int(got[w, 1])) == (tot, last), w
+
+
+def test_output_beyond_4gib_sampled():
+    # 65536 x 65536 bf16 output (8 GiB): element offsets pass 2^32, so every
+    # address in the epilogue must be 64-bit.  K = 64: a single stage.
+    M = N = 65536
+    K = 64
+    _say("8 GiB output")
+    A = draw((M, K), "uniform", -1, 1, 71)
+    B = draw((K, N), "uniform", -1, 1, 72)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    plan = asl.gemm_create(M, N, K, 1, (K, 1, 0), (N, 1, 0), (N, 1, 0), asl.AS_BF16, asl.AS_BF16, asl.AS_BF16, 0)
+    try:
+        asl.gemm_run(plan, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        asl.gemm_destroy(plan)
+    pts = sample_points(1, M, N, N_SAMPLES, seed=77)
+    pts = np.concatenate([pts, np.array([[0, M - 1, N - 1], [0, M - 1, 0], [0, 40000, 50000]])], axis=0)
+    idx = torch.from_numpy(pts).to(DEV)
+    got = _decode(C[idx[:, 1], idx[:, 2]])
+    Cref, T = oracle.gemm_points(bits(A), bits(B), pts, K, (K, 1, 0), (N, 1, 0), dims=(1, M, N))
+    # K = 64 of same-scale data: |C| is close to T, and rounding a correct
+    # result to bf16 (half an ulp, at most 2^-8 |C|) can exceed 1e-3 T on its
+    # own; the bf16-output allowance adds exactly that rounding.
+    extra = 2.0 ** -8 * np.abs(Cref)
+    nfail, util = oracle.check(got, Cref, T, extra=extra)
+    bad = np.nonzero(~(np.abs(got - Cref) <= 1e-3 * T + 1e-5 + extra))[0][:8]
+    assert nfail == 0, "%d sampled elements outside tolerance (max util %.3g); first: %s" % (
+        nfail, util, [(tuple(pts[i]), float(got[i]), float(Cref[i])) for i in bad])
+    del C
+    torch.cuda.empty_cache()
+
+
+def test_persistent_grid_bit_exact():
+    # 576 tiles of 128 x 128 walked by 512 resident workgroups (some take two
+    # tiles): the LDS ring streams across tile boundaries.  Integer data, so
+    # the result must equal the oracle exactly.
+    M = N = 3072
+    K = 128
+    _say("persistent grid, 576 tiles")
+    A = draw((M, K), "int", -4, 4, 81)
+    B = draw((K, N), "int", -4, 4, 82)
+    sa, sb = (K, 1, 0), (N, 1, 0)
+    C = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, asl.AS_FLAG_PERSISTENT | asl.AS_FLAG_TILE_128)
+    Cref, _ = oracle.gemm(bits(A), bits(B), 1, M, N, K, sa, sb, want_T=False)
+    assert np.array_equal(_decode(C), Cref)
+
+
+def test_persistent_grid_full_size_sampled():
+    w = WORKLOADS["gemm8192"]
+    _say("gemm8192 persistent, sampled")
+    _sampled_gemm(w, flags=asl.AS_FLAG_PERSISTENT)
