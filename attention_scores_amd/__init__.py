@@ -26,7 +26,7 @@ AS_BF16, AS_F32 = 0, 1
 AS_FLAG_NO_GROUPING = 0x1
 AS_FLAG_TILE_128 = 0x2
 AS_FLAG_TILE_256 = 0x4
-AS_FLAG_PERSISTENT = 0x8
+AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
             "sscore_run", "tilecast_run", "as_status_str", "as_last_error")

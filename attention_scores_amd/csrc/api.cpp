@@ -49,7 +49,8 @@ as_status ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 | AS_FLAG_PERSISTENT;
+constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 |
+                                 AS_FLAG_ONE_TILE_PER_WORKGROUP;
 constexpr int64_t kBK = asl::kTileK;
 constexpr int64_t kCus = 256;   // MI355X compute units
 
@@ -169,12 +170,13 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
     d.tiles = batch * d.tiles_m * d.tiles_n;
     d.grouped = !(flags & AS_FLAG_NO_GROUPING);
-    // One workgroup per tile, or with AS_FLAG_PERSISTENT as many as stay
-    // resident (one per CU for the 256 tile's 145 KiB of LDS, two for the
-    // 128 tile), each walking its XCD's tiles with the LDS ring streaming
-    // across tile boundaries.
+    // As many workgroups as stay resident (one per CU for the 256 tile's
+    // 145 KiB of LDS, two for the 128 tile), each walking its XCD's tiles
+    // with the LDS ring streaming across tile boundaries, so one tile's
+    // stores drain while the next tile computes; or, for the ablation, one
+    // workgroup per tile.
     const int64_t resident = (tile == 256 ? 1 : 2) * kCus;
-    d.grid = (flags & AS_FLAG_PERSISTENT) && d.tiles > resident ? resident : d.tiles;
+    d.grid = !(flags & AS_FLAG_ONE_TILE_PER_WORKGROUP) && d.tiles > resident ? resident : d.tiles;
     d.group_m = choose_group_m(d.tiles, d.tiles_m, d.tiles_n, tile, K);
     *out = d;
     return AS_OK;

@@ -308,6 +308,12 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TILE / 64][TILE / 6
     }
 }
 
+// Global stores one wave issues in epilogue<TILE, ROWS, OUT_BF16>.
+template <int TILE, int ROWS, bool OUT_BF16>
+constexpr int epilogue_stores() {
+    return (TILE / 64) * (32 / ROWS) * (ROWS * (TILE / 2) / (OUT_BF16 ? 8 : 4)) / 64;
+}
+
 // Cursor over the stream of stages a workgroup loads: tile t (logical),
 // stage k of it, and the global origins of that stage's A and B tiles.
 template <int TILE, int BK, bool A_K, bool B_K>
@@ -374,6 +380,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
+    constexpr int kEpiStores = epilogue_stores<TILE, 8, OUT_BF16>();
+    constexpr int kWaitAfterEpi = L * (S - 2) + kEpiStores < 63 ? L * (S - 2) + kEpiStores : 63;
     using Epi8 = EpiRegion<TILE, 8>;
     using Epi32 = EpiRegion<TILE, 32>;
     static_assert(kWaves * Epi32::kBytes <= S * kStage, "last-tile epilogue must fit in the ring");
@@ -430,7 +438,14 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
                                                  boff);
             // the next stage landed everywhere; nobody reads buffer `cur` any more
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 2), 0));
+            if (kt == 0 && t != first) {
+                // The previous tile's epilogue stores were issued after the
+                // awaited loads; vector memory operations retire in issue
+                // order, so they may stay in flight.
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWaitAfterEpi, 0));
+            } else {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 2), 0));
+            }
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.live());

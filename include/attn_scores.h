@@ -91,7 +91,8 @@ typedef struct {
 #define AS_FLAG_NO_GROUPING 0x1u  /* ablation: workgroup id -> tile is the identity (row-major tile order) */
 #define AS_FLAG_TILE_128    0x2u  /* force 128x128 output tiles */
 #define AS_FLAG_TILE_256    0x4u  /* force 256x256 output tiles */
-#define AS_FLAG_PERSISTENT  0x8u  /* launch only as many workgroups as stay resident; each walks several tiles */
+#define AS_FLAG_ONE_TILE_PER_WORKGROUP 0x8u  /* ablation: one workgroup per output tile instead of a resident
+                                               * (persistent) grid whose workgroups walk several tiles */
 
 typedef struct as_gemm_plan* as_gemm_t;
 
@@ -105,7 +106,9 @@ typedef struct as_gemm_plan* as_gemm_t;
  *   c_t          AS_F32, or AS_BF16 (round-to-nearest-even)
  *   flags        AS_FLAG_* bits
  * Chooses the output tile (256x256 or 128x128, 4 waves), the workgroup
- * grouping and the (persistent) grid.  Makes no HIP call.
+ * grouping and the grid: by default as many workgroups as stay resident
+ * (256 for the 256x256 tile, 512 for 128x128; fewer if there are fewer
+ * tiles), each walking several tiles.  Makes no HIP call.
  */
 AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t batch,
                       as_strides a, as_strides b, as_strides c,

@@ -122,11 +122,11 @@ def test_last_error_is_per_call():
 
 def test_tile_choice():
     p = asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192), c_t=asl.AS_BF16)
-    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024, 1024)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024, 256)   # one resident workgroup per CU
     asl.gemm_destroy(p)
     p = asl.gemm_create(8192, 8192, 8192, 1, RM(8192, 8192), RM(8192, 8192), RM(8192, 8192), c_t=asl.AS_BF16,
-                        flags=asl.AS_FLAG_PERSISTENT)
-    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024, 256)   # one workgroup per CU
+                        flags=asl.AS_FLAG_ONE_TILE_PER_WORKGROUP)
+    assert asl.gemm_plan_info(p) == (256, 256, 64, 1024, 1024)
     asl.gemm_destroy(p)
     p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512), flags=asl.AS_FLAG_TILE_256)
     assert asl.gemm_plan_info(p)[0] == 256
@@ -137,17 +137,17 @@ def test_tile_choice():
 
 
 SHAPES = [  # (M, N, K, batch, flags)
-    (8192, 8192, 8192, 1, 0),
-    (2048, 2048, 128, 32, 0),
+    (8192, 8192, 8192, 1, 0),                             # 1024 tiles over 256 workgroups
+    (2048, 2048, 128, 32, 0),                             # 8192 tiles of 128 over 512
     (65536, 256, 4096, 1, 0),
     (16384, 8192, 2048, 1, 0),
     (640, 384, 64, 1, 0),          # 15 tiles: not a multiple of the 8 XCDs
     (512, 512, 512, 3, asl.AS_FLAG_TILE_128),
     (1024, 768, 256, 5, 0),
-    (8192, 8192, 8256 - 64, 1, asl.AS_FLAG_PERSISTENT),   # 1024 tiles over 256 workgroups
-    (4096, 6144, 1024, 3, asl.AS_FLAG_PERSISTENT),        # 1152 tiles over 256 (not a multiple)
-    (2048, 2048, 128, 7, asl.AS_FLAG_PERSISTENT),         # 1792 tiles of 128 over 512 workgroups
-    (640, 384, 64, 1, asl.AS_FLAG_PERSISTENT),            # fewer tiles than workgroups
+    (8192, 8192, 8256 - 64, 1, asl.AS_FLAG_ONE_TILE_PER_WORKGROUP),
+    (4096, 6144, 1024, 3, 0),                             # 1152 tiles over 256 (not a multiple)
+    (2048, 2048, 128, 7, 0),                              # 1792 tiles of 128 over 512 workgroups
+    (2048, 2048, 128, 7, asl.AS_FLAG_ONE_TILE_PER_WORKGROUP),
     (8192, 8192, 8192, 1, asl.AS_FLAG_NO_GROUPING),
 ]
 
@@ -158,7 +158,7 @@ def test_schedule_is_a_bijection(M, N, K, batch, flags):
     tm, tn, _, wg, grid = asl.gemm_plan_info(p)
     tiles_m, tiles_n = M // tm, N // tn
     assert wg == batch * tiles_m * tiles_n
-    assert grid == (min(wg, 256 if tm == 256 else 512) if flags & asl.AS_FLAG_PERSISTENT else wg)
+    assert grid == (wg if flags & asl.AS_FLAG_ONE_TILE_PER_WORKGROUP else min(wg, 256 if tm == 256 else 512))
     seen = set()
     for h in range(wg):
         b, r, c = asl.gemm_plan_tile_of(p, h)
@@ -212,7 +212,7 @@ def test_attention_scores_share_whole_slices_per_xcd():
     # XCD computes 4 whole slices, so each slice's Q and K are fetched by one
     # XCD only.
     p = asl.gemm_create(2048, 2048, 128, 32, (128, 1, 2048 * 128), (1, 128, 2048 * 128), (2048, 1, 2048 * 2048))
-    assert asl.gemm_plan_info(p) == (128, 128, 64, 8192, 8192)
+    assert asl.gemm_plan_info(p) == (128, 128, 64, 8192, 512)
     slices = [set() for _ in range(8)]
     for h in range(8192):
         b, _, _ = asl.gemm_plan_tile_of(p, h)

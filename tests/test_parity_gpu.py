@@ -302,22 +302,45 @@ def test_output_beyond_4gib_sampled():
     torch.cuda.empty_cache()
 
 
-def test_persistent_grid_bit_exact():
-    # 576 tiles of 128 x 128 walked by 512 resident workgroups (some take two
-    # tiles): the LDS ring streams across tile boundaries.  Integer data, so
-    # the result must equal the oracle exactly.
+@pytest.mark.parametrize("K", [64, 128, 192])
+@pytest.mark.parametrize("flags", [0, asl.AS_FLAG_ONE_TILE_PER_WORKGROUP])
+def test_grid_kinds_bit_exact(K, flags):
+    # 576 tiles of 128 x 128: the resident grid has 512 workgroups, some of
+    # which take two tiles, so the LDS ring streams across a tile boundary
+    # after 1, 2 or 3 stages; the ablation launches one workgroup per tile.
+    # Integer data, so the result must equal the oracle exactly.
     M = N = 3072
-    K = 128
-    _say("persistent grid, 576 tiles")
+    _say("grid kinds, 576 tiles, K=%d flags=%d" % (K, flags))
     A = draw((M, K), "int", -4, 4, 81)
     B = draw((K, N), "int", -4, 4, 82)
     sa, sb = (K, 1, 0), (N, 1, 0)
-    C = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, asl.AS_FLAG_PERSISTENT | asl.AS_FLAG_TILE_128)
+    C = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, flags | asl.AS_FLAG_TILE_128)
     Cref, _ = oracle.gemm(bits(A), bits(B), 1, M, N, K, sa, sb, want_T=False)
     assert np.array_equal(_decode(C), Cref)
 
 
-def test_persistent_grid_full_size_sampled():
+@pytest.mark.parametrize("K,out,a_k,b_k", [(64, "f32", True, True), (192, "f32", False, False),
+                                           (128, "bf16", True, False)])
+def test_resident_grid_256_tiles_bit_exact(K, out, a_k, b_k):
+    # 17 x 16 = 272 tiles of 256 x 256 over 256 resident workgroups: 16 of
+    # them write two tiles, the first through the 8-row epilogue region while
+    # the next tile's stages load, with that epilogue's stores still in
+    # flight at the next stage wait.
+    M, N, batch = 4352, 4096, 1
+    _say("resident grid 256 tiles K=%d out=%s a_k=%s b_k=%s" % (K, out, a_k, b_k))
+    a_shape, sa, b_shape, sb = _layout(M, N, K, batch, a_k, b_k)
+    A = draw(a_shape, "int", -4, 4, 91 + K)
+    B = draw(b_shape, "int", -4, 4, 92 + K)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    C = _run_gemm(A, B, M, N, K, batch, sa, sb, od, asl.AS_FLAG_TILE_256)
+    Cref, _ = oracle.gemm(bits(A), bits(B), batch, M, N, K, sa, sb, want_T=False)
+    if out == "f32":
+        assert np.array_equal(_decode(C), Cref)
+    else:
+        assert np.array_equal(bits(C), oracle.f64_to_bf16_rne_array(Cref))
+
+
+def test_one_tile_per_workgroup_full_size_sampled():
     w = WORKLOADS["gemm8192"]
-    _say("gemm8192 persistent, sampled")
-    _sampled_gemm(w, flags=asl.AS_FLAG_PERSISTENT)
+    _say("gemm8192 one tile per workgroup, sampled")
+    _sampled_gemm(w, flags=asl.AS_FLAG_ONE_TILE_PER_WORKGROUP)
