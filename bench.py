@@ -8,7 +8,7 @@ before the timed region.
 Prints ONE JSON line with the metric, the kernel's roofline position (HIP
 events on the launch stream; algorithmic flops = 2*M*N*K per launch; peak =
 2.5 PFLOP/s dense bf16), the HBM traffic from the committed rocprofv3 counter
-summary when it was taken on the current kernel source, and the CPU oracle
+summary of the workload when it was taken on the current kernel source, and the CPU oracle
 timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -32,7 +32,6 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 HEADLINE = "gemm8192"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm8192.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_scores_amd", "csrc", f)
                   for f in ("gemm.hip", "schedule.hpp")]
 
@@ -45,12 +44,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s.txt" % name)
+
+
+def read_traffic(name: str):
+    """HBM bytes per launch of workload `name` from its committed counter
+    summary, if that summary was taken on the current kernel source."""
+    path = traffic_file(name)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -244,7 +249,7 @@ def main():
     flop = w.flop
     value = flop / (wall_ms * 1e-3) / 1e12
     achieved = flop / (ev_ms * 1e-3) / 1e12
-    traffic = read_traffic() if w.name == HEADLINE else None
+    traffic = read_traffic(w.name)
     compulsory_read = w.bytes_a + w.bytes_b
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
