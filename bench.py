@@ -12,6 +12,8 @@ summary of the workload when it was taken on the current kernel source, and the 
 timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
+      (defaults: warm up for about 0.5 s of launches, then time at least 50
+      launches and 0.1 s; the JSON line reports the counts used)
   python bench.py --workload NAME      other workloads (reported, not the headline)
   python bench.py --tilecast           tile fan-out microbenchmark (JSON lines)
   python bench.py --profile            short run for rocprofv3 (GEMM + a copy kernel of known size)
@@ -83,8 +85,16 @@ def _plan(asl, w, flags=0):
                            asl.AS_BF16, asl.AS_BF16, c_t, flags)
 
 
+WARMUP_S = 0.5      # default warm-up: launches for about this long, so the clocks settle
+TIMED_S = 0.1       # default timed region: at least this long (and at least 50 launches)
+
+
 def time_workload(w, steps, warmup, flags=0):
-    """(wall ms per step, event ms per launch, plan info) for workload w."""
+    """(wall ms per step, event ms per launch, plan info, steps, warmup) for
+    workload w.  steps / warmup None: sized from a short calibration so that
+    the warm-up lasts WARMUP_S and the timed region at least TIMED_S (the GPU
+    raises its clocks over tens of milliseconds of load, which 30 launches of
+    a 0.1 ms kernel do not reach)."""
     import torch
     import attention_scores_amd as asl
     dev = torch.device("cuda:0")
@@ -110,6 +120,19 @@ def time_workload(w, steps, warmup, flags=0):
 
         def run():
             asl.gemm_run(plan, a, b, c, sh)
+    if warmup is None or steps is None:
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+        per = max((time.perf_counter() - c0) / 10, 1e-6)
+        if warmup is None:
+            warmup = max(30, min(20000, int(WARMUP_S / per)))
+        if steps is None:
+            steps = max(50, min(20000, int(TIMED_S / per)))
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -127,7 +150,7 @@ def time_workload(w, steps, warmup, flags=0):
     wall_ms = (t1 - t0) * 1e3 / steps
     ev_ms = ev0.elapsed_time(ev1) / steps
     del A, B, C
-    return wall_ms, ev_ms, info
+    return wall_ms, ev_ms, info, steps, warmup
 
 
 def cpu_baseline(w, target_s=15.0):
@@ -214,8 +237,10 @@ def profile_run(steps, name=HEADLINE):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed launches (default: >= 50 and >= %.1f s)" % TIMED_S)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches first (default: about %.1f s worth, >= 30)" % WARMUP_S)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tilecast", action="store_true")
@@ -237,7 +262,7 @@ def main():
     asl.lib()
 
     if args.profile:
-        profile_run(max(1, args.steps), args.workload)
+        profile_run(args.steps if args.steps else 3, args.workload)
         return
     if args.tilecast:
         for line in tilecast_report():
@@ -245,7 +270,7 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
-    wall_ms, ev_ms, info = time_workload(w, args.steps, args.warmup, args.flags)
+    wall_ms, ev_ms, info, steps, warmup = time_workload(w, args.steps, args.warmup, args.flags)
     flop = w.flop
     value = flop / (wall_ms * 1e-3) / 1e12
     achieved = flop / (ev_ms * 1e-3) / 1e12
@@ -264,8 +289,8 @@ def main():
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(wall_ms, 4),
         "higher_is_better": True,
         "scaling": "strong",
