@@ -143,29 +143,33 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     if (batch > 1 && c.batch < M * c.row)
         return fail(AS_ERR_INVALID, "C batches overlap (batch stride %" PRId64 ")", c.batch);
 
-    // Tile choice.
+    if (K % 8)
+        return fail(AS_ERR_UNSUPPORTED, "K must be a multiple of 8 (K=%" PRId64 ")", K);
+
+    // Tile choice.  256x256 tiles when K is deep enough to amortise the
+    // epilogue, the grid still fills most CUs and edge tiles waste little;
+    // otherwise 128x128 tiles, whose 73 KiB of LDS lets two workgroups share
+    // a CU so one's stores overlap the other's loads (store-bound shapes such
+    // as attention scores with a short K).
+    auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
     int tile;
     if (flags & AS_FLAG_TILE_256) tile = 256;
     else if (flags & AS_FLAG_TILE_128) tile = 128;
-    // 256x256 tiles when K is deep enough to amortise the epilogue and the
-    // grid still fills most CUs; otherwise 128x128 tiles, whose 64 KiB of
-    // LDS lets two workgroups share a CU so one's stores overlap the other's
-    // loads (store-bound shapes such as attention scores with a short K).
-    else if (M % 256 == 0 && N % 256 == 0 && K >= 512 && batch * (M / 256) * (N / 256) >= 128) tile = 256;
-    else tile = 128;
-    if (M % tile || N % tile || K % kBK)
-        return fail(AS_ERR_UNSUPPORTED, "M and N must be multiples of the %dx%d tile and K of %" PRId64
-                    " (M=%" PRId64 " N=%" PRId64 " K=%" PRId64 ")", tile, tile, kBK, M, N, K);
+    else {
+        const int64_t area256 = cdiv(M, 256) * cdiv(N, 256) * 4, area128 = cdiv(M, 128) * cdiv(N, 128);
+        const bool deep = K >= 512, many = batch * cdiv(M, 256) * cdiv(N, 256) >= 128;
+        tile = (deep && many && area256 * 100 <= area128 * 106) ? 256 : 128;
+    }
     // Per-lane 32-bit byte offsets inside one staged tile.
     const int64_t a_span = (d.a_kmajor ? tile : kBK) * a_ld * 2;
     const int64_t b_span = (d.b_kmajor ? tile : kBK) * b_ld * 2;
     if (a_span >= (INT64_C(1) << 31) || b_span >= (INT64_C(1) << 31))
         return fail(AS_ERR_UNSUPPORTED, "leading strides too large for 32-bit tile offsets");
-    if (K / kBK > INT32_MAX) return fail(AS_ERR_UNSUPPORTED, "K too large");
+    if (cdiv(K, kBK) > INT32_MAX) return fail(AS_ERR_UNSUPPORTED, "K too large");
 
     d.tile = tile;
-    d.tiles_m = M / tile;
-    d.tiles_n = N / tile;
+    d.tiles_m = cdiv(M, tile);
+    d.tiles_n = cdiv(N, tile);
     if (d.tiles_m > INT32_MAX / d.tiles_n || d.tiles_m * d.tiles_n > INT32_MAX / batch)
         return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
     d.tiles = batch * d.tiles_m * d.tiles_n;

@@ -25,6 +25,15 @@
 //   MFMA            v_mfma_f32_32x32x16_bf16, fp32 accumulators.
 //   epilogue        fp32 stores, or round-to-nearest-even to bf16.
 //
+// Edges.  M and N need not be multiples of the tile, nor K of BK (K must be
+// a multiple of 8, one 16-byte chunk).  Every stage's buffer resource covers
+// exactly the operand bytes from the stage origin to the operand's last
+// element, so rows past M or N and k rows past K (MN-contiguous operands)
+// read as zero and never fault; in the last, partial K stage the chunks of a
+// K-contiguous operand at k >= K (which would otherwise read the next row)
+// are given out-of-range offsets and also read as zero.  Every product term
+// with k >= K is therefore 0 * 0, and outputs outside M x N are not stored.
+//
 // Lane maps (measured on gfx950 with a probe kernel):
 //   MFMA 32x32x16 bf16: A operand lane l = row l%32, k (l/32)*8+e (e<8);
 //     B operand lane l = column l%32, k (l/32)*8+e; result element e of lane
@@ -67,9 +76,15 @@ struct KArgs {
     int64_t a_ld, a_bs;   // A: stride of the non-contiguous index, batch stride
     int64_t b_ld, b_bs;
     int64_t c_ld, c_bs;
-    int32_t ktiles;       // K / BK (stages)
+    int64_t M, N, K;      // problem sizes (edge tiles are partial)
+    int32_t ktiles;       // ceil(K / BK) stages per tile
+    int32_t krem;         // K mod BK: valid k of the last stage (0: the last stage is full)
     int32_t tiles, tiles_m, tiles_n, group_m, grouped;
 };
+
+// A lane offset past any buffer resource's range (ranges are < 2^31 bytes):
+// the load returns zeros.
+constexpr uint32_t kOob = 0x80000000u;
 
 // Swizzle of a K-contiguous tile (rows of BK k = CHR chunks of 16 B): chunk
 // c of row r is stored in slot c ^ swz_k<CHR>(r).  A fragment read touches
@@ -115,6 +130,7 @@ struct OperandTile {
     static constexpr int kCHR = BK / 8;                              // chunks per row (K-major)
     static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;   // 1 KiB per wave-wide load
     static constexpr int kCH = R / 8;                                // chunks per row (MN-major)
+    static constexpr bool kKMaj = KMAJ;
 
     // Byte offset, relative to the tile origin in global memory, of the 16
     // bytes that lane `lane` of wave `w` fetches in its i-th load; the data
@@ -129,6 +145,20 @@ struct OperandTile {
             int k = p / kCH, s = p % kCH;
             int c = s ^ swz_mn<kCH>(k);
             return (uint32_t)(((int64_t)k * ld + c * 8) * 2);
+        }
+    }
+
+    // Element offset, along the contiguous dimension, of the chunk that lane
+    // `lane` of wave `w` fetches in its i-th load (k within the stage for a
+    // K-contiguous operand).
+    __device__ static int inner_of(int w, int i, int lane) {
+        int p = (w * kLoadsPerWave + i) * 64 + lane;
+        if constexpr (KMAJ) {
+            int r = p / kCHR, s = p % kCHR;
+            return (s ^ swz_k<kCHR>(r)) * 8;
+        } else {
+            int k = p / kCH, s = p % kCH;
+            return (s ^ swz_mn<kCH>(k)) * 8;
         }
     }
 
@@ -169,25 +199,54 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
-// The per-stage global -> LDS loads of one wave: kLoadsPerWave for A then
-// for B, each filling one 1 KiB row of the wave's part of the stage.  With
-// `live` false the resources have no valid range: the loads fetch nothing
-// and only keep the per-stage load count uniform (the buffer is dead).
+// Per-lane source offsets of a wave's stage loads.  For the last, partial K
+// stage of a K-contiguous operand, a chunk at k >= K would read the next
+// row, so its offset is moved out of range there.  A load of such an operand
+// covers 8 rows of 8 chunks and the chunk order depends only on the lane and
+// on the parity of the load's row group (the swizzle in swz_k<8>); kc[p] is
+// the lane's k offset in loads of parity p.  An MN-contiguous operand needs
+// no mask: its k rows past K lie past the resource's range.
 template <class OpA, class OpB>
+struct LaneOffsets {
+    uint32_t a[OpA::kLoadsPerWave], b[OpB::kLoadsPerWave];
+    uint32_t akc[2], bkc[2];
+};
+
+// The per-stage global -> LDS loads of one wave: kLoadsPerWave for A then
+// for B, each filling one 1 KiB row of the wave's part of the stage.  The
+// resources cover the operands' valid bytes from the stage origin; for a
+// dead stage (past the workgroup's last tile) they cover nothing: the loads
+// fetch nothing and only keep the per-stage load count uniform.  `klim` is
+// the stage's valid k (BK except in a partial last stage).
+template <class OpA, class OpB, bool RAGGED>
 struct StageLoads {
     static constexpr int kCount = OpA::kLoadsPerWave + OpB::kLoadsPerWave;
+    static_assert(OpA::kLoadsPerWave % 2 == 0 && OpB::kLoadsPerWave % 2 == 0,
+                  "a wave's loads must start on an even row group");
+    static_assert(OpA::kCHR == 8 && OpB::kCHR == 8, "the two-parity chunk order holds for 8-chunk rows");
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t sa, sb;   // LDS byte addresses of this wave's first A / B row in the stage
+    uint32_t klim;
 
-    __device__ void setup(const char* dst, int w, const uint16_t* a_src, const uint16_t* b_src, bool live) {
-        ra = make_rsrc(a_src, live ? 0x7fffffff : 0);
-        rb = make_rsrc(b_src, live ? 0x7fffffff : 0);
+    __device__ void setup(const char* dst, int w, const uint16_t* a_src, const uint16_t* b_src, int a_bytes,
+                          int b_bytes, int klim_) {
+        ra = make_rsrc(a_src, a_bytes);
+        rb = make_rsrc(b_src, b_bytes);
         sa = lds_u32(dst + w * OpA::kLoadsPerWave * 1024);
         sb = lds_u32(dst + OpA::kBytes + w * OpB::kLoadsPerWave * 1024);
+        if constexpr (RAGGED) klim = (uint32_t)__builtin_amdgcn_readfirstlane(klim_);
     }
-    __device__ void issue(int i, const uint32_t* aoff, const uint32_t* boff) const {
-        if (i < OpA::kLoadsPerWave) lds_dma16(ra, aoff[i], sa + i * 1024);
-        else lds_dma16(rb, boff[i - OpA::kLoadsPerWave], sb + (i - OpA::kLoadsPerWave) * 1024);
+    __device__ void issue(int i, const LaneOffsets<OpA, OpB>& o) const {
+        if (i < OpA::kLoadsPerWave) {
+            uint32_t v = o.a[i];
+            if constexpr (RAGGED && OpA::kKMaj) v = o.akc[i & 1] < klim ? v : kOob;
+            lds_dma16(ra, v, sa + i * 1024);
+        } else {
+            const int j = i - OpA::kLoadsPerWave;
+            uint32_t v = o.b[j];
+            if constexpr (RAGGED && OpB::kKMaj) v = o.bkc[j & 1] < klim ? v : kOob;
+            lds_dma16(rb, v, sb + j * 1024);
+        }
     }
 };
 
@@ -211,27 +270,26 @@ __device__ __forceinline__ void read_unit(Frags<TM, TN>& f, int u, const char* s
 // stage per MFMA.  Scheduling barriers keep that order, so every MFMA has
 // independent work issued next to it and the LDS sees a steady stream of
 // requests rather than bursts.
-template <class OpA, class OpB, int TM, int TN, bool LOADS>
+template <class OpA, class OpB, int TM, int TN, bool LOADS, bool RAGGED>
 __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, TN>& f, Frags<TM, TN>& g,
                                         const char* rd, int j, int m0, int n0, int lane,
-                                        const StageLoads<OpA, OpB>& ld, const uint32_t* aoff,
-                                        const uint32_t* boff) {
+                                        const StageLoads<OpA, OpB, RAGGED>& ld, const LaneOffsets<OpA, OpB>& off) {
     constexpr int kMfma = TM * TN;
     constexpr int kUnits = TM + TN;
-    constexpr int kLoads = StageLoads<OpA, OpB>::kCount;
+    constexpr int kLoads = StageLoads<OpA, OpB, RAGGED>::kCount;
 #pragma unroll
     for (int t = 0; t < kMfma; ++t) {
         const int mi = t / TN, ni = t % TN;
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
         if constexpr (LOADS) {
-            if (t < kLoads) ld.issue(t, aoff, boff);
+            if (t < kLoads) ld.issue(t, off);
         }
         if (t < kUnits) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (LOADS) {
 #pragma unroll
-        for (int t = kMfma; t < kLoads; ++t) ld.issue(t, aoff, boff);
+        for (int t = kMfma; t < kLoads; ++t) ld.issue(t, off);
     }
 #pragma unroll
     for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
@@ -259,9 +317,14 @@ struct EpiRegion {
 // rounded to nearest even right before its store) runs.  The stores are
 // non-temporal: C is written once and not re-read, so it should not push A
 // and B out of L2.
-template <int TILE, int ROWS, bool OUT_BF16>
+//
+// EDGE (a tile that extends past C): only rows < m_lim and columns < n_lim
+// of the quadrant (counted from r0, c0) are stored; a 16-byte piece that
+// straddles column n_lim goes out element by element.
+template <int TILE, int ROWS, bool OUT_BF16, bool EDGE = false>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TILE / 64][TILE / 64], char* region, void* Cv,
-                                         int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane) {
+                                         int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane,
+                                         int64_t m_lim = 0, int64_t n_lim = 0) {
     constexpr int WT = TILE / 2, TM = WT / 32, TN = WT / 32;
     constexpr int STRIDE = EpiRegion<TILE, ROWS>::kStride;
     constexpr int ELEMS = OUT_BF16 ? 8 : 4;          // elements per lane per store (16 bytes out)
@@ -289,6 +352,21 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TILE / 64][TILE / 6
                 const int row = piece / PPR, cp = piece % PPR;
                 const char* src = region + row * STRIDE + cp * ELEMS * 4;
                 const int64_t gi = c_off + (r0 + 32 * mi + ROWS * h + row) * ldc + c0 + cp * ELEMS;
+                if constexpr (EDGE) {
+                    const int rl = 32 * mi + ROWS * h + row, cl = cp * ELEMS;
+                    if (rl >= m_lim || cl >= n_lim) continue;
+                    if (cl + ELEMS > n_lim) {
+#pragma unroll
+                        for (int e = 0; e < ELEMS; ++e) {
+                            if (cl + e < n_lim) {
+                                const float x = *(const __attribute__((address_space(3))) float*)(lds_void_t*)(src + 4 * e);
+                                if constexpr (OUT_BF16) ((__bf16*)Cv)[gi + e] = (__bf16)x;
+                                else ((float*)Cv)[gi + e] = x;
+                            }
+                        }
+                        continue;
+                    }
+                }
                 if constexpr (OUT_BF16) {
                     const f32x4 lo = *(const lds_f32x4_t*)(lds_void_t*)src;
                     const f32x4 hi = *(const lds_f32x4_t*)(lds_void_t*)(src + 16);
@@ -316,10 +394,11 @@ constexpr int epilogue_stores() {
 
 // Cursor over the stream of stages a workgroup loads: tile t (logical),
 // stage k of it, and the global origins of that stage's A and B tiles.
-template <int TILE, int BK, bool A_K, bool B_K>
+template <int TILE, int BK, bool A_K, bool B_K, bool RAGGED>
 struct StageCursor {
     const KArgs& a;
     int t, k, stride, end;
+    int tm, tn;
     int64_t a_step, b_step;
     const uint16_t *pa, *pb;
 
@@ -331,7 +410,7 @@ struct StageCursor {
     }
     __device__ bool live() const { return t < end; }
     __device__ void origins() {
-        int bb, tm, tn;
+        int bb;
         logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
         pa = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE);
         pb = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE);
@@ -346,6 +425,31 @@ struct StageCursor {
             pb += b_step;
         }
     }
+    // Bytes from a stage origin to the end of the 16-byte chunk holding the
+    // operand's last element: `outer` rows of stride ld remain, the last with
+    // `inner` contiguous elements.  A chunk is never split by the range, so a
+    // 16-byte load is either wholly in range or wholly zero; the few bytes
+    // past the last element that a final partial chunk covers share its
+    // 16-byte-aligned block (never a new page) and feed only outputs past M or
+    // N, which are not stored.
+    static __device__ int extent(int64_t outer, int64_t inner, int64_t ld) {
+        const int64_t e = ((outer - 1) * ld + ((inner + 7) & ~int64_t(7))) * 2;
+        return e > 0x7fffffff ? 0x7fffffff : (int)e;
+    }
+    __device__ int a_bytes() const {
+        if (!live()) return 0;
+        if constexpr (!RAGGED) return 0x7fffffff;
+        const int64_t mr = a.M - (int64_t)tm * TILE, kr = a.K - (int64_t)k * BK;
+        return A_K ? extent(mr, kr, a.a_ld) : extent(kr, mr, a.a_ld);
+    }
+    __device__ int b_bytes() const {
+        if (!live()) return 0;
+        if constexpr (!RAGGED) return 0x7fffffff;
+        const int64_t nr = a.N - (int64_t)tn * TILE, kr = a.K - (int64_t)k * BK;
+        return B_K ? extent(nr, kr, a.b_ld) : extent(kr, nr, a.b_ld);
+    }
+    // Valid k of the stage: BK, or K mod BK in a partial last stage.
+    __device__ int klim() const { return (a.krem != 0 && k == a.ktiles - 1) ? a.krem : BK; }
 };
 
 // Pipeline (S LDS buffers; a stage is BK deep in K, NS = BK/16 MFMA
@@ -368,7 +472,12 @@ struct StageCursor {
 // A stage is requested S-1 steps before it is consumed.  Every step issues
 // the same number of loads (stages past the end fetch nothing), so the wait
 // count is a constant.
-template <int TILE, int BK, int S, bool A_K, bool B_K, bool OUT_BF16>
+//
+// RAGGED: M or N is not a multiple of TILE or K not of BK.  The stage
+// resources then cover exactly the valid bytes, the last partial K stage
+// masks its K-contiguous chunks, and edge tiles use the predicated epilogue;
+// otherwise none of that code is compiled in.
+template <int TILE, int BK, int S, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     constexpr int WT = TILE / 2;         // wave tile
     constexpr int TM = WT / 32;          // MFMA tiles per wave along M
@@ -398,20 +507,25 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, a.grouped != 0, first, stride, end);
     if (first >= end) return;
 
-    StageCursor<TILE, BK, A_K, B_K> cur_ld(a, first, stride, end);
-    uint32_t aoff[OpA::kLoadsPerWave], boff[OpB::kLoadsPerWave];
+    StageCursor<TILE, BK, A_K, B_K, RAGGED> cur_ld(a, first, stride, end);
+    LaneOffsets<OpA, OpB> off;
 #pragma unroll
-    for (int i = 0; i < OpA::kLoadsPerWave; ++i) aoff[i] = OpA::src_offset(w, i, lane, a.a_ld);
+    for (int i = 0; i < OpA::kLoadsPerWave; ++i) off.a[i] = OpA::src_offset(w, i, lane, a.a_ld);
 #pragma unroll
-    for (int i = 0; i < OpB::kLoadsPerWave; ++i) boff[i] = OpB::src_offset(w, i, lane, a.b_ld);
+    for (int i = 0; i < OpB::kLoadsPerWave; ++i) off.b[i] = OpB::src_offset(w, i, lane, a.b_ld);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        off.akc[p] = (uint32_t)OpA::inner_of(w, p, lane);
+        off.bkc[p] = (uint32_t)OpB::inner_of(w, p, lane);
+    }
 
     const int KT = a.ktiles;
-    StageLoads<OpA, OpB> ld;
+    StageLoads<OpA, OpB, RAGGED> ld;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.live());
+        ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim());
 #pragma unroll
-        for (int i = 0; i < L; ++i) ld.issue(i, aoff, boff);
+        for (int i = 0; i < L; ++i) ld.issue(i, off);
         cur_ld.advance();
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
@@ -422,6 +536,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
     for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB>(f[0], u, smem, 0, m0, n0, lane);
 
     int cur = 0;                                  // buffer of the current stage
+    bool prev_full = true;                        // the previous tile stored every piece
     for (int t = first; t < end; t += stride) {
         f32x16 acc[TM][TN];
 #pragma unroll
@@ -434,12 +549,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
             const int nxt = (cur + 1 == S) ? 0 : cur + 1;
 #pragma unroll
             for (int j = 0; j + 1 < NS; ++j)
-                substep<OpA, OpB, TM, TN, false>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, aoff,
-                                                 boff);
+                substep<OpA, OpB, TM, TN, false, RAGGED>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, off);
             // the next stage landed everywhere; nobody reads buffer `cur` any more
             __builtin_amdgcn_sched_barrier(0);
-            if (kt == 0 && t != first) {
-                // The previous tile's epilogue stores were issued after the
+            if (kt == 0 && t != first && (!RAGGED || prev_full)) {
+                // The previous tile's epilogue stores (all kEpiStores of
+                // them: it was not an edge tile) were issued after the
                 // awaited loads; vector memory operations retire in issue
                 // order, so they may stay in flight.
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWaitAfterEpi, 0));
@@ -448,9 +563,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
             }
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.live());
-            substep<OpA, OpB, TM, TN, true>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
-                                            aoff, boff);
+            ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim());
+            substep<OpA, OpB, TM, TN, true, RAGGED>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
+                                            off);
             __builtin_amdgcn_sched_barrier(0);
             cur_ld.advance();
             cur = nxt;
@@ -459,17 +574,29 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
         int bb, tm, tn;
         logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
         const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
-        if (t + stride < end) {
-            epilogue<TILE, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, lane);
-        } else {
+        const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
+        const int64_t m_lim = a.M - r0, n_lim = a.N - c0;   // rows / columns of the quadrant inside C
+        const bool last = t + stride >= end;
+        if (last) {
             // Last tile: only loads past the end (which fetch nothing but
             // still complete into LDS) are outstanding.  Once they have
             // landed and every wave is done reading the last stage, the ring
             // is free for 32-row staging.
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
             asm volatile("s_barrier" ::: "memory");
-            epilogue<TILE, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, lane);
         }
+        // The epilogues' per-lane index arithmetic depends only on the lane;
+        // an opaque copy keeps the compiler from hoisting all of it out of
+        // the tile loop, where it would stay live in registers throughout.
+        int el = lane;
+        if constexpr (RAGGED) asm volatile("" : "+v"(el));
+        if (RAGGED && !full)
+            epilogue<TILE, 8, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
+        else if (last)
+            epilogue<TILE, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+        else
+            epilogue<TILE, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+        prev_full = full;
     }
 }
 
@@ -480,8 +607,13 @@ constexpr int kStages = 2;
 
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
 int launch_t(const GemmDesc& d, KArgs k, hipStream_t s) {
-    k.ktiles = (int32_t)(d.K / kBK);
-    gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16><<<dim3((unsigned)d.grid), dim3(kThreads), 0, s>>>(k);
+    k.ktiles = (int32_t)((d.K + kBK - 1) / kBK);
+    k.krem = (int32_t)(d.K % kBK);
+    const bool ragged = d.M % TILE || d.N % TILE || d.K % kBK;
+    if (ragged)
+        gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16, true><<<dim3((unsigned)d.grid), dim3(kThreads), 0, s>>>(k);
+    else
+        gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16, false><<<dim3((unsigned)d.grid), dim3(kThreads), 0, s>>>(k);
     return (int)hipGetLastError();
 }
 
@@ -525,6 +657,9 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
     k.b_bs = d.b_batch;
     k.c_ld = d.c_row;
     k.c_bs = d.c_batch;
+    k.M = d.M;
+    k.N = d.N;
+    k.K = d.K;
     k.tiles = (int32_t)d.tiles;
     k.tiles_m = (int32_t)d.tiles_m;
     k.tiles_n = (int32_t)d.tiles_n;

@@ -6,7 +6,7 @@
 
 namespace asl {
 
-// K extent of one pipeline stage; K must be a multiple of it.
+// K extent of one pipeline stage (the last stage of a tile may be partial).
 constexpr int kTileK = 64;
 
 // Everything a GEMM launch needs, fixed at plan time.  Strides are elements.

@@ -50,7 +50,7 @@
  *   AS_ERR_UNSUPPORTED  a well-formed request the kernels do not cover
  *                       (operand dtypes other than bf16, a contiguous stride
  *                       other than 1, unaligned pointers or leading strides,
- *                       M/N/K not multiples of the chosen tile)
+ *                       K not a multiple of 8)
  *   AS_ERR_HIP          a HIP launch error (the text is in as_last_error())
  *   AS_ERR_NOMEM        host allocation of a plan failed
  * Nothing is ever computed silently wrong: an unsupported case is refused.
@@ -99,7 +99,10 @@ typedef struct as_gemm_plan* as_gemm_t;
 /*
  * Plan C = A.B for `batch` independent (M x K).(K x N) products.
  *   out          receives the plan handle (host memory)
- *   M, N, K      sizes, > 0
+ *   M, N, K      sizes, > 0; M and N arbitrary, K a multiple of 8.  Edge tiles
+ *                are partial: operand reads past M, N or K return zero
+ *                (range-checked buffer loads) and only C[0..M) x [0..N) is
+ *                written.
  *   batch        number of products, > 0
  *   a, b, c      element strides of A[b,i,k], B[b,k,j], C[b,i,j]
  *   a_t, b_t     must be AS_BF16

@@ -82,11 +82,24 @@ def test_create_rejects_bad_strides():
     del base
 
 
-@pytest.mark.parametrize("M,N,K", [(500, 512, 512), (512, 520, 512), (512, 512, 80), (384, 384, 100)])
-def test_create_refuses_ragged_shapes(M, N, K):
+@pytest.mark.parametrize("M,N,K", [(512, 512, 100), (384, 384, 4), (1, 1, 12)])
+def test_create_refuses_k_not_a_multiple_of_8(M, N, K):
     st = _status(asl.gemm_create, M, N, K, 1, (K + (-K) % 8, 1, 0), (N + (-N) % 8, 1, 0), (N + (-N) % 8, 1, 0))
     assert st == asl.AS_ERR_UNSUPPORTED
-    assert "multiple" in asl.as_last_error()
+    assert "multiple of 8" in asl.as_last_error()
+
+
+@pytest.mark.parametrize("M,N,K,tile", [(500, 512, 512, 128), (512, 520, 512, 128), (512, 512, 80, 128),
+                                        (1, 1, 8, 128), (8000, 8000, 8000, 256), (8100, 8000, 4096, 256),
+                                        (4224, 4224, 4096, 128)])
+def test_ragged_shapes_plan_partial_tiles(M, N, K, tile):
+    # M and N need not be multiples of the tile nor K of the 64-deep stage:
+    # edge tiles are partial, the tile count rounds up.
+    p = asl.gemm_create(M, N, K, 1, (K + (-K) % 8, 1, 0), (N + (-N) % 8, 1, 0), (N + (-N) % 8, 1, 0))
+    tm, tn, tk, tiles, _ = asl.gemm_plan_info(p)
+    assert (tm, tn, tk) == (tile, tile, 64)
+    assert tiles == -(-M // tm) * -(-N // tn)
+    asl.gemm_destroy(p)
 
 
 def test_create_refuses_huge_leading_stride():
@@ -149,6 +162,8 @@ SHAPES = [  # (M, N, K, batch, flags)
     (2048, 2048, 128, 7, 0),                              # 1792 tiles of 128 over 512 workgroups
     (2048, 2048, 128, 7, asl.AS_FLAG_ONE_TILE_PER_WORKGROUP),
     (8192, 8192, 8192, 1, asl.AS_FLAG_NO_GROUPING),
+    (1000, 3000, 96, 3, 0),                               # ragged: partial edge tiles
+    (4100, 4104, 520, 2, asl.AS_FLAG_TILE_256),
 ]
 
 
@@ -156,7 +171,7 @@ SHAPES = [  # (M, N, K, batch, flags)
 def test_schedule_is_a_bijection(M, N, K, batch, flags):
     p = asl.gemm_create(M, N, K, batch, (K, 1, M * K), (N, 1, K * N), (N, 1, M * N), flags=flags)
     tm, tn, _, wg, grid = asl.gemm_plan_info(p)
-    tiles_m, tiles_n = M // tm, N // tn
+    tiles_m, tiles_n = -(-M // tm), -(-N // tn)
     assert wg == batch * tiles_m * tiles_n
     assert grid == (wg if flags & asl.AS_FLAG_ONE_TILE_PER_WORKGROUP else min(wg, 256 if tm == 256 else 512))
     seen = set()

@@ -344,3 +344,121 @@ def test_one_tile_per_workgroup_full_size_sampled():
     w = WORKLOADS["gemm8192"]
     _say("gemm8192 one tile per workgroup, sampled")
     _sampled_gemm(w, flags=asl.AS_FLAG_ONE_TILE_PER_WORKGROUP)
+
+
+# ------------------------------------------------------------ ragged shapes --
+# M and N need not be multiples of the tile, nor K of the 64-deep stage (K a
+# multiple of 8).  Operands live in padded storage whose padding holds NaN
+# bit patterns: a chunk read past K inside a row would turn the result into
+# NaN.  C lives in a larger buffer filled with a sentinel: every element
+# outside [0, M) x [0, N) of every batch must keep it.
+
+_NAN_BF16 = 0x7FC1
+_SENT_F32 = 0x7FC00123
+_SENT_BF16 = 0x7FC3
+
+
+def _padded(rows, cols, batch, ld, seed):
+    """[batch, rows, ld] bf16 storage: integers in [-4, 4] in the first `cols`
+    columns, NaN bit patterns in the padding; also one spare row of NaN."""
+    vals = bits(draw((batch, rows, cols), "int", -4, 4, seed)).astype(np.uint16)
+    st = np.full((batch, rows + 1, ld), _NAN_BF16, dtype=np.uint16)
+    st[:, :rows, :cols] = vals
+    return st, (rows + 1) * ld
+
+
+def _ragged(M, N, K, batch, a_k, b_k, out, flags, seed):
+    lda = (K if a_k else M) + (-(K if a_k else M)) % 8 + 8
+    ldb = (K if b_k else N) + (-(K if b_k else N)) % 8 + 8
+    if a_k:
+        A, abs_ = _padded(M, K, batch, lda, seed)
+        sa = (lda, 1, abs_)
+    else:
+        A, abs_ = _padded(K, M, batch, lda, seed)
+        sa = (1, lda, abs_)
+    if b_k:
+        B, bbs = _padded(N, K, batch, ldb, seed + 1)
+        sb = (1, ldb, bbs)
+    else:
+        B, bbs = _padded(K, N, batch, ldb, seed + 1)
+        sb = (ldb, 1, bbs)
+    bf = out == "bf16"
+    align = 8 if bf else 4
+    ldc = N + (-N) % align + align
+    rows_c = M + 3
+    sent = _SENT_BF16 if bf else _SENT_F32
+    cdt = torch.int16 if bf else torch.int32
+    Cst = torch.full((batch, rows_c, ldc), sent - (1 << 16 if bf and sent >= 1 << 15 else 0), dtype=cdt, device=DEV)
+    Ad = torch.from_numpy(A.view(np.int16)).to(DEV)
+    Bd = torch.from_numpy(B.view(np.int16)).to(DEV)
+    plan = asl.gemm_create(M, N, K, batch, sa, sb, (ldc, 1, rows_c * ldc), asl.AS_BF16, asl.AS_BF16,
+                           asl.AS_BF16 if bf else asl.AS_F32, flags)
+    try:
+        asl.gemm_run(plan, Ad.data_ptr(), Bd.data_ptr(), Cst.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        asl.gemm_destroy(plan)
+    got = Cst.cpu().numpy().view(np.uint16 if bf else np.uint32)
+    Cref, _ = oracle.gemm(A, B, batch, M, N, K, sa, sb, want_T=False)
+    if bf:
+        want = oracle.f64_to_bf16_rne_array(Cref)
+        assert np.array_equal(got[:, :M, :N], want), "bf16 output differs from RNE(oracle)"
+    else:
+        assert np.array_equal(np.ascontiguousarray(got[:, :M, :N]).view(np.float32).astype(np.float64), Cref), \
+            "fp32 output differs"
+    outside = np.ones(got.shape, dtype=bool)
+    outside[:, :M, :N] = False
+    assert np.all(got[outside] == sent), "stores outside the M x N output"
+
+
+RAGGED = [  # (M, N, K, batch, tile flag)
+    (1, 1, 8, 1, asl.AS_FLAG_TILE_128),          # one element, one partial stage
+    (7, 13, 24, 2, asl.AS_FLAG_TILE_128),
+    (129, 130, 72, 1, asl.AS_FLAG_TILE_128),      # 2x2 tiles, one full + one 8-deep stage
+    (300, 517, 200, 2, asl.AS_FLAG_TILE_128),     # N not a multiple of 8: element stores at the edge
+    (257, 300, 136, 1, asl.AS_FLAG_TILE_256),
+    (513, 260, 8, 1, asl.AS_FLAG_TILE_256),
+    (256, 256, 520, 1, asl.AS_FLAG_TILE_256),     # full tiles, partial last stage only
+]
+
+
+@pytest.mark.parametrize("M,N,K,batch,tflag", RAGGED)
+@pytest.mark.parametrize("a_k,b_k", LAYOUTS, ids=lambda v: str(v))
+def test_ragged_shapes_bit_exact_fp32(M, N, K, batch, tflag, a_k, b_k):
+    _say("ragged fp32 M=%d N=%d K=%d b=%d flags=%d a_k=%s b_k=%s" % (M, N, K, batch, tflag, a_k, b_k))
+    _ragged(M, N, K, batch, a_k, b_k, "f32", tflag, 1000 + M + K)
+
+
+@pytest.mark.parametrize("M,N,K,batch,tflag", RAGGED[1:5])
+@pytest.mark.parametrize("a_k,b_k", [(True, False), (False, True)], ids=lambda v: str(v))
+def test_ragged_shapes_bit_exact_bf16(M, N, K, batch, tflag, a_k, b_k):
+    _say("ragged bf16 M=%d N=%d K=%d b=%d flags=%d a_k=%s b_k=%s" % (M, N, K, batch, tflag, a_k, b_k))
+    _ragged(M, N, K, batch, a_k, b_k, "bf16", tflag, 2000 + M + K)
+
+
+@pytest.mark.parametrize("flags", [0, asl.AS_FLAG_ONE_TILE_PER_WORKGROUP])
+def test_ragged_resident_grid_walks_edge_and_interior_tiles(flags):
+    # 17 x 17 x 4 = 1156 tiles of 128 over 512 resident workgroups: walks mix
+    # edge tiles (element stores, full store drain) with interior ones.
+    _say("ragged resident grid flags=%d" % flags)
+    _ragged(2100, 2050, 136, 4, True, False, "f32", asl.AS_FLAG_TILE_128 | flags, 31)
+
+
+def test_ragged_attention_scores():
+    # 3 slices of Q [1000, 96] . K [77, 96]^T: a 96-deep head (one full and
+    # one half stage), 77 keys (N not a multiple of 8), padded S rows.
+    batch, Lq, Lk, d = 3, 1000, 77, 96
+    _say("ragged sscore %dx%dx%dx%d" % (batch, Lq, Lk, d))
+    Q = draw((batch, Lq, d), "int", -4, 4, 41)
+    Kt = draw((batch, Lk, d), "int", -4, 4, 42)
+    ldc = 80
+    S = torch.full((batch, Lq, ldc), float("nan"), dtype=torch.float32, device=DEV)
+    Qd, Kd = Q.to(DEV), Kt.to(DEV)      # keep the device copies alive across the call
+    asl.sscore_run(Qd.data_ptr(), Kd.data_ptr(), S.data_ptr(), batch, Lq, Lk, d,
+                   (d, 1, Lq * d), (d, 1, Lk * d), (ldc, 1, Lq * ldc), asl.AS_BF16, asl.AS_F32,
+                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    Sref, _ = oracle.sscore(bits(Q), bits(Kt), batch, Lq, Lk, d, (d, 1, Lq * d), (d, 1, Lk * d))
+    got = S.cpu().numpy()
+    assert np.array_equal(got[:, :, :Lk].astype(np.float64), Sref)
+    assert np.all(np.isnan(got[:, :, Lk:]))
