@@ -16,6 +16,10 @@ What is computed (pages cited by title and section):
   * Attention scores S_i = Q_i K^T, no scale and no softmax -- "Hopper TMA
     Multicast" deep-dive, Attention/GEMM reuse use-case, equation
     S_0 = Q_0 K^T, S_1 = Q_1 K^T.
+  * Attention forward O = softmax(scale * Q K^T) V (textbook scaled dot
+    product, no mask), the FlashAttention-class operator the score product
+    belongs to -- same deep-dive, Attention/GEMM reuse use-case and the
+    "Attention K/V" row of its comparison table.
   * Tile fan-out microbenchmark accounting (consumers x iterations x tile
     bytes) and per-consumer data checksum -- same deep-dive, sections
     "Microbenchmark source" and "run results".
@@ -73,6 +77,9 @@ def _load():
     lib.oracle_sscore.restype = i32
     lib.oracle_sscore_points.argtypes = [u16p, u16p, ctypes.c_void_p, i64, dp, dp, i64] + [i64] * 6 + [i32]
     lib.oracle_sscore_points.restype = i32
+    lib.oracle_attention.argtypes = [u16p, u16p, u16p, ctypes.c_void_p, i64, dp, dp] + [i64] * 5 + [i64] * 9 + \
+        [ctypes.c_double, i32]
+    lib.oracle_attention.restype = i32
     lib.oracle_tilecast_bytes.argtypes = [i64, i64, i64]
     lib.oracle_tilecast_bytes.restype = ctypes.c_double
     lib.oracle_tilecast_group.argtypes = [i64, i64, i64, i32]
@@ -201,6 +208,61 @@ def sscore_points(Q: np.ndarray, Kt: np.ndarray, pts: np.ndarray, d: int,
     if rc != 0:
         raise RuntimeError("oracle_sscore_points failed")
     return S, T
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, batch: int, Lq: int, Lk: int, d: int, dv: int,
+              sq: Tuple[int, int, int], sk: Tuple[int, int, int], sv: Tuple[int, int, int], scale: float,
+              rows: Optional[np.ndarray] = None, nthreads: int = 0):
+    """O = softmax(scale * Q K^T) V per (b, i) row in fp64; returns (O, TO).
+
+    Q [b,i,d], K [b,j,d], V [b,j,c] addressed by (row, col, batch) element
+    strides.  ``rows``: optional [n, 2] array of (b, i) pairs; then O and TO
+    are [n, dv], else [batch, Lq, dv].  TO = sum_j p_j |V_jc| / sum_j p_j.
+    """
+    Q = np.ascontiguousarray(_as_bits(Q)).reshape(-1)
+    K = np.ascontiguousarray(_as_bits(K)).reshape(-1)
+    V = np.ascontiguousarray(_as_bits(V)).reshape(-1)
+    _span_ok(Q, (batch, Lq, d), (sq[2], sq[0], sq[1]))
+    _span_ok(K, (batch, Lk, d), (sk[2], sk[0], sk[1]))
+    _span_ok(V, (batch, Lk, dv), (sv[2], sv[0], sv[1]))
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+        if r.size and (r[:, 0].min() < 0 or r[:, 0].max() >= batch or r[:, 1].min() < 0 or r[:, 1].max() >= Lq):
+            raise ValueError("row pair out of range")
+        n = r.shape[0]
+        shape = (n, dv)
+    else:
+        r = None
+        n = 0
+        shape = (batch, Lq, dv)
+    O = np.empty(shape, dtype=np.float64)
+    TO = np.empty(shape, dtype=np.float64)
+    rc = _load().oracle_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(r) if r is not None else None, n,
+                                  _ptr(O), _ptr(TO), batch, Lq, Lk, d, dv, sq[0], sq[1], sq[2],
+                                  sk[0], sk[1], sk[2], sv[0], sv[1], sv[2], float(scale), nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle_attention failed")
+    return O, TO
+
+
+# Attention tolerance.  A fused kernel rounds the probabilities p_j to bf16
+# (unit roundoff 2^-8) before the p.V product; that alone moves O by at most
+# 2^-8 * TO.  Score, exponential and fp32 accumulation errors are orders of
+# magnitude smaller at these sizes.  The bound allows twice the rounding term.
+ATTN_RTOL = 2.0 ** -7
+ATTN_ATOL = 1e-6
+
+
+def check_attention(out: np.ndarray, O_ref: np.ndarray, TO: np.ndarray, out_bf16: bool = False):
+    """(n_fail, max_util) for |O_gpu - O_ref| <= 2^-7 * TO + 1e-6 (+ 2^-8 |O_ref|
+    for a bf16 output, its own rounding)."""
+    extra = 2.0 ** -8 * np.abs(O_ref) if out_bf16 else 0.0
+    out = np.asarray(out, dtype=np.float64)
+    bound = ATTN_RTOL * TO + ATTN_ATOL + extra
+    diff = np.abs(out - O_ref)
+    bad = ~np.isfinite(out) | ~(diff <= bound)
+    util = np.where(np.isfinite(diff), diff / bound, np.inf)
+    return int(bad.sum()), float(util.max()) if util.size else 0.0
 
 
 def tilecast_bytes(consumers: int, iters: int, tile_bytes: int) -> float:

@@ -16,6 +16,8 @@
  *    Multicast" deep-dive, section on the Attention/GEMM reuse use-case, the
  *    CTA0/CTA1 equation S_0 = Q_0 K^T, S_1 = Q_1 K^T).  No scale factor and no
  *    softmax are applied: the pages' equation has none.
+ *  - Attention forward O = softmax(scale * Q K^T) V, the FlashAttention-class
+ *    operator the score product belongs to (see oracle_attention).
  *  - The tile fan-out microbenchmark's accounting and data checksum (same
  *    deep-dive, sections "Microbenchmark source" and "run results": each
  *    iteration every consumer loads the tile with index
@@ -238,6 +240,108 @@ int oracle_sscore_points(const uint16_t* Q, const uint16_t* Kt, const int64_t* p
                          int64_t k_row, int64_t k_col, int64_t k_batch, int nthreads) {
     return oracle_gemm_points(Q, Kt, pts, npts, S, T, d, q_row, q_col, q_batch,
                               k_col, k_row, k_batch, nthreads);
+}
+
+/* ---------------------------------------------------- attention forward -- */
+
+/*
+ * Attention forward over the same Q and K: O = softmax(scale * Q K^T) V.
+ * The pages introduce the score product as the inner step of
+ * FlashAttention-class operators whose neighbouring query tiles consume the
+ * same key and value tiles ("Hopper TMA Multicast" deep-dive, Attention/GEMM
+ * reuse use-case and the comparison table's "Attention K/V" row); they do
+ * not spell out the softmax, so this is the textbook scaled-dot-product
+ * attention, without a mask:
+ *   S[b,i,j] = sum_d Q[b,i,d] K[b,j,d]               (d ascending, exact)
+ *   t_j      = scale * S[b,i,j]
+ *   p_j      = exp(t_j - max_j t_j)                  (the max only keeps
+ *                                                      exp in range)
+ *   O[b,i,c] = sum_j p_j V[b,j,c] / sum_j p_j        (j ascending)
+ * and, for the tolerance of a result whose p_j pass through bf16,
+ *   TO[b,i,c] = sum_j p_j |V[b,j,c]| / sum_j p_j.
+ * Rows are the flattened (b, i) pairs listed in `rows` (npairs of them), or
+ * every one of batch*Lq when rows is NULL; O and TO are [rows][dv].
+ */
+typedef struct {
+    const uint16_t *Q, *K, *V;
+    const int64_t* rows;
+    double *O, *TO;
+    int64_t Lq, Lk, d, dv;
+    int64_t q_row, q_col, q_batch, k_row, k_col, k_batch, v_row, v_col, v_batch;
+    double scale;
+    int64_t begin, end;
+} attn_job;
+
+static void* attn_worker(void* arg) {
+    const attn_job* g = (const attn_job*)arg;
+    double* t = (double*)malloc(sizeof(double) * (size_t)g->Lk);
+    if (!t) return (void*)1;
+    for (int64_t r = g->begin; r < g->end; ++r) {
+        int64_t b, i;
+        if (g->rows) { b = g->rows[2 * r]; i = g->rows[2 * r + 1]; }
+        else { b = r / g->Lq; i = r % g->Lq; }
+        const uint16_t* q = g->Q + b * g->q_batch + i * g->q_row;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < g->Lk; ++j) {
+            const uint16_t* k = g->K + b * g->k_batch + j * g->k_row;
+            double s = 0.0;
+            for (int64_t x = 0; x < g->d; ++x)
+                s += oracle_bf16_to_f64(q[x * g->q_col]) * oracle_bf16_to_f64(k[x * g->k_col]);
+            t[j] = g->scale * s;
+            if (t[j] > m) m = t[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < g->Lk; ++j) {
+            t[j] = exp(t[j] - m);
+            l += t[j];
+        }
+        double* o = g->O + r * g->dv;
+        double* to = g->TO ? g->TO + r * g->dv : NULL;
+        for (int64_t c = 0; c < g->dv; ++c) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < g->Lk; ++j) {
+                double v = oracle_bf16_to_f64(g->V[b * g->v_batch + j * g->v_row + c * g->v_col]);
+                acc += t[j] * v;
+                mag += t[j] * fabs(v);
+            }
+            o[c] = acc / l;
+            if (to) to[c] = mag / l;
+        }
+    }
+    free(t);
+    return NULL;
+}
+
+int oracle_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int64_t* rows,
+                     int64_t npairs, double* O, double* TO, int64_t batch, int64_t Lq, int64_t Lk,
+                     int64_t d, int64_t dv, int64_t q_row, int64_t q_col, int64_t q_batch,
+                     int64_t k_row, int64_t k_col, int64_t k_batch,
+                     int64_t v_row, int64_t v_col, int64_t v_batch, double scale, int nthreads) {
+    if (!Q || !K || !V || !O || batch <= 0 || Lq <= 0 || Lk <= 0 || d <= 0 || dv <= 0) return -1;
+    int64_t n = rows ? npairs : batch * Lq;
+    if (n < 0) return -1;
+    if (n == 0) return 0;
+    int nt = resolve_threads(nthreads);
+    if (nt > n) nt = (int)n;
+    pthread_t* th = (pthread_t*)calloc((size_t)nt, sizeof(pthread_t));
+    attn_job* jobs = (attn_job*)calloc((size_t)nt, sizeof(attn_job));
+    if (!th || !jobs) { free(th); free(jobs); return -1; }
+    int rc = 0;
+    for (int w = 0; w < nt; ++w) {
+        attn_job g = {Q, K, V, rows, O, TO, Lq, Lk, d, dv, q_row, q_col, q_batch, k_row, k_col, k_batch,
+                      v_row, v_col, v_batch, scale, n * w / nt, n * (w + 1) / nt};
+        jobs[w] = g;
+        if (pthread_create(&th[w], NULL, attn_worker, &jobs[w]) != 0) { jobs[w].end = -1; rc = -1; }
+    }
+    for (int w = 0; w < nt; ++w) {
+        if (jobs[w].end < 0) continue;
+        void* ret = NULL;
+        pthread_join(th[w], &ret);
+        if (ret) rc = -1;
+    }
+    free(th);
+    free(jobs);
+    return rc;
 }
 
 /* ------------------------------------------------- tile fan-out bench -- */

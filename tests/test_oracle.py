@@ -5,6 +5,7 @@ wrong sign, an exchanged index or stride, a transposed operand, a wrong
 rounding rule -- fails at least one of them; ``test_pins_catch_planted_mistakes``
 plants such slips on the CPU and shows they are caught.
 """
+import math
 import os
 
 import numpy as np
@@ -393,3 +394,145 @@ def test_pins_catch_planted_mistakes():
     # sign slip: -A
     Cn, _ = oracle.gemm(bits((-Ai.float()).to(torch.bfloat16)), bits(Bi), 1, M, N, K, (K, 1, 0), (N, 1, 0))
     assert not np.array_equal(Cn[0], exact)
+
+
+# ------------------------------------------------------ attention forward --
+
+def _attn_ref_library(q, k, v, scale):
+    """softmax(scale q k^T) v with scipy's softmax and numpy's matmul."""
+    import scipy.special
+    return scipy.special.softmax(scale * (q @ k.T), axis=1) @ v
+
+
+def _attn_inputs(b, Lq, Lk, d, dv, seed, dist="normal"):
+    Q = draw((b, Lq, d), dist, -1, 1, seed)
+    K = draw((b, Lk, d), dist, -1, 1, seed + 1)
+    V = draw((b, Lk, dv), dist, -1, 1, seed + 2)
+    return Q, K, V
+
+
+def _attn(Q, K, V, scale, rows=None):
+    b, Lq, d = Q.shape
+    Lk, dv = V.shape[1], V.shape[2]
+    return oracle.attention(bits(Q), bits(K), bits(V), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
+                            (dv, 1, Lk * dv), scale, rows=rows)
+
+
+@pytest.mark.parametrize("b,Lq,Lk,d,dv", [(1, 1, 1, 1, 1), (2, 3, 5, 4, 2), (1, 7, 33, 16, 8), (3, 4, 17, 8, 5)])
+def test_attention_matches_library_softmax_on_tiny_shapes(b, Lq, Lk, d, dv):
+    Q, K, V = _attn_inputs(b, Lq, Lk, d, dv, 700 + Lk)
+    O, TO = _attn(Q, K, V, 0.3)
+    for x in range(b):
+        ref = _attn_ref_library(Q[x].double().numpy(), K[x].double().numpy(), V[x].double().numpy(), 0.3)
+        assert np.allclose(O[x], ref, rtol=0, atol=1e-12 * (1 + np.abs(ref).max()))
+    assert np.all(TO >= np.abs(O) - 1e-12)
+
+
+def test_attention_is_the_mean_of_v_when_keys_are_zero():
+    # every score is 0, so the softmax is uniform: O_i = mean_j V_j
+    Q, _, V = _attn_inputs(2, 5, 24, 8, 6, 710)
+    K = torch.zeros((2, 24, 8), dtype=torch.bfloat16)
+    O, _ = _attn(Q, K, V, 0.7)
+    mean = V.double().numpy().mean(axis=1)
+    for i in range(5):
+        assert np.allclose(O[:, i, :], mean, rtol=0, atol=1e-14)
+
+
+def test_attention_dominant_diagonal_closed_form():
+    # Q = K = a*I (n x n): S = a^2 I, so row i weighs key i by e^x (x = scale a^2)
+    # and every other key by 1: O_i = (e^x V_i + sum_{j != i} V_j) / (e^x + n - 1)
+    n, a, scale = 12, 2.0, 0.8
+    QK = torch.zeros((1, n, n), dtype=torch.bfloat16)
+    for i in range(n):
+        QK[0, i, i] = a
+    V = draw((1, n, 5), "normal", 0, 1, 720)
+    O, _ = _attn(QK, QK, V, scale)
+    v = V[0].double().numpy()
+    ex = np.exp(scale * a * a)
+    for i in range(n):
+        want = (ex * v[i] + (v.sum(axis=0) - v[i])) / (ex + n - 1)
+        assert np.allclose(O[0, i], want, rtol=1e-14, atol=1e-14)
+
+
+def test_attention_exact_powers_of_two():
+    # integer scores and scale = ln 2: every weight is a power of two, so the
+    # result is a ratio of integers known exactly (Fractions)
+    from fractions import Fraction
+    Q = draw((1, 3, 6), "int", -1, 1, 730)
+    K = draw((1, 9, 6), "int", -1, 1, 731)
+    V = draw((1, 9, 4), "int", -4, 4, 732)
+    O, _ = _attn(Q, K, V, math.log(2.0))
+    q, k, v = (t[0].float().numpy().astype(np.int64) for t in (Q, K, V))
+    s = q @ k.T
+    for i in range(3):
+        m = s[i].max()
+        w = [Fraction(2) ** int(s[i, j] - m) for j in range(9)]
+        for c in range(4):
+            want = sum(w[j] * int(v[j, c]) for j in range(9)) / sum(w)
+            assert abs(O[0, i, c] - float(want)) <= 1e-14 * (1 + abs(float(want)))
+
+
+def test_attention_shift_and_key_permutation_invariance():
+    Q, K, V = _attn_inputs(1, 6, 20, 8, 4, 740)
+    O, _ = _attn(Q, K, V, 0.5)
+    # a constant added to every score of a row (an extra dimension: q -> [q, 1], k -> [k, c])
+    Qx = torch.cat([Q, torch.ones((1, 6, 1), dtype=torch.bfloat16)], dim=2)
+    Kx = torch.cat([K, torch.full((1, 20, 1), 3.0, dtype=torch.bfloat16)], dim=2)
+    Ox, _ = _attn(Qx, Kx, V, 0.5)
+    assert np.allclose(Ox, O, rtol=0, atol=1e-13)
+    # keys reordered together with their values
+    perm = torch.randperm(20, generator=torch.Generator().manual_seed(741))
+    Op, _ = _attn(Q, K[:, perm], V[:, perm], 0.5)
+    assert np.allclose(Op, O, rtol=0, atol=1e-13)
+
+
+def test_attention_rows_are_convex_combinations_of_v():
+    Q, K, V = _attn_inputs(2, 8, 30, 16, 6, 750)
+    O, TO = _attn(Q, K, V, 0.9)
+    v = V.double().numpy()
+    assert np.all(O >= v.min(axis=1)[:, None, :] - 1e-13)
+    assert np.all(O <= v.max(axis=1)[:, None, :] + 1e-13)
+    ones = torch.ones_like(V)
+    O1, _ = _attn(Q, K, ones, 0.9)
+    assert np.allclose(O1, 1.0, rtol=0, atol=1e-14)
+
+
+def test_attention_strides_broadcast_and_row_subset():
+    b, Lq, Lk, d, dv = 2, 5, 11, 8, 3
+    Q, K, V = _attn_inputs(b, Lq, Lk, d, dv, 760)
+    O, TO = _attn(Q, K, V, 0.4)
+    # K and V stored transposed ([b, d, Lk] / [b, dv, Lk]) give identical bits
+    Kt = K.transpose(1, 2).contiguous()
+    Vt = V.transpose(1, 2).contiguous()
+    O2, TO2 = oracle.attention(bits(Q), bits(Kt), bits(Vt), b, Lq, Lk, d, dv, (d, 1, Lq * d),
+                               (1, Lk, Lk * d), (1, Lk, Lk * dv), 0.4)
+    assert np.array_equal(O2, O) and np.array_equal(TO2, TO)
+    # batch stride 0 broadcasts K and V
+    Ob, _ = oracle.attention(bits(Q), bits(K[:1]), bits(V[:1]), b, Lq, Lk, d, dv, (d, 1, Lq * d),
+                             (d, 1, 0), (dv, 1, 0), 0.4)
+    O0, _ = _attn(Q, K[:1].expand(b, -1, -1).contiguous(), V[:1].expand(b, -1, -1).contiguous(), 0.4)
+    assert np.array_equal(Ob, O0)
+    # selected rows equal the full result's rows
+    rows = np.array([[1, 4], [0, 0], [1, 2]])
+    Or, TOr = _attn(Q, K, V, 0.4, rows=rows)
+    for n, (x, i) in enumerate(rows):
+        assert np.array_equal(Or[n], O[x, i]) and np.array_equal(TOr[n], TO[x, i])
+
+
+def test_attention_pins_catch_planted_mistakes():
+    """Slips planted on the CPU (wrong scale, transposed V, a dropped key,
+    the softmax taken over queries) are each caught by the library pin."""
+    Lq = Lk = 9
+    d = dv = 9
+    Q, K, V = _attn_inputs(1, Lq, Lk, d, dv, 770)
+    q, k, v = Q[0].double().numpy(), K[0].double().numpy(), V[0].double().numpy()
+    ref = _attn_ref_library(q, k, v, 0.6)
+    ok = lambda O: np.allclose(O[0], ref, rtol=0, atol=1e-12)
+    assert ok(_attn(Q, K, V, 0.6)[0])
+    assert not ok(_attn(Q, K, V, 1.0)[0])                                   # scale dropped
+    Ovt, _ = oracle.attention(bits(Q), bits(K), bits(V), 1, Lq, Lk, d, dv, (d, 1, 0), (d, 1, 0), (1, dv, 0), 0.6)
+    assert not ok(Ovt)                                                      # V transposed
+    Od, _ = oracle.attention(bits(Q), bits(K), bits(V), 1, Lq, Lk - 1, d, dv, (d, 1, 0), (d, 1, 0), (dv, 1, 0), 0.6)
+    assert not np.allclose(Od[0], ref, rtol=0, atol=1e-12)                  # last key dropped
+    Oq, _ = _attn(K, Q, V, 0.6)
+    assert not ok(Oq)                                                       # softmax over queries

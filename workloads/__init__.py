@@ -10,8 +10,9 @@ both are rounded to bf16 (round-to-nearest-even, torch's conversion).  An
 operand is drawn in its STORAGE order (a column-major matrix is drawn as its
 row-major transpose), so the bits depend only on (seed, shape, distribution).
 
-The five workloads are dense, unstructured matrices; the pages measure no
-public dataset, so nothing here stands in for one.
+The five contraction workloads and the attention-forward workload are dense,
+unstructured matrices; the pages measure no public dataset, so nothing here
+stands in for one.
 """
 from __future__ import annotations
 
@@ -99,6 +100,61 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 ORDER = ["gemm512", "sscore32x2048", "gemm8192", "gemm65536x256x4096", "gemm16384x8192x2048_colA"]
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """Attention forward O = softmax(scale Q K^T) V over `batch` slices;
+    Q [Lq, d], K [Lk, d], V [Lk, dv], O [Lq, dv], all with the last
+    dimension contiguous."""
+    name: str
+    batch: int
+    Lq: int
+    Lk: int
+    d: int
+    dv: int
+    dist: str
+    lo: float
+    hi: float
+    seeds: Tuple[int, int, int]   # Q, K, V
+    scale: float
+    out: str                      # "f32" or "bf16"
+    description: str
+
+    @property
+    def flop(self) -> float:
+        """Q.K^T and P.V: 2*b*Lq*Lk*(d + dv)."""
+        return 2.0 * self.batch * self.Lq * self.Lk * (self.d + self.dv)
+
+    def strides(self):
+        """(row, col, batch) element strides of Q, K, V and O."""
+        return ((self.d, 1, self.Lq * self.d), (self.d, 1, self.Lk * self.d),
+                (self.dv, 1, self.Lk * self.dv), (self.dv, 1, self.Lq * self.dv))
+
+    @property
+    def bytes_in(self) -> int:
+        return 2 * self.batch * (self.Lq * self.d + self.Lk * self.d + self.Lk * self.dv)
+
+    @property
+    def bytes_out(self) -> int:
+        return (4 if self.out == "f32" else 2) * self.batch * self.Lq * self.dv
+
+
+# The attention forward consumes the score workload's very Q and K (same
+# seeds, shapes and distribution) plus a V drawn alike.
+ATTN_WORKLOADS: Dict[str, AttnWorkload] = {
+    "attn32x2048": AttnWorkload(
+        "attn32x2048", 32, 2048, 2048, 128, 128, "normal", 0.0, 1.0, (201, 202, 203), 128 ** -0.5, "bf16",
+        "attention forward O=softmax(Q.K^T/sqrt(128)).V, 32 slices of Q,K,V [2048,128], N(0,1), bf16 O"),
+}
+
+
+def attn_operands(w: AttnWorkload):
+    """(Q, K, V) bf16 CPU tensors [batch, L, d] for attention workload ``w``."""
+    Q = draw((w.batch, w.Lq, w.d), w.dist, w.lo, w.hi, w.seeds[0])
+    K = draw((w.batch, w.Lk, w.d), w.dist, w.lo, w.hi, w.seeds[1])
+    V = draw((w.batch, w.Lk, w.dv), w.dist, w.lo, w.hi, w.seeds[2])
+    return Q, K, V
 
 
 def draw(shape, dist: str, lo: float, hi: float, seed: int) -> torch.Tensor:
