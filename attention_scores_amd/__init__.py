@@ -29,7 +29,7 @@ AS_FLAG_TILE_256 = 0x4
 AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
-            "sscore_run", "tilecast_run", "as_status_str", "as_last_error")
+            "sscore_run", "attn_fwd_run", "tilecast_run", "as_status_str", "as_last_error")
 
 
 class Strides(ctypes.Structure):
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.sscore_run.argtypes = [vp, vp, vp, i64, i64, i64, i64, Strides, Strides, Strides,
                                  ctypes.c_int, ctypes.c_int, vp]
         L.sscore_run.restype = ctypes.c_int
+        L.attn_fwd_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, Strides, Strides, Strides, Strides,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        L.attn_fwd_run.restype = ctypes.c_int
         L.tilecast_run.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
         L.tilecast_run.restype = ctypes.c_int
         L.as_status_str.argtypes = [ctypes.c_int]
@@ -136,6 +139,15 @@ def gemm_plan_tile_of(plan: int, slot: int):
     b, r, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     _check(lib().gemm_plan_tile_of(plan, slot, ctypes.byref(b), ctypes.byref(r), ctypes.byref(c)))
     return b.value, r.value, c.value
+
+
+def attn_fwd_run(Q: int, K: int, V: int, O: int, batch: int, Lq: int, Lk: int, d: int, dv: int,
+                 q: Tuple[int, int, int], k: Tuple[int, int, int], v: Tuple[int, int, int],
+                 o: Tuple[int, int, int], scale: float, qkv_t: int = AS_BF16, o_t: int = AS_BF16,
+                 stream: int = 0) -> None:
+    """O = softmax(scale Q K^T) V on device pointers (see attn_fwd_run in attn_scores.h)."""
+    _check(lib().attn_fwd_run(Q, K, V, O, batch, Lq, Lk, d, dv, Strides(*q), Strides(*k), Strides(*v),
+                              Strides(*o), float(scale), qkv_t, o_t, stream))
 
 
 def sscore_run(Q: int, K: int, S: int, batch: int, Lq: int, Lk: int, dim: int, q: Tuple[int, int, int],
@@ -246,6 +258,29 @@ def sscore(Q, K, out=None, out_dtype=None):
     _require_cuda(out)
     sscore_run(Q.data_ptr(), K.data_ptr(), out.data_ptr(), b, Lq, Lk, d, _strides3(Q), _strides3(K),
                _strides3(out), _dtype_code(Q.dtype), _dtype_code(out.dtype), _stream_handle(Q))
+    return out
+
+
+def attention(Q, K, V, scale=None, out=None, out_dtype=None):
+    """O = softmax(scale Q K^T) V per slice: Q [b,Lq,d], K [b,Lk,d], V [b,Lk,dv]
+    bf16 -> O [b,Lq,dv] (default scale 1/sqrt(d), bf16 output)."""
+    torch = _torch()
+    _require_cuda(Q, K, V)
+    if Q.dim() != 3 or K.dim() != 3 or V.dim() != 3:
+        raise AsError(AS_ERR_INVALID, "Q, K and V must be [batch, L, d]")
+    b, Lq, d = Q.shape
+    Lk, dv = V.shape[1], V.shape[2]
+    if K.shape[0] != b or V.shape[0] != b or K.shape[2] != d or K.shape[1] != Lk:
+        raise AsError(AS_ERR_INVALID, "Q, K and V shapes do not match")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        od = out_dtype if out_dtype is not None else torch.bfloat16
+        out = torch.empty((b, Lq, dv), dtype=od, device=Q.device)
+    _require_cuda(out)
+    attn_fwd_run(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), b, Lq, Lk, d, dv, _strides3(Q),
+                 _strides3(K), _strides3(V), _strides3(out), scale, _dtype_code(Q.dtype), _dtype_code(out.dtype),
+                 _stream_handle(Q))
     return out
 
 

@@ -3,6 +3,7 @@
 #include "attn_scores.h"
 
 #include <cinttypes>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -290,6 +291,53 @@ as_status sscore_run(const void* Q, const void* K, void* S,
     next_slot = (next_slot + 1) % 8;
     if (cached < 8) ++cached;
     return run_desc(d, Q, K, S, hip_stream);
+}
+
+as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t Lq,
+                       int64_t Lk, int64_t d, int64_t dv, as_strides q, as_strides k, as_strides v,
+                       as_strides o, float scale, as_dtype qkv_t, as_dtype o_t, void* hip_stream) {
+    if (batch <= 0 || Lq <= 0 || Lk <= 0 || d <= 0 || dv <= 0)
+        return fail(AS_ERR_INVALID, "sizes must be positive (batch=%" PRId64 " Lq=%" PRId64 " Lk=%" PRId64
+                    " d=%" PRId64 " dv=%" PRId64 ")", batch, Lq, Lk, d, dv);
+    for (as_dtype t : {qkv_t, o_t})
+        if (t != AS_BF16 && t != AS_F32) return fail(AS_ERR_INVALID, "unknown dtype %d", (int)t);
+    if (!std::isfinite(scale)) return fail(AS_ERR_INVALID, "scale must be finite");
+    const int64_t sv[12] = {q.row, q.col, q.batch, k.row, k.col, k.batch, v.row, v.col, v.batch,
+                            o.row, o.col, o.batch};
+    for (int64_t x : sv)
+        if (x < 0) return fail(AS_ERR_INVALID, "negative stride %" PRId64, x);
+    if (o.row < dv && Lq > 1) return fail(AS_ERR_INVALID, "O rows overlap (row stride %" PRId64 " < dv)", o.row);
+    if (batch > 1 && o.batch < Lq * o.row)
+        return fail(AS_ERR_INVALID, "O batches overlap (batch stride %" PRId64 ")", o.batch);
+    if (!Q || !K || !V || !O) return fail(AS_ERR_INVALID, "null device pointer");
+    if (qkv_t != AS_BF16) return fail(AS_ERR_UNSUPPORTED, "Q, K and V must be bf16");
+    if (d != dv || (d != 64 && d != 128))
+        return fail(AS_ERR_UNSUPPORTED, "head dimensions d = dv in {64, 128} only (d=%" PRId64 " dv=%" PRId64 ")",
+                    d, dv);
+    if (q.col != 1 || k.col != 1 || v.col != 1 || o.col != 1)
+        return fail(AS_ERR_UNSUPPORTED, "Q, K, V and O need a contiguous last dimension (column stride 1)");
+    if (q.row % 8 || k.row % 8 || v.row % 8 || o.row % 4)
+        return fail(AS_ERR_UNSUPPORTED, "row strides must be multiples of 8 elements (O: 4)");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+        return fail(AS_ERR_UNSUPPORTED, "device pointers must be 16-byte aligned");
+    if (Lq > INT32_MAX / 2 || Lk > INT32_MAX / 2) return fail(AS_ERR_UNSUPPORTED, "sequence too long");
+    // 32-bit offsets inside one staged 64-key tile.
+    if (64 * k.row * 2 >= (INT64_C(1) << 31) || 64 * v.row * 2 >= (INT64_C(1) << 31))
+        return fail(AS_ERR_UNSUPPORTED, "K or V row stride too large for 32-bit tile offsets");
+    asl::AttnDesc ad{};
+    ad.batch = batch; ad.Lq = Lq; ad.Lk = Lk; ad.d = d;
+    ad.q_row = q.row; ad.q_batch = q.batch;
+    ad.k_row = k.row; ad.k_batch = k.batch;
+    ad.v_row = v.row; ad.v_batch = v.batch;
+    ad.o_row = o.row; ad.o_batch = o.batch;
+    ad.o_bf16 = (o_t == AS_BF16);
+    ad.c = (float)((double)scale * 1.4426950408889634);   // log2(e)
+    ad.qtiles = (Lq + asl::kAttnQueriesPerWorkgroup - 1) / asl::kAttnQueriesPerWorkgroup;
+    if (ad.qtiles > INT32_MAX / batch) return fail(AS_ERR_UNSUPPORTED, "too many query tiles");
+    ad.tiles = batch * ad.qtiles;
+    int e = asl::launch_attn(ad, Q, K, V, O, hip_stream);
+    if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
+    return ok();
 }
 
 as_status tilecast_run(const void* buf, int64_t rows, int64_t cols, int32_t tile_m, int32_t tile_n,

@@ -25,6 +25,8 @@
 //   MFMA            v_mfma_f32_32x32x16_bf16, fp32 accumulators.
 //   epilogue        fp32 stores, or round-to-nearest-even to bf16.
 //
+// Lane maps and the operand tile's LDS layout: tile.hpp.
+//
 // Edges.  M and N need not be multiples of the tile, nor K of BK (K must be
 // a multiple of 8, one 16-byte chunk).  Every stage's buffer resource covers
 // exactly the operand bytes from the stage origin to the operand's last
@@ -34,40 +36,16 @@
 // are given out-of-range offsets and also read as zero.  Every product term
 // with k >= K is therefore 0 * 0, and outputs outside M x N are not stored.
 //
-// Lane maps (measured on gfx950 with a probe kernel):
-//   MFMA 32x32x16 bf16: A operand lane l = row l%32, k (l/32)*8+e (e<8);
-//     B operand lane l = column l%32, k (l/32)*8+e; result element e of lane
-//     l = row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-//   ds_read_b64_tr_b16: within each 16-lane group, result lane i element j is
-//     element i%4 of the 8 bytes addressed by lane 4j + i/4 of the group.
-//   buffer/global_load ... lds dwordx4: lane l's 16 bytes land at
-//     LDS base + 16*l.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "internal.hpp"
 #include "schedule.hpp"
+#include "tile.hpp"
 
 namespace asl {
 namespace kern {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-typedef __attribute__((address_space(3))) i16x8 lds_i16x8_t;
-typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
-
-constexpr int kWaves = 4;      // 2 x 2
-constexpr int kThreads = 64 * kWaves;
-
-// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
-// no swizzle, offsets checked against num_records.
-constexpr int kRsrcWord3 = 0x00020000;
 
 struct KArgs {
     const uint16_t* A;
@@ -81,123 +59,6 @@ struct KArgs {
     int32_t krem;         // K mod BK: valid k of the last stage (0: the last stage is full)
     int32_t tiles, tiles_m, tiles_n, group_m, grouped;
 };
-
-// A lane offset past any buffer resource's range (ranges are < 2^31 bytes):
-// the load returns zeros.
-constexpr uint32_t kOob = 0x80000000u;
-
-// Swizzle of a K-contiguous tile (rows of BK k = CHR chunks of 16 B): chunk
-// c of row r is stored in slot c ^ swz_k<CHR>(r).  A fragment read touches
-// one chunk index in 32 consecutive rows; with these XORs any 8 consecutive
-// rows fall in 8 distinct 16-byte bank groups of a 128-byte bank line and
-// any 16 in 16 distinct groups of a 256-byte line.
-//   CHR = 4 (64-byte rows): rows with equal r mod 4 get distinct slots;
-//   CHR = 8 (128-byte rows): rows with equal r mod 2 get distinct slots.
-template <int CHR>
-__device__ __forceinline__ int swz_k(int r) {
-    if constexpr (CHR == 4) return ((r >> 2) ^ (r >> 1)) & 3;
-    else return (r & 7) ^ ((r >> 3) & 1);
-}
-
-// Swizzle of an MN-contiguous tile (rows are k, CH chunks of 16 B per row):
-// chunk c of row k is stored in slot c ^ swz_mn(k).  The transposing reads
-// touch 4 consecutive chunks of 4 consecutive rows; the XOR spreads them over
-// 16 distinct bank groups.
-template <int CH>
-__device__ __forceinline__ int swz_mn(int k) { return ((k & 3) << 2) & (CH - 1); }
-
-// Buffer resource over `bytes` bytes at `base`.  The operands are wave
-// uniform by construction; readfirstlane makes that visible to the compiler
-// so the descriptor lives in SGPRs (the loads take it as a scalar operand).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-    void* q = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
-}
-
-// s_waitcnt immediate for the gfx9 family: vmcnt <= vm (6 bits, split
-// [3:0] and [15:14]), lgkmcnt <= lgkm (4 bits [11:8]), expcnt unconstrained.
-constexpr int waitcnt_imm(int vm, int lgkm) {
-    return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
-}
-
-// One operand tile of R (M or N extent) x BK (K) bf16 per pipeline stage.
-template <int R, bool KMAJ, int BK>
-struct OperandTile {
-    static constexpr int kBytes = R * BK * 2;
-    static constexpr int kCHR = BK / 8;                              // chunks per row (K-major)
-    static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;   // 1 KiB per wave-wide load
-    static constexpr int kCH = R / 8;                                // chunks per row (MN-major)
-    static constexpr bool kKMaj = KMAJ;
-
-    // Byte offset, relative to the tile origin in global memory, of the 16
-    // bytes that lane `lane` of wave `w` fetches in its i-th load; the data
-    // lands at LDS byte (w*kLoadsPerWave + i)*1024 + lane*16.
-    __device__ static uint32_t src_offset(int w, int i, int lane, int64_t ld) {
-        int p = (w * kLoadsPerWave + i) * 64 + lane;      // destination chunk index
-        if constexpr (KMAJ) {
-            int r = p / kCHR, s = p % kCHR;
-            int c = s ^ swz_k<kCHR>(r);
-            return (uint32_t)(((int64_t)r * ld + c * 8) * 2);
-        } else {
-            int k = p / kCH, s = p % kCH;
-            int c = s ^ swz_mn<kCH>(k);
-            return (uint32_t)(((int64_t)k * ld + c * 8) * 2);
-        }
-    }
-
-    // Element offset, along the contiguous dimension, of the chunk that lane
-    // `lane` of wave `w` fetches in its i-th load (k within the stage for a
-    // K-contiguous operand).
-    __device__ static int inner_of(int w, int i, int lane) {
-        int p = (w * kLoadsPerWave + i) * 64 + lane;
-        if constexpr (KMAJ) {
-            int r = p / kCHR, s = p % kCHR;
-            return (s ^ swz_k<kCHR>(r)) * 8;
-        } else {
-            int k = p / kCH, s = p % kCH;
-            return (s ^ swz_mn<kCH>(k)) * 8;
-        }
-    }
-
-    // Fragment for MFMA operand rows/columns [mn0, mn0+32) and k16 substep j
-    // (< BK/16): lane l receives 8 consecutive k of row/column mn0 + l%32.
-    __device__ static bf16x8 frag(const char* lds, int mn0, int j, int lane) {
-        if constexpr (KMAJ) {
-            int r = mn0 + (lane & 31);
-            int c = 2 * j + (lane >> 5);
-            const lds_i16x8_t* p = (const lds_i16x8_t*)(lds + r * (BK * 2) + ((c ^ swz_k<kCHR>(r)) << 4));
-            i16x8 v = *p;
-            return __builtin_bit_cast(bf16x8, v);
-        } else {
-            int g = lane >> 4, s = lane & 15;
-            int col = mn0 + (g & 1) * 16 + 4 * (s & 3);
-            int cc = col >> 3, sub = (col & 7) * 2;
-            int k0 = 16 * j + (g >> 1) * 8 + (s >> 2);
-            int k1 = k0 + 4;
-            const char* p0 = lds + k0 * (R * 2) + ((cc ^ swz_mn<kCH>(k0)) << 4) + sub;
-            const char* p1 = lds + k1 * (R * 2) + ((cc ^ swz_mn<kCH>(k1)) << 4) + sub;
-            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
-            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p1);
-            i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            return __builtin_bit_cast(bf16x8, v);
-        }
-    }
-};
-
-// One 16-byte-per-lane global -> LDS load: lane l's bytes at rsrc base +
-// voff land at LDS address m0 + 16*l.  Issued as inline assembly so that the
-// compiler does not insert its own (conservative) vmcnt waits before later
-// LDS reads; the kernel orders these loads explicitly (s_waitcnt vmcnt + s_barrier).
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
 
 // Per-lane source offsets of a wave's stage loads.  For the last, partial K
 // stage of a K-contiguous operand, a chunk at k >= K would read the next

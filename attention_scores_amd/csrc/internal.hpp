@@ -32,6 +32,19 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
 // grid; the device schedule, shared with the kernels).  False if empty.
 bool tile_of_slot(const GemmDesc& d, int64_t i, int64_t* b, int64_t* tm, int64_t* tn);
 
+// Attention forward O = softmax(scale Q K^T) V, d == dv in {64, 128}.
+// Strides are elements; every operand's last dimension is contiguous.
+constexpr int kAttnQueriesPerWorkgroup = 256;
+struct AttnDesc {
+    int64_t batch, Lq, Lk, d;
+    int64_t q_row, q_batch, k_row, k_batch, v_row, v_batch, o_row, o_batch;
+    bool o_bf16;
+    float c;                         // scale * log2(e)
+    int64_t qtiles, tiles;           // query tiles per slice, workgroups
+};
+
+int launch_attn(const AttnDesc& d, const void* Q, const void* K, const void* V, void* O, void* stream);
+
 struct TilecastDesc {
     const void* buf;
     int64_t rows, cols;

@@ -4,6 +4,7 @@
  * Operations
  *   gemm_*      C[b,i,j] = sum_k A[b,i,k] * B[b,k,j]          (beta = 0, no alpha)
  *   sscore_run  S[b,i,j] = sum_d Q[b,i,d] * K[b,j,d]  = Q.K^T  (no scale, no softmax)
+ *   attn_fwd_run  O = softmax(scale * Q.K^T) V, fused (the scores stay on chip)
  *   tilecast_run  tile fan-out microbenchmark
  *
  * Where the operations are defined:
@@ -154,6 +155,32 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
                      int64_t batch, int64_t Lq, int64_t Lk, int64_t dim,
                      as_strides q, as_strides k, as_strides s,
                      as_dtype qk_t, as_dtype s_t, void* hip_stream);
+
+/*
+ * Attention forward O[b] = softmax(scale * Q[b] K[b]^T) V[b]: for every
+ * query i, O[b,i,:] = sum_j p_j V[b,j,:] / sum_j p_j with
+ * p_j = exp(scale * S[b,i,j] - max_j scale * S[b,i,j]) and S the scores of
+ * sscore_run.  No mask.  The score product is the inner step of the
+ * FlashAttention-class operators whose neighbouring query tiles consume the
+ * same key and value tiles ("Hopper TMA Multicast" deep-dive, Attention/GEMM
+ * reuse use-case and the comparison table's "Attention K/V" row); the
+ * softmax is the textbook scaled dot-product attention, which the pages name
+ * but do not write out.  One fused kernel: the scores stay in registers.
+ *   Q [batch, Lq, d], K [batch, Lk, d], V [batch, Lk, dv], O [batch, Lq, dv],
+ *   each addressed by (row, col, batch) element strides with col == 1;
+ *   row strides multiples of 8 (O: 4), pointers 16-byte aligned.
+ *   d == dv, 64 or 128.  Lq, Lk >= 1, any length.  qkv_t AS_BF16; o_t AS_BF16
+ *   (round-to-nearest-even) or AS_F32.  scale finite.
+ * Numerics: scores accumulate in fp32; probabilities are rounded to bf16
+ * before the P.V product (fp32 accumulation); the result is divided by the
+ * fp32 sum of the unrounded probabilities.  Errors as for the other entry
+ * points (AS_ERR_UNSUPPORTED: other head sizes, dtypes, strides or
+ * alignments).  Asynchronous on `hip_stream`.
+ */
+AS_API as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O,
+                              int64_t batch, int64_t Lq, int64_t Lk, int64_t d, int64_t dv,
+                              as_strides q, as_strides k, as_strides v, as_strides o,
+                              float scale, as_dtype qkv_t, as_dtype o_t, void* hip_stream);
 
 /*
  * Tile fan-out microbenchmark.  `consumers` workgroups (a multiple of 8, at

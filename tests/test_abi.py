@@ -268,3 +268,32 @@ def test_tilecast_argument_checks():
     assert st(tile_m=1024) == asl.AS_ERR_UNSUPPORTED       # 128 KiB tile
     assert st(rows=4000) == asl.AS_ERR_UNSUPPORTED
     assert st(buf=24) == asl.AS_ERR_UNSUPPORTED
+
+
+def test_attn_fwd_argument_checks():
+    q = (128, 1, 2048 * 128)
+    o = (128, 1, 2048 * 128)
+    ok = dict(batch=2, Lq=2048, Lk=2048, d=128, dv=128)
+
+    def st(Q=16, K=32, V=48, O=64, q=q, k=q, v=q, o=o, scale=0.1, qkv_t=asl.AS_BF16, o_t=asl.AS_BF16, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return _status(asl.attn_fwd_run, Q, K, V, O, a["batch"], a["Lq"], a["Lk"], a["d"], a["dv"], q, k, v, o,
+                       scale, qkv_t, o_t)
+
+    assert st(batch=0) == asl.AS_ERR_INVALID
+    assert st(Lk=0) == asl.AS_ERR_INVALID
+    assert st(O=0) == asl.AS_ERR_INVALID                                   # null
+    assert st(scale=float("inf")) == asl.AS_ERR_INVALID
+    assert st(o_t=7) == asl.AS_ERR_INVALID
+    assert st(q=(-128, 1, 0)) == asl.AS_ERR_INVALID
+    assert st(o=(64, 1, 2048 * 64)) == asl.AS_ERR_INVALID                  # O rows overlap
+    assert st(o=(128, 1, 1000)) == asl.AS_ERR_INVALID                      # O batches overlap
+    assert st(d=96, dv=96, q=(96, 1, 0), k=(96, 1, 0), v=(96, 1, 0), o=(96, 1, 2048 * 96)) == asl.AS_ERR_UNSUPPORTED
+    assert st(dv=64) == asl.AS_ERR_UNSUPPORTED                             # d != dv
+    assert st(qkv_t=asl.AS_F32) == asl.AS_ERR_UNSUPPORTED
+    assert st(k=(128, 2, 0)) == asl.AS_ERR_UNSUPPORTED                     # non-contiguous last dim
+    assert st(v=(132, 1, 0)) == asl.AS_ERR_UNSUPPORTED                     # row stride % 8
+    assert st(Q=24) == asl.AS_ERR_UNSUPPORTED                              # misaligned
+    assert st(k=(1 << 24, 1, 0)) == asl.AS_ERR_UNSUPPORTED                 # 32-bit tile offsets
+    assert "16-byte" not in asl.as_last_error()

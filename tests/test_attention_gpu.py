@@ -1,0 +1,162 @@
+"""GPU parity of the fused attention forward (through the C ABI) against the oracle.
+
+Bars: on data whose every probability is a power of two down to 2^-8
+(integer scores in [-4, 4] with scale ln 2) the bf16 probabilities, both
+products and every partial sum are exact in fp32; what remains are the
+hardware exp2's last-bit errors (in the fp32 sum of probabilities and the
+running rescale factors, about 1 ulp each) and the final division, which
+together stay far below |O_gpu - O_ref| <= 2^-18 * TO.  A dropped key tile,
+a wrong rescale or a key permutation slip moves O by orders of magnitude
+more.  On general
+data the probabilities pass through bf16: |O_gpu - O_ref| <= 2^-7 * TO + 1e-6
+(+ 2^-8 |O_ref| for a bf16 output), TO = sum_j p_j |v_j| / sum_j p_j.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_scores_amd as asl
+import oracle
+from workloads import ATTN_WORKLOADS, attn_operands, bits, draw
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    asl.lib()  # fails loudly if the HIP library is missing
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0):
+    """Q, K, V: CPU bf16 [b, L, d]; returns the decoded output [b, Lq, dv] and the raw buffer."""
+    b, Lq, d = Q.shape
+    Lk, dv = V.shape[1], V.shape[2]
+    ldo = ldo or dv
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    Ob = torch.full((b, Lq + rows_pad, ldo), float("nan"), dtype=od, device=DEV)
+    asl.attn_fwd_run(Qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), Ob.data_ptr(), b, Lq, Lk, d, dv,
+                     (d, 1, Lq * d), (d, 1, Lk * d), (dv, 1, Lk * dv), (ldo, 1, (Lq + rows_pad) * ldo), scale,
+                     asl.AS_BF16, asl.AS_BF16 if out == "bf16" else asl.AS_F32,
+                     torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    raw = Ob.float().cpu().numpy().astype(np.float64)
+    return raw[:, :Lq, :dv], raw
+
+
+def _ref(Q, K, V, scale, rows=None):
+    b, Lq, d = Q.shape
+    Lk, dv = V.shape[1], V.shape[2]
+    return oracle.attention(bits(Q), bits(K), bits(V), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
+                            (dv, 1, Lk * dv), scale, rows=rows)
+
+
+def _sparse_q(b, Lq, d, seed):
+    """Entries in {-1, 0, 1}, exactly four nonzeros per row."""
+    g = torch.Generator().manual_seed(seed)
+    Q = torch.zeros((b, Lq, d), dtype=torch.float32)
+    idx = torch.argsort(torch.rand((b, Lq, d), generator=g), dim=2)[:, :, :4]
+    sign = torch.randint(0, 2, (b, Lq, 4), generator=g).float() * 2 - 1
+    Q.scatter_(2, idx, sign)
+    return Q.to(torch.bfloat16)
+
+
+EXACT = [  # (batch, Lq, Lk, d)
+    (2, 256, 128, 128),
+    (1, 512, 640, 64),
+    (1, 300, 77, 128),      # ragged queries and keys (last key tile 13 of 64)
+    (3, 97, 1, 64),         # a single key
+    (1, 1, 200, 128),
+]
+
+
+@pytest.mark.parametrize("b,Lq,Lk,d", EXACT)
+def test_exact_power_of_two_probabilities(b, Lq, Lk, d):
+    _say("attn exact b=%d Lq=%d Lk=%d d=%d" % (b, Lq, Lk, d))
+    Q = _sparse_q(b, Lq, d, 900 + Lq)
+    K = draw((b, Lk, d), "int", -1, 1, 901 + Lk)
+    V = draw((b, Lk, d), "int", -4, 4, 902 + d)
+    got, _ = _run(Q, K, V, math.log(2.0), out="f32")
+    ref, TO = _ref(Q, K, V, math.log(2.0))
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= 2.0 ** -18 * TO), "max err/TO %.3g, max err/|O| %.3g" % (
+        (err / TO).max(), (err / np.maximum(np.abs(ref), 1e-30)).max())
+
+
+RANDOM = [  # (batch, Lq, Lk, d, out)
+    (2, 512, 512, 128, "bf16"),
+    (2, 512, 512, 128, "f32"),
+    (1, 300, 1000, 64, "f32"),
+    (3, 129, 77, 128, "bf16"),
+    (1, 1024, 2048, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("b,Lq,Lk,d,out", RANDOM)
+def test_random_data_within_tolerance(b, Lq, Lk, d, out):
+    _say("attn random b=%d Lq=%d Lk=%d d=%d out=%s" % (b, Lq, Lk, d, out))
+    Q = draw((b, Lq, d), "normal", 0, 1, 910 + Lq)
+    K = draw((b, Lk, d), "normal", 0, 1, 911 + Lk)
+    V = draw((b, Lk, d), "normal", 0, 1, 912 + d)
+    scale = d ** -0.5
+    got, _ = _run(Q, K, V, scale, out=out)
+    ref, TO = _ref(Q, K, V, scale)
+    nfail, util = oracle.check_attention(got, ref, TO, out_bf16=(out == "bf16"))
+    assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
+
+
+def test_padded_output_leaves_the_rest_untouched():
+    # O rows of stride 136 with 2 spare rows per slice: only [0, Lq) x [0, dv) is written
+    b, Lq, Lk, d = 2, 300, 200, 128
+    Q = draw((b, Lq, d), "normal", 0, 1, 920)
+    K = draw((b, Lk, d), "normal", 0, 1, 921)
+    V = draw((b, Lk, d), "normal", 0, 1, 922)
+    got, raw = _run(Q, K, V, 0.1, out="f32", ldo=136, rows_pad=2)
+    ref, TO = _ref(Q, K, V, 0.1)
+    assert oracle.check_attention(got, ref, TO)[0] == 0
+    mask = np.ones(raw.shape, dtype=bool)
+    mask[:, :Lq, :d] = False
+    assert np.all(np.isnan(raw[mask]))
+
+
+def test_workload_sampled_rows_and_determinism():
+    w = ATTN_WORKLOADS["attn32x2048"]
+    _say("attn workload %s sampled" % w.name)
+    Q, K, V = attn_operands(w)
+    got, _ = _run(Q, K, V, w.scale, out=w.out)
+    again, _ = _run(Q, K, V, w.scale, out=w.out)
+    assert np.array_equal(got, again)
+    rng = np.random.default_rng(930)
+    rows = np.stack([rng.integers(0, w.batch, 96), rng.integers(0, w.Lq, 96)], axis=1)
+    rows = np.concatenate([rows, [[0, 0], [w.batch - 1, w.Lq - 1], [5, 255], [5, 256]]])
+    ref, TO = _ref(Q, K, V, w.scale, rows=rows)
+    sel = got[rows[:, 0], rows[:, 1]]
+    nfail, util = oracle.check_attention(sel, ref, TO, out_bf16=(w.out == "bf16"))
+    assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
+
+
+def test_matches_the_unfused_path_on_the_score_workload():
+    # softmax of the scores sscore_run writes, times V, agrees with the fused
+    # result (both against the oracle's bound) on two slices of the workload
+    w = ATTN_WORKLOADS["attn32x2048"]
+    Q, K, V = (t[:2].contiguous() for t in attn_operands(w))
+    got, _ = _run(Q, K, V, w.scale, out="f32")
+    S = asl.sscore(Q.to(DEV), K.to(DEV))
+    P = torch.softmax(S.double() * w.scale, dim=2)
+    O = (P @ V.to(DEV).double()).cpu().numpy()
+    ref, TO = _ref(Q, K, V, w.scale, rows=np.array([[b, i] for b in range(2) for i in range(0, w.Lq, 37)]))
+    sel = O[:, ::37].reshape(-1, w.dv)
+    assert np.max(np.abs(sel - ref)) < 1e-5       # the unfused fp32-score path is near exact
+    nfail, _ = oracle.check_attention(got[:, ::37].reshape(-1, w.dv), ref, TO)
+    assert nfail == 0
