@@ -21,8 +21,10 @@
 //                 16*s + 8*h + e (e < 8) in elements 8*s + e: exactly the B
 //                 operand of a k16 step over those keys.
 //   softmax       online (running max m and sum l per query, base 2 with
-//                 scale*log2(e) folded in): max and sum over a lane's keys in
-//                 registers, one exchange with lane l^32 for the max.
+//                 scale*log2(e) folded into one fma per score): max and sum
+//                 over a lane's keys in registers, one exchange with lane l^32
+//                 for the max; the max is refreshed lazily (O is rescaled
+//                 only when a query's scores outgrow it by 2^8).
 //   O^T += V^T P^T  MFMA A = V fragment (LDS, transposing reads), B = P
 //                 (the probabilities, rounded to bf16).  Result lane l holds
 //                 query l%32: the running rescale by 2^(m_old - m_new) is a
@@ -85,7 +87,10 @@ __device__ __forceinline__ void issue_kv_stage(const AttnArgs& a, const uint16_t
     for (int i = 0; i < OpV::kLoadsPerWave; ++i) lds_dma16(r, voff[i], base + i * 1024);
 }
 
-template <int D, bool OUT_BF16>
+// CPOS: the scale is positive (c > 0; a zero scale arrives as the smallest
+// positive normal float, which leaves every 2^(c*s - m) at 1 to fp32
+// precision); otherwise negative.
+template <int D, bool OUT_BF16, bool CPOS>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
     constexpr int DH = D / 64;                    // 64-deep halves of a key row
     constexpr int DS = D / 16;                    // k16 steps of K Q^T
@@ -139,10 +144,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
     for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
         for (int jq = 0; jq < 2; ++jq) o[vt][jq] = f32x16{};
+    // Running max m (base-2 units) and lane-partial sum l per query tile.
+    // The max is refreshed lazily: while no lane's new scores exceed its m by
+    // more than kLazy, m stays (probabilities then reach at most 2^kLazy) and
+    // O and l need no rescale; when one lane's max grows further, every lane
+    // of the wave moves to its exact running max.
+    constexpr float kLazy = 8.0f;
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
     for (int j = 0; j < a.ktiles; ++j) {
         const char* st = smem + (j & 1) * kStage;
+        const char* sv = st + kKBytes;
 
         // S^T = K Q^T for 2 key tiles x 2 query tiles.
         f32x16 s[2][2];
@@ -163,8 +175,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
                     s[kt][jq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt], qf[jq][ds], s[kt][jq], 0, 0, 0);
         }
 
-        // Keys past Lk (last tile only): score -inf.  Element e of s[kt][.]
-        // is key 32*kt + 16*(e/8) + 8*h + e%8 of the tile.
+        // Keys past Lk (last tile only) get the neutral score of the max,
+        // so their probability comes out as exactly 0.  Element e of
+        // s[kt][.] is key 32*kt + 16*(e/8) + 8*h + e%8 of the tile.
         const int valid = a.Lk - j * kBN;
         if (valid < kBN) {
 #pragma unroll
@@ -173,37 +186,51 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
                 for (int jq = 0; jq < 2; ++jq)
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
-                        if (32 * kt + 16 * (e / 8) + 8 * h + e % 8 >= valid) s[kt][jq][e] = -INFINITY;
+                        if (32 * kt + 16 * (e / 8) + 8 * h + e % 8 >= valid) s[kt][jq][e] = CPOS ? -INFINITY : INFINITY;
         }
 
-        // Online softmax per query tile; P in bf16 as the B operand of V^T P^T.
-        bf16x8 pf[2][4];
+        // Largest scaled score per query (scale > 0: the max of S, scale < 0:
+        // the min), one exchange with lane l^32, which holds the query's
+        // other 32 keys.
+        float mn[2];
+        bool grow = false;
 #pragma unroll
         for (int jq = 0; jq < 2; ++jq) {
-            float mx = -INFINITY;
+            float x = CPOS ? -INFINITY : INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    s[kt][jq][e] *= a.c;
-                    mx = fmaxf(mx, s[kt][jq][e]);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m[jq], mx);
-            const float alpha = __builtin_amdgcn_exp2f(m[jq] - mn);
-            m[jq] = mn;
+                for (int e = 0; e < 16; ++e) x = CPOS ? fmaxf(x, s[kt][jq][e]) : fminf(x, s[kt][jq][e]);
+            float mt = x * a.c;
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mn[jq] = fmaxf(m[jq], mt);
+            grow |= mn[jq] > m[jq] + kLazy;
+        }
+        if (__any(grow)) {
+#pragma unroll
+            for (int jq = 0; jq < 2; ++jq) {
+                const float alpha = __builtin_amdgcn_exp2f(m[jq] - mn[jq]);
+                m[jq] = mn[jq];
+                l[jq] *= alpha;
+#pragma unroll
+                for (int vt = 0; vt < VT; ++vt) o[vt][jq] *= alpha;
+            }
+        }
+
+        // p = 2^(c*s - m), rounded to bf16 as the B operand of V^T P^T.
+        bf16x8 pf[2][4];
+#pragma unroll
+        for (int jq = 0; jq < 2; ++jq) {
             float sum = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(s[kt][jq][e] - mn);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][jq][e], a.c, -m[jq]));
                     s[kt][jq][e] = p;
                     sum += p;
                 }
-            l[jq] = l[jq] * alpha + sum;
-#pragma unroll
-            for (int vt = 0; vt < VT; ++vt) o[vt][jq] *= alpha;
+            l[jq] += sum;
 #pragma unroll
             for (int js = 0; js < 4; ++js)
 #pragma unroll
@@ -211,7 +238,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
         }
 
         // O^T += V^T P^T over the tile's 4 k16 key steps.
-        const char* sv = st + kKBytes;
 #pragma unroll
         for (int js = 0; js < 4; ++js) {
 #pragma unroll
@@ -262,7 +288,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
 
 template <int D, bool OUT_BF16>
 int launch_attn_t(const AttnDesc& d, const AttnArgs& k, hipStream_t s) {
-    attn_fwd_kernel<D, OUT_BF16><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
+    if (k.c > 0.f) attn_fwd_kernel<D, OUT_BF16, true><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
+    else attn_fwd_kernel<D, OUT_BF16, false><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
     return (int)hipGetLastError();
 }
 
@@ -289,7 +316,9 @@ int launch_attn(const AttnDesc& d, const void* Q, const void* K, const void* V, 
     k.qtiles = (int32_t)d.qtiles;
     k.tiles = (int32_t)d.tiles;
     k.ktiles = (int32_t)((d.Lk + kBN - 1) / kBN);
-    k.c = d.c;
+    // A zero scale makes every probability 1: the smallest positive normal
+    // c keeps c*s - m at 0 to fp32 precision and masked keys at -inf.
+    k.c = d.c == 0.f ? 1.17549435e-38f : d.c;
     hipStream_t s = (hipStream_t)stream;
     if (d.d == 128) return d.o_bf16 ? launch_attn_t<128, true>(d, k, s) : launch_attn_t<128, false>(d, k, s);
     return d.o_bf16 ? launch_attn_t<64, true>(d, k, s) : launch_attn_t<64, false>(d, k, s);

@@ -14,7 +14,8 @@ timed on a bounded sample of the same workload.
   python bench.py [--gpus 1] [--steps K] [--warmup W]
       (defaults: warm up for about 0.5 s of launches, then time at least 50
       launches and 0.1 s; the JSON line reports the counts used)
-  python bench.py --workload NAME      other workloads (reported, not the headline)
+  python bench.py --workload NAME      other workloads (reported, not the headline);
+                                       attn32x2048 is the fused attention forward
   python bench.py --tilecast           tile fan-out microbenchmark (JSON lines)
   python bench.py --profile            short run for rocprofv3 (GEMM + a copy kernel of known size)
 """
@@ -34,13 +35,20 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 HEADLINE = "gemm8192"
-KERNEL_SOURCES = [os.path.join(ROOT, "attention_scores_amd", "csrc", f)
-                  for f in ("gemm.hip", "schedule.hpp")]
+KERNEL_SOURCES = {kind: [os.path.join(ROOT, "attention_scores_amd", "csrc", f)
+                          for f in (main, "schedule.hpp", "tile.hpp")]
+                  for kind, main in (("gemm", "gemm.hip"), ("attn", "attn.hip"))}
 
 
-def kernel_source_hash() -> str:
+def kernel_kind(name: str) -> str:
+    from workloads import ATTN_WORKLOADS
+    return "attn" if name in ATTN_WORKLOADS else "gemm"
+
+
+def kernel_source_hash(kind: str = "gemm") -> str:
+    """Hash of the sources of the kernel a workload runs (for stale-summary checks)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kind]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -62,7 +70,7 @@ def read_traffic(name: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel_kind(name)):
         return None
     try:
         return {"read_bytes": float(vals["hbm_read_bytes_per_launch"]),
@@ -87,6 +95,61 @@ def _plan(asl, w, flags=0):
 
 WARMUP_S = 0.5      # default warm-up: launches for about this long, so the clocks settle
 TIMED_S = 0.1       # default timed region: at least this long (and at least 50 launches)
+
+
+def _timed(run, steps, warmup, stream):
+    """(wall ms per step, event ms per launch, steps, warmup) of launches of
+    run(); steps / warmup None: sized from a short calibration (WARMUP_S,
+    TIMED_S).  HIP events are recorded on the launch stream."""
+    import torch
+    if warmup is None or steps is None:
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+        per = max((time.perf_counter() - c0) / 10, 1e-6)
+        if warmup is None:
+            warmup = max(30, min(20000, int(WARMUP_S / per)))
+        if steps is None:
+            steps = max(50, min(20000, int(TIMED_S / per)))
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps, steps, warmup
+
+
+def time_attention(w, steps, warmup):
+    """(wall ms, event ms, steps, warmup) for attention workload w."""
+    import torch
+    import attention_scores_amd as asl
+    from workloads import attn_operands
+    dev = torch.device("cuda:0")
+    Q, K, V = (t.to(dev) for t in attn_operands(w))
+    od = torch.bfloat16 if w.out == "bf16" else torch.float32
+    O = torch.empty((w.batch, w.Lq, w.dv), dtype=od, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sq, sk, sv, so = w.strides()
+    o_t = asl.AS_BF16 if w.out == "bf16" else asl.AS_F32
+    args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), w.batch, w.Lq, w.Lk, w.d, w.dv,
+            sq, sk, sv, so, w.scale, asl.AS_BF16, o_t, stream.cuda_stream)
+
+    def run():
+        asl.attn_fwd_run(*args)
+    out = _timed(run, steps, warmup, stream)
+    del Q, K, V, O
+    return out
 
 
 def time_workload(w, steps, warmup, flags=0):
@@ -120,35 +183,9 @@ def time_workload(w, steps, warmup, flags=0):
 
         def run():
             asl.gemm_run(plan, a, b, c, sh)
-    if warmup is None or steps is None:
-        for _ in range(3):
-            run()
-        torch.cuda.synchronize()
-        c0 = time.perf_counter()
-        for _ in range(10):
-            run()
-        torch.cuda.synchronize()
-        per = max((time.perf_counter() - c0) / 10, 1e-6)
-        if warmup is None:
-            warmup = max(30, min(20000, int(WARMUP_S / per)))
-        if steps is None:
-            steps = max(50, min(20000, int(TIMED_S / per)))
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
-        run()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    wall_ms, ev_ms, steps, warmup = _timed(run, steps, warmup, stream)
     if w.kind != "sscore":
         asl.gemm_destroy(plan)
-    wall_ms = (t1 - t0) * 1e3 / steps
-    ev_ms = ev0.elapsed_time(ev1) / steps
     del A, B, C
     return wall_ms, ev_ms, info, steps, warmup
 
@@ -183,6 +220,34 @@ def cpu_baseline(w, target_s=15.0):
     return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d output rows of the %dx%dx%d product (fp64 oracle incl. the sum|a*b| pass), "
                       "%.1f s" % (total_rows, w.M, w.M, w.N, w.K, secs)}
+
+
+def cpu_baseline_attn(w, target_s=12.0):
+    """The attention oracle, as it stands, on a bounded sample of query rows of w."""
+    import numpy as np
+    import oracle
+    from workloads import attn_operands, bits
+    Q, K, V = (bits(t) for t in attn_operands(w))
+    threads = min(16, os.cpu_count() or 1)
+    sq, sk, sv, _ = w.strides()
+
+    def rows_job(r0, n):
+        rows = np.stack([np.zeros(n, dtype=np.int64), np.arange(r0, r0 + n, dtype=np.int64)], axis=1)
+        t = time.perf_counter()
+        oracle.attention(Q, K, V, w.batch, w.Lq, w.Lk, w.d, w.dv, sq, sk, sv, w.scale, rows=rows,
+                         nthreads=threads)
+        return time.perf_counter() - t
+
+    probe = threads
+    t_probe = rows_job(0, probe)
+    n = max(threads, int(probe * target_s / max(t_probe, 1e-3)) // threads * threads)
+    n = min(n, w.Lq - probe)
+    t_main = rows_job(probe, n)
+    rows, secs = probe + n, t_probe + t_main
+    flop = 2.0 * rows * w.Lk * (w.d + w.dv)
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d query rows of slice 0 (fp64 oracle incl. the sum p|v| pass), %.1f s"
+                      % (rows, w.Lq, secs)}
 
 
 def tilecast_report(iters=5000):
@@ -220,9 +285,11 @@ def tilecast_report(iters=5000):
 def profile_run(steps, name=HEADLINE):
     """Short run for counter collection: one workload, then a copy kernel of known size."""
     import torch
-    from workloads import WORKLOADS
-    w = WORKLOADS[name]
-    time_workload(w, steps, 1)
+    from workloads import ATTN_WORKLOADS, WORKLOADS
+    if name in ATTN_WORKLOADS:
+        time_attention(ATTN_WORKLOADS[name], steps, 1)
+    else:
+        time_workload(WORKLOADS[name], steps, 1)
     n = 1 << 29                                  # 1 GiB of bf16 read, 1 GiB written
     src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
@@ -232,6 +299,41 @@ def profile_run(steps, name=HEADLINE):
     torch.cuda.synchronize()
     print(json.dumps({"profile": "done", "gemm_launches": steps + 1, "copy_bytes_each_way": 2 * n,
                       "copy_launches": steps}))
+
+
+METRIC = "bf16 GEMM TFLOP/s at 8192^3 (MFMA util %); HBM bytes read / compulsory bytes"
+
+
+def attention_line(w, args):
+    """The JSON line for a fused-attention workload (MFMA-bound: 2*b*Lq*Lk*(d+dv) flop)."""
+    wall_ms, ev_ms, steps, warmup = time_attention(w, args.steps, args.warmup)
+    achieved = w.flop / (ev_ms * 1e-3) / 1e12
+    traffic = read_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(w.flop / (wall_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, %s)" % w.dist,
+        "config": {"workload": w.description, "batch": w.batch, "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "dv": w.dv,
+                   "queries_per_workgroup": 256, "keys_per_stage": 64},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": (traffic["read_bytes"] + traffic["write_bytes"]) if traffic else None,
+                     "kernel_ms": round(ev_ms, 4)},
+        "hbm_bytes_per_s_compulsory": round((w.bytes_in + w.bytes_out) / (ev_ms * 1e-3) / 1e9, 1),
+        "hbm_read_over_compulsory": (round(traffic["read_bytes"] / w.bytes_in, 3) if traffic else None),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_attn(w)
+    return out
 
 
 def main():
@@ -269,6 +371,10 @@ def main():
             print(json.dumps(line))
         return
 
+    from workloads import ATTN_WORKLOADS
+    if args.workload in ATTN_WORKLOADS:
+        print(json.dumps(attention_line(ATTN_WORKLOADS[args.workload], args)))
+        return
     w = WORKLOADS[args.workload]
     wall_ms, ev_ms, info, steps, warmup = time_workload(w, args.steps, args.warmup, args.flags)
     flop = w.flop
@@ -285,7 +391,7 @@ def main():
         roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4)})
     out = {
-        "metric": "bf16 GEMM TFLOP/s at 8192^3 (MFMA util %); HBM bytes read / compulsory bytes",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
