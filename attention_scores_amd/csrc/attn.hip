@@ -10,8 +10,8 @@
 // XCD-contiguous ranges as the GEMM schedule), so each K/V tile comes from
 // HBM once per XCD and from its L2 for the other query tiles.
 //
-// Workgroup: 4 waves, 256 queries (64 per wave), key stages of 64 keys
-// double-buffered in LDS by buffer_load ... lds.  Everything is computed
+// Workgroup: 8 waves, 256 queries (32 per wave, two waves per SIMD), key
+// stages of 64 keys double-buffered in LDS by buffer_load ... lds.  Everything is computed
 // transposed, so that a lane owns one query:
 //   S^T = K Q^T   MFMA A = K fragment (LDS, rows = keys), B = Q fragment
 //                 (registers for the whole kernel).  Result lane l holds query
@@ -52,8 +52,13 @@ struct AttnArgs {
 };
 
 constexpr int kBN = 64;               // keys per stage
-constexpr int kQW = 64;               // queries per wave
-constexpr int kBQ = kQW * kWaves;     // queries per workgroup
+constexpr int kBQ = kAttnQueriesPerWorkgroup;   // queries per workgroup (256)
+// 32-query MFMA tiles per wave.  One (8 waves of 32 queries, two waves per
+// SIMD) measured 67.8 us against 77.8 us for two (4 waves of 64 queries,
+// one per SIMD) on 32 slices of 2048 x 2048 x 128: the second wave on a SIMD
+// covers LDS latency and softmax arithmetic, and the smaller register set
+// needs no accumulator copies.
+constexpr int kAttnJQ = 1;
 
 // Row of an MFMA A-operand tile that lane row r reads: bits 2 and 3 exchanged.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -90,13 +95,19 @@ __device__ __forceinline__ void issue_kv_stage(const AttnArgs& a, const uint16_t
 // CPOS: the scale is positive (c > 0; a zero scale arrives as the smallest
 // positive normal float, which leaves every 2^(c*s - m) at 1 to fp32
 // precision); otherwise negative.
-template <int D, bool OUT_BF16, bool CPOS>
-__global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
+//
+// JQ: 32-query MFMA tiles per wave (2: 4 waves of 64 queries; 1: 8 waves of
+// 32 queries, two per SIMD, which hide each other's latencies but read every
+// K and V fragment twice as often per MFMA).
+template <int D, bool OUT_BF16, bool CPOS, int JQ>
+__global__ void __launch_bounds__(64 * kBQ / (32 * JQ), 1) attn_fwd_kernel(AttnArgs a) {
+    constexpr int QW = 32 * JQ;                   // queries per wave
+    constexpr int NW = kBQ / QW;                  // waves per workgroup
     constexpr int DH = D / 64;                    // 64-deep halves of a key row
     constexpr int DS = D / 16;                    // k16 steps of K Q^T
     constexpr int VT = D / 32;                    // 32-wide value-column tiles
-    using OpK = OperandTile<kBN, true, 64>;       // [64 keys][64 d], d contiguous
-    using OpV = OperandTile<D, false, kBN>;       // [64 keys][D], value columns contiguous
+    using OpK = OperandTile<kBN, true, 64, NW>;   // [64 keys][64 d], d contiguous
+    using OpV = OperandTile<D, false, kBN, NW>;   // [64 keys][D], value columns contiguous
     constexpr int kKBytes = DH * OpK::kBytes;
     constexpr int kStage = kKBytes + OpV::kBytes;
     __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
@@ -110,7 +121,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
     tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, true, first, stride, end);
     if (first >= end) return;
     const int bb = first / a.qtiles;
-    const int q0 = (first - bb * a.qtiles) * kBQ + w * kQW;   // this wave's first query
+    const int q0 = (first - bb * a.qtiles) * kBQ + w * QW;    // this wave's first query
 
     // Stage loads: K halves then V, each lane's 16-byte pieces.
     uint32_t koff[OpK::kLoadsPerWave], voff[OpV::kLoadsPerWave];
@@ -122,10 +133,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
     const uint16_t* vb = a.V + bb * a.v_bs;
 
     // Q fragments (B operand of K Q^T): query q0 + 32*jq + col, d 16*s + 8*h ..+7.
-    bf16x8 qf[2][DS];
+    bf16x8 qf[JQ][DS];
     const uint16_t* qb = a.Q + bb * a.q_bs;
 #pragma unroll
-    for (int jq = 0; jq < 2; ++jq) {
+    for (int jq = 0; jq < JQ; ++jq) {
         const int q = q0 + 32 * jq + col;
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
@@ -139,29 +150,34 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // Q and the first stages
     asm volatile("s_barrier" ::: "memory");
 
-    f32x16 o[VT][2];
+    f32x16 o[VT][JQ];
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-        for (int jq = 0; jq < 2; ++jq) o[vt][jq] = f32x16{};
+        for (int jq = 0; jq < JQ; ++jq) o[vt][jq] = f32x16{};
     // Running max m (base-2 units) and lane-partial sum l per query tile.
     // The max is refreshed lazily: while no lane's new scores exceed its m by
     // more than kLazy, m stays (probabilities then reach at most 2^kLazy) and
     // O and l need no rescale; when one lane's max grows further, every lane
     // of the wave moves to its exact running max.
     constexpr float kLazy = 8.0f;
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    float m[JQ], l[JQ];
+#pragma unroll
+    for (int jq = 0; jq < JQ; ++jq) {
+        m[jq] = -INFINITY;
+        l[jq] = 0.f;
+    }
 
     for (int j = 0; j < a.ktiles; ++j) {
         const char* st = smem + (j & 1) * kStage;
         const char* sv = st + kKBytes;
 
         // S^T = K Q^T for 2 key tiles x 2 query tiles.
-        f32x16 s[2][2];
+        f32x16 s[2][JQ];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int jq = 0; jq < 2; ++jq) s[kt][jq] = f32x16{};
+            for (int jq = 0; jq < JQ; ++jq) s[kt][jq] = f32x16{};
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
             bf16x8 kf[2];
@@ -171,7 +187,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int jq = 0; jq < 2; ++jq)
+                for (int jq = 0; jq < JQ; ++jq)
                     s[kt][jq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt], qf[jq][ds], s[kt][jq], 0, 0, 0);
         }
 
@@ -183,7 +199,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int jq = 0; jq < 2; ++jq)
+                for (int jq = 0; jq < JQ; ++jq)
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
                         if (32 * kt + 16 * (e / 8) + 8 * h + e % 8 >= valid) s[kt][jq][e] = CPOS ? -INFINITY : INFINITY;
@@ -192,10 +208,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
         // Largest scaled score per query (scale > 0: the max of S, scale < 0:
         // the min), one exchange with lane l^32, which holds the query's
         // other 32 keys.
-        float mn[2];
+        float mn[JQ];
         bool grow = false;
 #pragma unroll
-        for (int jq = 0; jq < 2; ++jq) {
+        for (int jq = 0; jq < JQ; ++jq) {
             float x = CPOS ? -INFINITY : INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -208,7 +224,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
         }
         if (__any(grow)) {
 #pragma unroll
-            for (int jq = 0; jq < 2; ++jq) {
+            for (int jq = 0; jq < JQ; ++jq) {
                 const float alpha = __builtin_amdgcn_exp2f(m[jq] - mn[jq]);
                 m[jq] = mn[jq];
                 l[jq] *= alpha;
@@ -218,9 +234,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
         }
 
         // p = 2^(c*s - m), rounded to bf16 as the B operand of V^T P^T.
-        bf16x8 pf[2][4];
+        bf16x8 pf[JQ][4];
 #pragma unroll
-        for (int jq = 0; jq < 2; ++jq) {
+        for (int jq = 0; jq < JQ; ++jq) {
             float sum = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -244,7 +260,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
             for (int vt = 0; vt < VT; ++vt) {
                 const bf16x8 vf = OpV::frag(sv, 32 * vt, js, lane);
 #pragma unroll
-                for (int jq = 0; jq < 2; ++jq)
+                for (int jq = 0; jq < JQ; ++jq)
                     o[vt][jq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[jq][js], o[vt][jq], 0, 0, 0);
             }
         }
@@ -259,7 +275,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
     // O = O^T / l: lane holds query q0 + 32*jq + col, value columns
     // 32*vt + 8*g + 4*h + (0..3) in elements 4*g .. 4*g+3.
 #pragma unroll
-    for (int jq = 0; jq < 2; ++jq) {
+    for (int jq = 0; jq < JQ; ++jq) {
         const float lt = l[jq] + __shfl_xor(l[jq], 32);
         const float inv = 1.0f / lt;
         const int q = q0 + 32 * jq + col;
@@ -288,8 +304,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnArgs a) {
 
 template <int D, bool OUT_BF16>
 int launch_attn_t(const AttnDesc& d, const AttnArgs& k, hipStream_t s) {
-    if (k.c > 0.f) attn_fwd_kernel<D, OUT_BF16, true><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
-    else attn_fwd_kernel<D, OUT_BF16, false><<<dim3((unsigned)d.tiles), dim3(kThreads), 0, s>>>(k);
+    constexpr int JQ = kAttnJQ;
+    constexpr unsigned threads = 64 * kBQ / (32 * JQ);
+    if (k.c > 0.f) attn_fwd_kernel<D, OUT_BF16, true, JQ><<<dim3((unsigned)d.tiles), dim3(threads), 0, s>>>(k);
+    else attn_fwd_kernel<D, OUT_BF16, false, JQ><<<dim3((unsigned)d.tiles), dim3(threads), 0, s>>>(k);
     return (int)hipGetLastError();
 }
 

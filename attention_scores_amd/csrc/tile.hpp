@@ -78,12 +78,14 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
     return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
 }
 
-// One operand tile of R (M or N extent) x BK (K) bf16 per pipeline stage.
-template <int R, bool KMAJ, int BK>
+// One operand tile of R (M or N extent) x BK (K) bf16 per pipeline stage,
+// loaded by the NW waves of a workgroup.
+template <int R, bool KMAJ, int BK, int NW = kWaves>
 struct OperandTile {
     static constexpr int kBytes = R * BK * 2;
     static constexpr int kCHR = BK / 8;                              // chunks per row (K-major)
-    static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;   // 1 KiB per wave-wide load
+    static constexpr int kLoadsPerWave = kBytes / 1024 / NW;       // 1 KiB per wave-wide load
+    static_assert(kLoadsPerWave >= 1 && kLoadsPerWave * NW * 1024 == kBytes, "tile must split into whole loads");
     static constexpr int kCH = R / 8;                                // chunks per row (MN-major)
     static constexpr bool kKMaj = KMAJ;
 

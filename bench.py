@@ -232,7 +232,8 @@ def cpu_baseline_attn(w, target_s=12.0):
     sq, sk, sv, _ = w.strides()
 
     def rows_job(r0, n):
-        rows = np.stack([np.zeros(n, dtype=np.int64), np.arange(r0, r0 + n, dtype=np.int64)], axis=1)
+        flat = np.arange(r0, r0 + n, dtype=np.int64)          # (slice, query) rows in order
+        rows = np.stack([flat // w.Lq, flat % w.Lq], axis=1)
         t = time.perf_counter()
         oracle.attention(Q, K, V, w.batch, w.Lq, w.Lk, w.d, w.dv, sq, sk, sv, w.scale, rows=rows,
                          nthreads=threads)
@@ -241,13 +242,13 @@ def cpu_baseline_attn(w, target_s=12.0):
     probe = threads
     t_probe = rows_job(0, probe)
     n = max(threads, int(probe * target_s / max(t_probe, 1e-3)) // threads * threads)
-    n = min(n, w.Lq - probe)
+    n = min(n, w.batch * w.Lq - probe)
     t_main = rows_job(probe, n)
     rows, secs = probe + n, t_probe + t_main
     flop = 2.0 * rows * w.Lk * (w.d + w.dv)
     return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d query rows of slice 0 (fp64 oracle incl. the sum p|v| pass), %.1f s"
-                      % (rows, w.Lq, secs)}
+            "sample": "%d of %d query rows (fp64 oracle incl. the sum p|v| pass), %.1f s"
+                      % (rows, w.batch * w.Lq, secs)}
 
 
 def tilecast_report(iters=5000):
