@@ -78,7 +78,7 @@ def _load():
     lib.oracle_sscore_points.argtypes = [u16p, u16p, ctypes.c_void_p, i64, dp, dp, i64] + [i64] * 6 + [i32]
     lib.oracle_sscore_points.restype = i32
     lib.oracle_attention.argtypes = [u16p, u16p, u16p, ctypes.c_void_p, i64, dp, dp] + [i64] * 5 + [i64] * 9 + \
-        [ctypes.c_double, i32]
+        [ctypes.c_double, i32, i32]
     lib.oracle_attention.restype = i32
     lib.oracle_tilecast_bytes.argtypes = [i64, i64, i64]
     lib.oracle_tilecast_bytes.restype = ctypes.c_double
@@ -212,8 +212,10 @@ def sscore_points(Q: np.ndarray, Kt: np.ndarray, pts: np.ndarray, d: int,
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, batch: int, Lq: int, Lk: int, d: int, dv: int,
               sq: Tuple[int, int, int], sk: Tuple[int, int, int], sv: Tuple[int, int, int], scale: float,
-              rows: Optional[np.ndarray] = None, nthreads: int = 0):
+              rows: Optional[np.ndarray] = None, nthreads: int = 0, causal: bool = False):
     """O = softmax(scale * Q K^T) V per (b, i) row in fp64; returns (O, TO).
+
+    causal: query i sees keys j <= i + (Lk - Lq) only (needs Lk >= Lq).
 
     Q [b,i,d], K [b,j,d], V [b,j,c] addressed by (row, col, batch) element
     strides.  ``rows``: optional [n, 2] array of (b, i) pairs; then O and TO
@@ -239,7 +241,8 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, batch: int, Lq: int, 
     TO = np.empty(shape, dtype=np.float64)
     rc = _load().oracle_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(r) if r is not None else None, n,
                                   _ptr(O), _ptr(TO), batch, Lq, Lk, d, dv, sq[0], sq[1], sq[2],
-                                  sk[0], sk[1], sk[2], sv[0], sv[1], sv[2], float(scale), nthreads)
+                                  sk[0], sk[1], sk[2], sv[0], sv[1], sv[2], float(scale), int(bool(causal)),
+                                  nthreads)
     if rc != 0:
         raise RuntimeError("oracle_attention failed")
     return O, TO

@@ -536,3 +536,68 @@ def test_attention_pins_catch_planted_mistakes():
     assert not np.allclose(Od[0], ref, rtol=0, atol=1e-12)                  # last key dropped
     Oq, _ = _attn(K, Q, V, 0.6)
     assert not ok(Oq)                                                       # softmax over queries
+
+
+def _attn_c(Q, K, V, scale, rows=None):
+    b, Lq, d = Q.shape
+    Lk, dv = V.shape[1], V.shape[2]
+    return oracle.attention(bits(Q), bits(K), bits(V), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
+                            (dv, 1, Lk * dv), scale, rows=rows, causal=True)
+
+
+def _attn_ref_causal(q, k, v, scale):
+    """Masked softmax with scipy: query i sees keys j <= i + (Lk - Lq)."""
+    import scipy.special
+    Lq, Lk = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T)
+    mask = np.arange(Lk)[None, :] > (np.arange(Lq)[:, None] + (Lk - Lq))
+    s[mask] = -np.inf
+    return scipy.special.softmax(s, axis=1) @ v
+
+
+@pytest.mark.parametrize("b,Lq,Lk,d,dv", [(1, 1, 1, 4, 2), (2, 5, 5, 4, 3), (1, 7, 33, 16, 8), (3, 9, 9, 8, 5)])
+def test_causal_attention_matches_masked_library_softmax(b, Lq, Lk, d, dv):
+    Q, K, V = _attn_inputs(b, Lq, Lk, d, dv, 780 + Lk)
+    O, TO = _attn_c(Q, K, V, 0.4)
+    for x in range(b):
+        ref = _attn_ref_causal(Q[x].double().numpy(), K[x].double().numpy(), V[x].double().numpy(), 0.4)
+        assert np.allclose(O[x], ref, rtol=0, atol=1e-12 * (1 + np.abs(ref).max()))
+
+
+def test_causal_attention_first_and_last_rows():
+    # Lq == Lk: query 0 sees key 0 only (O_0 = V_0 exactly); the last query
+    # sees every key (equal to the unmasked row)
+    Q, K, V = _attn_inputs(2, 12, 12, 8, 6, 790)
+    O, _ = _attn_c(Q, K, V, 0.7)
+    Of, _ = _attn(Q, K, V, 0.7)
+    assert np.array_equal(O[:, 0, :], V[:, 0, :].double().numpy())
+    assert np.allclose(O[:, -1, :], Of[:, -1, :], rtol=0, atol=1e-14)
+    # Lk > Lq: the mask aligns to the last key, so query i sees i + Lk - Lq + 1 keys
+    Q2, K2, V2 = _attn_inputs(1, 4, 10, 8, 3, 791)
+    O2, _ = _attn_c(Q2, K2, V2, 0.5)
+    for i in range(4):
+        n = i + 10 - 4 + 1
+        Oi, _ = _attn(Q2[:, i:i + 1], K2[:, :n], V2[:, :n], 0.5)
+        assert np.allclose(O2[0, i], Oi[0, 0], rtol=0, atol=1e-14)
+
+
+def test_causal_attention_ignores_masked_keys_and_catches_off_by_one():
+    # changing keys/values that the mask hides changes nothing; a mask one key
+    # too wide or too narrow (emulated by shifting Lk against Lq) does
+    Q, K, V = _attn_inputs(1, 8, 8, 8, 4, 800)
+    O, _ = _attn_c(Q, K, V, 0.6)
+    K2, V2 = K.clone(), V.clone()
+    K2[:, 5:], V2[:, 5:] = 3.0, -2.0
+    O2, _ = _attn_c(Q, K2, V2, 0.6)
+    assert np.array_equal(O[:, :5], O2[:, :5])
+    assert not np.allclose(O[:, 5:], O2[:, 5:])
+    q, k, v = Q[0].double().numpy(), K[0].double().numpy(), V[0].double().numpy()
+    ref = _attn_ref_causal(q, k, v, 0.6)
+    assert np.allclose(O[0], ref, rtol=0, atol=1e-12)
+    # one key too many: the first 7 queries against the same 8 keys see
+    # j <= i + 1 under the bottom-right alignment
+    Ow, _ = _attn_c(Q[:, :7], K, V, 0.6)
+    assert not np.allclose(Ow[0], ref[:7], rtol=0, atol=1e-12)
+    # one key too few: all 8 queries against the first 7 keys are refused (Lk < Lq)
+    with pytest.raises(RuntimeError):
+        _attn_c(Q, K[:, :7], V[:, :7], 0.6)
