@@ -27,6 +27,7 @@ AS_FLAG_NO_GROUPING = 0x1
 AS_FLAG_TILE_128 = 0x2
 AS_FLAG_TILE_256 = 0x4
 AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
+AS_ATTN_CAUSAL = 0x1
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
             "sscore_run", "attn_fwd_run", "tilecast_run", "as_status_str", "as_last_error")
@@ -81,7 +82,7 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_int, ctypes.c_int, vp]
         L.sscore_run.restype = ctypes.c_int
         L.attn_fwd_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, Strides, Strides, Strides, Strides,
-                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp]
         L.attn_fwd_run.restype = ctypes.c_int
         L.tilecast_run.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
         L.tilecast_run.restype = ctypes.c_int
@@ -144,10 +145,10 @@ def gemm_plan_tile_of(plan: int, slot: int):
 def attn_fwd_run(Q: int, K: int, V: int, O: int, batch: int, Lq: int, Lk: int, d: int, dv: int,
                  q: Tuple[int, int, int], k: Tuple[int, int, int], v: Tuple[int, int, int],
                  o: Tuple[int, int, int], scale: float, qkv_t: int = AS_BF16, o_t: int = AS_BF16,
-                 stream: int = 0) -> None:
+                 flags: int = 0, stream: int = 0) -> None:
     """O = softmax(scale Q K^T) V on device pointers (see attn_fwd_run in attn_scores.h)."""
     _check(lib().attn_fwd_run(Q, K, V, O, batch, Lq, Lk, d, dv, Strides(*q), Strides(*k), Strides(*v),
-                              Strides(*o), float(scale), qkv_t, o_t, stream))
+                              Strides(*o), float(scale), qkv_t, o_t, flags, stream))
 
 
 def sscore_run(Q: int, K: int, S: int, batch: int, Lq: int, Lk: int, dim: int, q: Tuple[int, int, int],
@@ -261,9 +262,10 @@ def sscore(Q, K, out=None, out_dtype=None):
     return out
 
 
-def attention(Q, K, V, scale=None, out=None, out_dtype=None):
+def attention(Q, K, V, scale=None, out=None, out_dtype=None, causal=False):
     """O = softmax(scale Q K^T) V per slice: Q [b,Lq,d], K [b,Lk,d], V [b,Lk,dv]
-    bf16 -> O [b,Lq,dv] (default scale 1/sqrt(d), bf16 output)."""
+    bf16 -> O [b,Lq,dv] (default scale 1/sqrt(d), bf16 output); causal: query
+    i sees keys j <= i + Lk - Lq only."""
     torch = _torch()
     _require_cuda(Q, K, V)
     if Q.dim() != 3 or K.dim() != 3 or V.dim() != 3:
@@ -280,7 +282,7 @@ def attention(Q, K, V, scale=None, out=None, out_dtype=None):
     _require_cuda(out)
     attn_fwd_run(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), b, Lq, Lk, d, dv, _strides3(Q),
                  _strides3(K), _strides3(V), _strides3(out), scale, _dtype_code(Q.dtype), _dtype_code(out.dtype),
-                 _stream_handle(Q))
+                 AS_ATTN_CAUSAL if causal else 0, _stream_handle(Q))
     return out
 
 

@@ -295,13 +295,18 @@ as_status sscore_run(const void* Q, const void* K, void* S,
 
 as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t Lq,
                        int64_t Lk, int64_t d, int64_t dv, as_strides q, as_strides k, as_strides v,
-                       as_strides o, float scale, as_dtype qkv_t, as_dtype o_t, void* hip_stream) {
+                       as_strides o, float scale, as_dtype qkv_t, as_dtype o_t, uint32_t flags,
+                       void* hip_stream) {
     if (batch <= 0 || Lq <= 0 || Lk <= 0 || d <= 0 || dv <= 0)
         return fail(AS_ERR_INVALID, "sizes must be positive (batch=%" PRId64 " Lq=%" PRId64 " Lk=%" PRId64
                     " d=%" PRId64 " dv=%" PRId64 ")", batch, Lq, Lk, d, dv);
     for (as_dtype t : {qkv_t, o_t})
         if (t != AS_BF16 && t != AS_F32) return fail(AS_ERR_INVALID, "unknown dtype %d", (int)t);
     if (!std::isfinite(scale)) return fail(AS_ERR_INVALID, "scale must be finite");
+    if (flags & ~AS_ATTN_CAUSAL) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~AS_ATTN_CAUSAL);
+    const bool causal = (flags & AS_ATTN_CAUSAL) != 0;
+    if (causal && Lk < Lq)
+        return fail(AS_ERR_INVALID, "causal attention needs Lk >= Lq (Lq=%" PRId64 " Lk=%" PRId64 ")", Lq, Lk);
     const int64_t sv[12] = {q.row, q.col, q.batch, k.row, k.col, k.batch, v.row, v.col, v.batch,
                             o.row, o.col, o.batch};
     for (int64_t x : sv)
@@ -331,6 +336,7 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
     ad.v_row = v.row; ad.v_batch = v.batch;
     ad.o_row = o.row; ad.o_batch = o.batch;
     ad.o_bf16 = (o_t == AS_BF16);
+    ad.causal = causal;
     ad.c = (float)((double)scale * 1.4426950408889634);   // log2(e)
     ad.qtiles = (Lq + asl::kAttnQueriesPerWorkgroup - 1) / asl::kAttnQueriesPerWorkgroup;
     if (ad.qtiles > INT32_MAX / batch) return fail(AS_ERR_UNSUPPORTED, "too many query tiles");

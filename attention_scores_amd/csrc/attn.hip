@@ -31,7 +31,10 @@
 //                 per-lane multiply.
 // Ragged shapes: K and V stage resources cover exactly the valid rows, so
 // rows past Lk read as zero; their scores are set to -inf before the max.
-// Query rows past Lq read as zero and are not stored.
+// Query rows past Lq read as zero and are not stored.  Causal mask (query i
+// sees keys j <= i + Lk - Lq): a workgroup visits only the key tiles its
+// last query sees, and tiles crossing a wave's diagonal get the same -inf
+// treatment per key.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,6 +51,7 @@ struct AttnArgs {
     void* O;
     int64_t q_ld, q_bs, k_ld, k_bs, v_ld, v_bs, o_ld, o_bs;
     int32_t Lq, Lk, qtiles, tiles, ktiles;
+    int32_t causal;       // query i sees keys j <= i + (Lk - Lq) only
     float c;   // scale * log2(e)
 };
 
@@ -121,7 +125,17 @@ __global__ void __launch_bounds__(64 * kBQ / (32 * JQ), 1) attn_fwd_kernel(AttnA
     tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, true, first, stride, end);
     if (first >= end) return;
     const int bb = first / a.qtiles;
-    const int q0 = (first - bb * a.qtiles) * kBQ + w * QW;    // this wave's first query
+    const int qt0 = (first - bb * a.qtiles) * kBQ;             // the workgroup's first query
+    const int q0 = qt0 + w * QW;                               // this wave's first query
+    // Key tiles the workgroup visits: all of them, or with the causal mask
+    // those up to the last key its last query sees.
+    const int off = a.Lk - a.Lq;
+    int nkt = a.ktiles;
+    if (a.causal) {
+        const int qlast = (qt0 + kBQ < a.Lq ? qt0 + kBQ : a.Lq) - 1;
+        const int kend = qlast + off + 1;                      // keys 0 .. kend-1
+        nkt = (kend + kBN - 1) / kBN;
+    }
 
     // Stage loads: K halves then V, each lane's 16-byte pieces.
     uint32_t koff[OpK::kLoadsPerWave], voff[OpV::kLoadsPerWave];
@@ -146,7 +160,7 @@ __global__ void __launch_bounds__(64 * kBQ / (32 * JQ), 1) attn_fwd_kernel(AttnA
     }
 
     issue_kv_stage<D, OpK, OpV>(a, kb, vb, 0, smem, w, koff, voff);
-    if (a.ktiles > 1) issue_kv_stage<D, OpK, OpV>(a, kb, vb, 1, smem + kStage, w, koff, voff);
+    if (nkt > 1) issue_kv_stage<D, OpK, OpV>(a, kb, vb, 1, smem + kStage, w, koff, voff);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // Q and the first stages
     asm volatile("s_barrier" ::: "memory");
 
@@ -168,7 +182,7 @@ __global__ void __launch_bounds__(64 * kBQ / (32 * JQ), 1) attn_fwd_kernel(AttnA
         l[jq] = 0.f;
     }
 
-    for (int j = 0; j < a.ktiles; ++j) {
+    for (int j = 0; j < nkt; ++j) {
         const char* st = smem + (j & 1) * kStage;
         const char* sv = st + kKBytes;
 
@@ -194,15 +208,21 @@ __global__ void __launch_bounds__(64 * kBQ / (32 * JQ), 1) attn_fwd_kernel(AttnA
         // Keys past Lk (last tile only) get the neutral score of the max,
         // so their probability comes out as exactly 0.  Element e of
         // s[kt][.] is key 32*kt + 16*(e/8) + 8*h + e%8 of the tile.
+        // With the causal mask, query q sees tile keys k < q + off - j*kBN + 1;
+        // only tiles crossing this wave's diagonal need the per-key test.
         const int valid = a.Lk - j * kBN;
-        if (valid < kBN) {
+        const bool diag = a.causal && j * kBN + kBN - 1 > q0 + off;
+        if (valid < kBN || diag) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int jq = 0; jq < JQ; ++jq) {
+                const int lim_c = a.causal ? q0 + 32 * jq + col + off - j * kBN + 1 : kBN;
+                const int lim = lim_c < valid ? lim_c : valid;     // keys < lim are visible
 #pragma unroll
-                for (int jq = 0; jq < JQ; ++jq)
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
-                        if (32 * kt + 16 * (e / 8) + 8 * h + e % 8 >= valid) s[kt][jq][e] = CPOS ? -INFINITY : INFINITY;
+                        if (32 * kt + 16 * (e / 8) + 8 * h + e % 8 >= lim) s[kt][jq][e] = CPOS ? -INFINITY : INFINITY;
+            }
         }
 
         // Largest scaled score per query (scale > 0: the max of S, scale < 0:
@@ -269,7 +289,7 @@ __global__ void __launch_bounds__(64 * kBQ / (32 * JQ), 1) attn_fwd_kernel(AttnA
         // it with stage j+2.
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         asm volatile("s_barrier" ::: "memory");
-        if (j + 2 < a.ktiles) issue_kv_stage<D, OpK, OpV>(a, kb, vb, j + 2, smem + (j & 1) * kStage, w, koff, voff);
+        if (j + 2 < nkt) issue_kv_stage<D, OpK, OpV>(a, kb, vb, j + 2, smem + (j & 1) * kStage, w, koff, voff);
     }
 
     // O = O^T / l: lane holds query q0 + 32*jq + col, value columns
@@ -334,6 +354,7 @@ int launch_attn(const AttnDesc& d, const void* Q, const void* K, const void* V, 
     k.qtiles = (int32_t)d.qtiles;
     k.tiles = (int32_t)d.tiles;
     k.ktiles = (int32_t)((d.Lk + kBN - 1) / kBN);
+    k.causal = d.causal ? 1 : 0;
     // A zero scale makes every probability 1: the smallest positive normal
     // c keeps c*s - m at 0 to fp32 precision and masked keys at -inf.
     k.c = d.c == 0.f ? 1.17549435e-38f : d.c;

@@ -39,6 +39,7 @@ struct AttnDesc {
     int64_t batch, Lq, Lk, d;
     int64_t q_row, q_batch, k_row, k_batch, v_row, v_batch, o_row, o_batch;
     bool o_bf16;
+    bool causal;                     // query i sees keys j <= i + (Lk - Lq)
     float c;                         // scale * log2(e)
     int64_t qtiles, tiles;           // query tiles per slice, workgroups
 };

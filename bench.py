@@ -143,7 +143,7 @@ def time_attention(w, steps, warmup):
     sq, sk, sv, so = w.strides()
     o_t = asl.AS_BF16 if w.out == "bf16" else asl.AS_F32
     args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), w.batch, w.Lq, w.Lk, w.d, w.dv,
-            sq, sk, sv, so, w.scale, asl.AS_BF16, o_t, stream.cuda_stream)
+            sq, sk, sv, so, w.scale, asl.AS_BF16, o_t, asl.AS_ATTN_CAUSAL if w.causal else 0, stream.cuda_stream)
 
     def run():
         asl.attn_fwd_run(*args)
@@ -231,21 +231,24 @@ def cpu_baseline_attn(w, target_s=12.0):
     threads = min(16, os.cpu_count() or 1)
     sq, sk, sv, _ = w.strides()
 
+    order = np.random.default_rng(7).permutation(w.batch * w.Lq)  # rows of every cost, in any prefix
+
     def rows_job(r0, n):
-        flat = np.arange(r0, r0 + n, dtype=np.int64)          # (slice, query) rows in order
+        flat = order[r0:r0 + n]
         rows = np.stack([flat // w.Lq, flat % w.Lq], axis=1)
         t = time.perf_counter()
         oracle.attention(Q, K, V, w.batch, w.Lq, w.Lk, w.d, w.dv, sq, sk, sv, w.scale, rows=rows,
-                         nthreads=threads)
-        return time.perf_counter() - t
+                         nthreads=threads, causal=w.causal)
+        secs = time.perf_counter() - t
+        keys = (rows[:, 1] + (w.Lk - w.Lq) + 1).sum() if w.causal else n * w.Lk   # keys each row sees
+        return secs, 2.0 * float(keys) * (w.d + w.dv)
 
     probe = threads
-    t_probe = rows_job(0, probe)
+    t_probe, f_probe = rows_job(0, probe)
     n = max(threads, int(probe * target_s / max(t_probe, 1e-3)) // threads * threads)
     n = min(n, w.batch * w.Lq - probe)
-    t_main = rows_job(probe, n)
-    rows, secs = probe + n, t_probe + t_main
-    flop = 2.0 * rows * w.Lk * (w.d + w.dv)
+    t_main, f_main = rows_job(probe, n)
+    rows, secs, flop = probe + n, t_probe + t_main, f_probe + f_main
     return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d query rows (fp64 oracle incl. the sum p|v| pass), %.1f s"
                       % (rows, w.batch * w.Lq, secs)}
@@ -306,7 +309,8 @@ METRIC = "bf16 GEMM TFLOP/s at 8192^3 (MFMA util %); HBM bytes read / compulsory
 
 
 def attention_line(w, args):
-    """The JSON line for a fused-attention workload (MFMA-bound: 2*b*Lq*Lk*(d+dv) flop)."""
+    """The JSON line for a fused-attention workload (MFMA-bound: 2*(d+dv) flop per visible
+    (query, key) pair, b*Lq*Lk of them without the causal mask)."""
     wall_ms, ev_ms, steps, warmup = time_attention(w, args.steps, args.warmup)
     achieved = w.flop / (ev_ms * 1e-3) / 1e12
     traffic = read_traffic(w.name)
@@ -324,7 +328,7 @@ def attention_line(w, args):
         "dtype": "bf16",
         "data": "synthetic (seeded, %s)" % w.dist,
         "config": {"workload": w.description, "batch": w.batch, "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "dv": w.dv,
-                   "queries_per_workgroup": 256, "keys_per_stage": 64},
+                   "causal": w.causal, "queries_per_workgroup": 256, "keys_per_stage": 64},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": (traffic["read_bytes"] + traffic["write_bytes"]) if traffic else None,

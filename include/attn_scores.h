@@ -160,7 +160,11 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
  * Attention forward O[b] = softmax(scale * Q[b] K[b]^T) V[b]: for every
  * query i, O[b,i,:] = sum_j p_j V[b,j,:] / sum_j p_j with
  * p_j = exp(scale * S[b,i,j] - max_j scale * S[b,i,j]) and S the scores of
- * sscore_run.  No mask.  The score product is the inner step of the
+ * sscore_run.  With AS_ATTN_CAUSAL in `flags`, query i sees only keys
+ * j <= i + (Lk - Lq) (the mask aligned to the last key: with Lq == Lk,
+ * keys 0..i; Lk >= Lq required, AS_ERR_INVALID otherwise); lesson 07 names
+ * causal attention as the case whose tiles cost different amounts ("The
+ * second wall: the static schedule's tail").  The score product is the inner step of the
  * FlashAttention-class operators whose neighbouring query tiles consume the
  * same key and value tiles ("Hopper TMA Multicast" deep-dive, Attention/GEMM
  * reuse use-case and the comparison table's "Attention K/V" row); the
@@ -177,10 +181,13 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
  * points (AS_ERR_UNSUPPORTED: other head sizes, dtypes, strides or
  * alignments).  Asynchronous on `hip_stream`.
  */
+#define AS_ATTN_CAUSAL 0x1u   /* attn_fwd_run: query i sees keys j <= i + (Lk - Lq) only */
+
 AS_API as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O,
                               int64_t batch, int64_t Lq, int64_t Lk, int64_t d, int64_t dv,
                               as_strides q, as_strides k, as_strides v, as_strides o,
-                              float scale, as_dtype qkv_t, as_dtype o_t, void* hip_stream);
+                              float scale, as_dtype qkv_t, as_dtype o_t, uint32_t flags,
+                              void* hip_stream);
 
 /*
  * Tile fan-out microbenchmark.  `consumers` workgroups (a multiple of 8, at

@@ -275,17 +275,20 @@ def test_attn_fwd_argument_checks():
     o = (128, 1, 2048 * 128)
     ok = dict(batch=2, Lq=2048, Lk=2048, d=128, dv=128)
 
-    def st(Q=16, K=32, V=48, O=64, q=q, k=q, v=q, o=o, scale=0.1, qkv_t=asl.AS_BF16, o_t=asl.AS_BF16, **kw):
+    def st(Q=16, K=32, V=48, O=64, q=q, k=q, v=q, o=o, scale=0.1, qkv_t=asl.AS_BF16, o_t=asl.AS_BF16, flags=0,
+           **kw):
         a = dict(ok)
         a.update(kw)
         return _status(asl.attn_fwd_run, Q, K, V, O, a["batch"], a["Lq"], a["Lk"], a["d"], a["dv"], q, k, v, o,
-                       scale, qkv_t, o_t)
+                       scale, qkv_t, o_t, flags)
 
     assert st(batch=0) == asl.AS_ERR_INVALID
     assert st(Lk=0) == asl.AS_ERR_INVALID
     assert st(O=0) == asl.AS_ERR_INVALID                                   # null
     assert st(scale=float("inf")) == asl.AS_ERR_INVALID
     assert st(o_t=7) == asl.AS_ERR_INVALID
+    assert st(flags=0x2) == asl.AS_ERR_INVALID                              # unknown flag
+    assert st(flags=asl.AS_ATTN_CAUSAL, Lk=1024) == asl.AS_ERR_INVALID      # causal needs Lk >= Lq
     assert st(q=(-128, 1, 0)) == asl.AS_ERR_INVALID
     assert st(o=(64, 1, 2048 * 64)) == asl.AS_ERR_INVALID                  # O rows overlap
     assert st(o=(128, 1, 1000)) == asl.AS_ERR_INVALID                      # O batches overlap

@@ -37,7 +37,7 @@ def _say(msg):
     print("[case] " + msg, flush=True)
 
 
-def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0):
+def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0, causal=False):
     """Q, K, V: CPU bf16 [b, L, d]; returns the decoded output [b, Lq, dv] and the raw buffer."""
     b, Lq, d = Q.shape
     Lk, dv = V.shape[1], V.shape[2]
@@ -48,17 +48,17 @@ def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0):
     asl.attn_fwd_run(Qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), Ob.data_ptr(), b, Lq, Lk, d, dv,
                      (d, 1, Lq * d), (d, 1, Lk * d), (dv, 1, Lk * dv), (ldo, 1, (Lq + rows_pad) * ldo), scale,
                      asl.AS_BF16, asl.AS_BF16 if out == "bf16" else asl.AS_F32,
-                     torch.cuda.current_stream().cuda_stream)
+                     flags=asl.AS_ATTN_CAUSAL if causal else 0, stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     raw = Ob.float().cpu().numpy().astype(np.float64)
     return raw[:, :Lq, :dv], raw
 
 
-def _ref(Q, K, V, scale, rows=None):
+def _ref(Q, K, V, scale, rows=None, causal=False):
     b, Lq, d = Q.shape
     Lk, dv = V.shape[1], V.shape[2]
     return oracle.attention(bits(Q), bits(K), bits(V), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
-                            (dv, 1, Lk * dv), scale, rows=rows)
+                            (dv, 1, Lk * dv), scale, rows=rows, causal=causal)
 
 
 def _sparse_q(b, Lq, d, seed):
@@ -160,3 +160,50 @@ def test_matches_the_unfused_path_on_the_score_workload():
     assert np.max(np.abs(sel - ref)) < 1e-5       # the unfused fp32-score path is near exact
     nfail, _ = oracle.check_attention(got[:, ::37].reshape(-1, w.dv), ref, TO)
     assert nfail == 0
+
+
+CAUSAL = [  # (batch, Lq, Lk, d)
+    (2, 512, 512, 128),      # diagonal through every wave's tiles
+    (1, 300, 1000, 64),      # Lk > Lq: the mask aligned to the last key
+    (3, 129, 129, 128),      # ragged queries and keys
+    (1, 1, 77, 128),         # one query sees every key
+    (1, 640, 700, 64),
+]
+
+
+@pytest.mark.parametrize("b,Lq,Lk,d", CAUSAL)
+def test_causal_exact_power_of_two_probabilities(b, Lq, Lk, d):
+    _say("attn causal exact b=%d Lq=%d Lk=%d d=%d" % (b, Lq, Lk, d))
+    Q = _sparse_q(b, Lq, d, 940 + Lq)
+    K = draw((b, Lk, d), "int", -1, 1, 941 + Lk)
+    V = draw((b, Lk, d), "int", -4, 4, 942 + d)
+    got, _ = _run(Q, K, V, math.log(2.0), out="f32", causal=True)
+    ref, TO = _ref(Q, K, V, math.log(2.0), causal=True)
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= 2.0 ** -18 * TO), "max err/TO %.3g" % (err / TO).max()
+
+
+@pytest.mark.parametrize("b,Lq,Lk,d", CAUSAL)
+def test_causal_random_data_within_tolerance(b, Lq, Lk, d):
+    _say("attn causal random b=%d Lq=%d Lk=%d d=%d" % (b, Lq, Lk, d))
+    Q = draw((b, Lq, d), "normal", 0, 1, 950 + Lq)
+    K = draw((b, Lk, d), "normal", 0, 1, 951 + Lk)
+    V = draw((b, Lk, d), "normal", 0, 1, 952 + d)
+    got, _ = _run(Q, K, V, d ** -0.5, out="bf16", causal=True)
+    ref, TO = _ref(Q, K, V, d ** -0.5, causal=True)
+    nfail, util = oracle.check_attention(got, ref, TO, out_bf16=True)
+    assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
+
+
+def test_causal_workload_sampled_rows():
+    w = ATTN_WORKLOADS["attn32x2048"]
+    _say("attn causal workload sampled")
+    Q, K, V = attn_operands(w)
+    got, _ = _run(Q, K, V, w.scale, out=w.out, causal=True)
+    rng = np.random.default_rng(960)
+    rows = np.stack([rng.integers(0, w.batch, 96), rng.integers(0, w.Lq, 96)], axis=1)
+    rows = np.concatenate([rows, [[0, 0], [0, 1], [3, 63], [3, 64], [w.batch - 1, w.Lq - 1], [7, 255], [7, 256]]])
+    ref, TO = _ref(Q, K, V, w.scale, rows=rows, causal=True)
+    nfail, util = oracle.check_attention(got[rows[:, 0], rows[:, 1]], ref, TO, out_bf16=True)
+    assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)

@@ -120,11 +120,17 @@ class AttnWorkload:
     scale: float
     out: str                      # "f32" or "bf16"
     description: str
+    causal: bool = False          # query i sees keys j <= i + Lk - Lq only
 
     @property
     def flop(self) -> float:
-        """Q.K^T and P.V: 2*b*Lq*Lk*(d + dv)."""
-        return 2.0 * self.batch * self.Lq * self.Lk * (self.d + self.dv)
+        """Q.K^T and P.V over the visible (query, key) pairs: 2*(d + dv) each."""
+        if self.causal:
+            off = self.Lk - self.Lq
+            pairs = self.Lq * (off + 1) + self.Lq * (self.Lq - 1) / 2.0
+        else:
+            pairs = float(self.Lq) * self.Lk
+        return 2.0 * self.batch * pairs * (self.d + self.dv)
 
     def strides(self):
         """(row, col, batch) element strides of Q, K, V and O."""
@@ -146,6 +152,10 @@ ATTN_WORKLOADS: Dict[str, AttnWorkload] = {
     "attn32x2048": AttnWorkload(
         "attn32x2048", 32, 2048, 2048, 128, 128, "normal", 0.0, 1.0, (201, 202, 203), 128 ** -0.5, "bf16",
         "attention forward O=softmax(Q.K^T/sqrt(128)).V, 32 slices of Q,K,V [2048,128], N(0,1), bf16 O"),
+    "attn32x2048_causal": AttnWorkload(
+        "attn32x2048_causal", 32, 2048, 2048, 128, 128, "normal", 0.0, 1.0, (201, 202, 203), 128 ** -0.5, "bf16",
+        "causal attention forward (query i sees keys 0..i), 32 slices of Q,K,V [2048,128], N(0,1), bf16 O",
+        causal=True),
 }
 
 
