@@ -28,9 +28,12 @@ AS_FLAG_TILE_128 = 0x2
 AS_FLAG_TILE_256 = 0x4
 AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
 AS_ATTN_CAUSAL = 0x1
+AS_ATTN_QUERIES_256 = 0x2
+AS_ATTN_QUERIES_128 = 0x4
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
-            "sscore_run", "attn_fwd_run", "tilecast_run", "as_status_str", "as_last_error")
+            "sscore_run", "attn_fwd_run", "attn_fwd_plan_info", "tilecast_run", "as_status_str",
+            "as_last_error")
 
 
 class Strides(ctypes.Structure):
@@ -84,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, Strides, Strides, Strides, Strides,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp]
         L.attn_fwd_run.restype = ctypes.c_int
+        L.attn_fwd_plan_info.argtypes = [i64, i64, u32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        L.attn_fwd_plan_info.restype = ctypes.c_int
         L.tilecast_run.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
         L.tilecast_run.restype = ctypes.c_int
         L.as_status_str.argtypes = [ctypes.c_int]
@@ -149,6 +154,13 @@ def attn_fwd_run(Q: int, K: int, V: int, O: int, batch: int, Lq: int, Lk: int, d
     """O = softmax(scale Q K^T) V on device pointers (see attn_fwd_run in attn_scores.h)."""
     _check(lib().attn_fwd_run(Q, K, V, O, batch, Lq, Lk, d, dv, Strides(*q), Strides(*k), Strides(*v),
                               Strides(*o), float(scale), qkv_t, o_t, flags, stream))
+
+
+def attn_fwd_plan_info(batch: int, Lq: int, flags: int = 0):
+    """(queries per workgroup, keys per stage, workgroups) attn_fwd_run chooses."""
+    qw, ks, wg = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().attn_fwd_plan_info(batch, Lq, flags, ctypes.byref(qw), ctypes.byref(ks), ctypes.byref(wg)))
+    return qw.value, ks.value, wg.value
 
 
 def sscore_run(Q: int, K: int, S: int, batch: int, Lq: int, Lk: int, dim: int, q: Tuple[int, int, int],

@@ -187,6 +187,22 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     return AS_OK;
 }
 
+// Attention work items: 256 queries, or 128 with each stage's keys split
+// over the two waves of a SIMD (returns 1 or 2).  One workgroup runs per CU,
+// so the grid runs in rounds of kCus items; a 128-query item takes 0.565 of
+// a 256-query one (measured: 78.2 vs 69.1 us for the same 32 x 2048^2 x 128
+// work in twice the items).  The shorter items win where they fill the
+// rounds better, and always with the causal mask, whose items cost
+// different amounts and balance only when each is short.
+int attn_key_split(int64_t batch, int64_t Lq, uint32_t flags) {
+    if (flags & AS_ATTN_QUERIES_256) return 1;
+    if (flags & AS_ATTN_QUERIES_128) return 2;
+    if (flags & AS_ATTN_CAUSAL) return 2;
+    const int64_t n256 = batch * ((Lq + 255) / 256), n128 = batch * ((Lq + 127) / 128);
+    const int64_t r256 = (n256 + kCus - 1) / kCus, r128 = (n128 + kCus - 1) / kCus;
+    return 565 * r128 < 1000 * r256 ? 2 : 1;
+}
+
 bool plan_live(const as_gemm_plan* p) {
     std::lock_guard<std::mutex> lk(g_plans_mu);
     return p && plans().count(p);
@@ -303,7 +319,10 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
     for (as_dtype t : {qkv_t, o_t})
         if (t != AS_BF16 && t != AS_F32) return fail(AS_ERR_INVALID, "unknown dtype %d", (int)t);
     if (!std::isfinite(scale)) return fail(AS_ERR_INVALID, "scale must be finite");
-    if (flags & ~AS_ATTN_CAUSAL) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~AS_ATTN_CAUSAL);
+    constexpr uint32_t kAttnFlags = AS_ATTN_CAUSAL | AS_ATTN_QUERIES_256 | AS_ATTN_QUERIES_128;
+    if (flags & ~kAttnFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kAttnFlags);
+    if ((flags & AS_ATTN_QUERIES_256) && (flags & AS_ATTN_QUERIES_128))
+        return fail(AS_ERR_INVALID, "AS_ATTN_QUERIES_256 and AS_ATTN_QUERIES_128 are exclusive");
     const bool causal = (flags & AS_ATTN_CAUSAL) != 0;
     if (causal && Lk < Lq)
         return fail(AS_ERR_INVALID, "causal attention needs Lk >= Lq (Lq=%" PRId64 " Lk=%" PRId64 ")", Lq, Lk);
@@ -326,8 +345,8 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
         return fail(AS_ERR_UNSUPPORTED, "device pointers must be 16-byte aligned");
     if (Lq > INT32_MAX / 2 || Lk > INT32_MAX / 2) return fail(AS_ERR_UNSUPPORTED, "sequence too long");
-    // 32-bit offsets inside one staged 64-key tile.
-    if (64 * k.row * 2 >= (INT64_C(1) << 31) || 64 * v.row * 2 >= (INT64_C(1) << 31))
+    // 32-bit offsets inside one staged tile of up to 128 keys.
+    if (128 * k.row * 2 >= (INT64_C(1) << 31) || 128 * v.row * 2 >= (INT64_C(1) << 31))
         return fail(AS_ERR_UNSUPPORTED, "K or V row stride too large for 32-bit tile offsets");
     asl::AttnDesc ad{};
     ad.batch = batch; ad.Lq = Lq; ad.Lk = Lk; ad.d = d;
@@ -338,11 +357,28 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
     ad.o_bf16 = (o_t == AS_BF16);
     ad.causal = causal;
     ad.c = (float)((double)scale * 1.4426950408889634);   // log2(e)
-    ad.qtiles = (Lq + asl::kAttnQueriesPerWorkgroup - 1) / asl::kAttnQueriesPerWorkgroup;
+    ad.key_split = attn_key_split(batch, Lq, flags);
+    const int64_t bq = asl::attn_queries_per_workgroup(ad.key_split);
+    ad.qtiles = (Lq + bq - 1) / bq;
     if (ad.qtiles > INT32_MAX / batch) return fail(AS_ERR_UNSUPPORTED, "too many query tiles");
     ad.tiles = batch * ad.qtiles;
     int e = asl::launch_attn(ad, Q, K, V, O, hip_stream);
     if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
+    return ok();
+}
+
+as_status attn_fwd_plan_info(int64_t batch, int64_t Lq, uint32_t flags, int32_t* queries_per_workgroup,
+                             int32_t* keys_per_stage, int64_t* workgroups) {
+    if (batch <= 0 || Lq <= 0) return fail(AS_ERR_INVALID, "sizes must be positive");
+    constexpr uint32_t kAttnFlags = AS_ATTN_CAUSAL | AS_ATTN_QUERIES_256 | AS_ATTN_QUERIES_128;
+    if (flags & ~kAttnFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kAttnFlags);
+    if ((flags & AS_ATTN_QUERIES_256) && (flags & AS_ATTN_QUERIES_128))
+        return fail(AS_ERR_INVALID, "AS_ATTN_QUERIES_256 and AS_ATTN_QUERIES_128 are exclusive");
+    const int ks = attn_key_split(batch, Lq, flags);
+    const int64_t bq = asl::attn_queries_per_workgroup(ks);
+    if (queries_per_workgroup) *queries_per_workgroup = (int32_t)bq;
+    if (keys_per_stage) *keys_per_stage = 64 * ks;
+    if (workgroups) *workgroups = batch * ((Lq + bq - 1) / bq);
     return ok();
 }
 

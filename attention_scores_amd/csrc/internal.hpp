@@ -34,13 +34,16 @@ bool tile_of_slot(const GemmDesc& d, int64_t i, int64_t* b, int64_t* tm, int64_t
 
 // Attention forward O = softmax(scale Q K^T) V, d == dv in {64, 128}.
 // Strides are elements; every operand's last dimension is contiguous.
-constexpr int kAttnQueriesPerWorkgroup = 256;
+// key_split 1: 256 queries per workgroup; 2: 128 queries, the keys of each
+// stage split over the two waves of a SIMD.
+constexpr int attn_queries_per_workgroup(int key_split) { return key_split == 2 ? 128 : 256; }
 struct AttnDesc {
     int64_t batch, Lq, Lk, d;
     int64_t q_row, q_batch, k_row, k_batch, v_row, v_batch, o_row, o_batch;
     bool o_bf16;
     bool causal;                     // query i sees keys j <= i + (Lk - Lq)
     float c;                         // scale * log2(e)
+    int key_split;                   // 1 or 2
     int64_t qtiles, tiles;           // query tiles per slice, workgroups
 };
 

@@ -311,7 +311,9 @@ METRIC = "bf16 GEMM TFLOP/s at 8192^3 (MFMA util %); HBM bytes read / compulsory
 def attention_line(w, args):
     """The JSON line for a fused-attention workload (MFMA-bound: 2*(d+dv) flop per visible
     (query, key) pair, b*Lq*Lk of them without the causal mask)."""
+    import attention_scores_amd as asl
     wall_ms, ev_ms, steps, warmup = time_attention(w, args.steps, args.warmup)
+    qw, kps, wgs = asl.attn_fwd_plan_info(w.batch, w.Lq, asl.AS_ATTN_CAUSAL if w.causal else 0)
     achieved = w.flop / (ev_ms * 1e-3) / 1e12
     traffic = read_traffic(w.name)
     out = {
@@ -328,7 +330,7 @@ def attention_line(w, args):
         "dtype": "bf16",
         "data": "synthetic (seeded, %s)" % w.dist,
         "config": {"workload": w.description, "batch": w.batch, "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "dv": w.dv,
-                   "causal": w.causal, "queries_per_workgroup": 256, "keys_per_stage": 64},
+                   "causal": w.causal, "queries_per_workgroup": qw, "keys_per_stage": kps, "workgroups": wgs},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": (traffic["read_bytes"] + traffic["write_bytes"]) if traffic else None,

@@ -180,14 +180,32 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
  * fp32 sum of the unrounded probabilities.  Errors as for the other entry
  * points (AS_ERR_UNSUPPORTED: other head sizes, dtypes, strides or
  * alignments).  Asynchronous on `hip_stream`.
+ * Work items: one workgroup computes 256 queries of a slice over all the keys
+ * they see, or 128 queries with the keys of each stage split over two waves
+ * and merged at the end.  By default the 128-query items are used with the
+ * causal mask (items then cost different amounts, and shorter ones balance
+ * better; they are launched heaviest first) and when 256-query items would
+ * number fewer than the 256 CUs; AS_ATTN_QUERIES_256 / AS_ATTN_QUERIES_128
+ * force one shape (AS_ERR_INVALID if both).  The shapes sum in different
+ * orders, so their results differ within the rounding bound; each is
+ * deterministic run to run.
  */
 #define AS_ATTN_CAUSAL 0x1u   /* attn_fwd_run: query i sees keys j <= i + (Lk - Lq) only */
+#define AS_ATTN_QUERIES_256 0x2u  /* force work items of 256 queries (each wave sweeps all keys) */
+#define AS_ATTN_QUERIES_128 0x4u  /* force work items of 128 queries (two waves split each key stage) */
 
 AS_API as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O,
                               int64_t batch, int64_t Lq, int64_t Lk, int64_t d, int64_t dv,
                               as_strides q, as_strides k, as_strides v, as_strides o,
                               float scale, as_dtype qkv_t, as_dtype o_t, uint32_t flags,
                               void* hip_stream);
+
+/* The work items attn_fwd_run chooses for `batch` slices of Lq queries under
+ * `flags`: queries per workgroup (256 or 128), keys per LDS stage (64 or
+ * 128) and workgroups launched.  Any output pointer may be NULL.  Host-only,
+ * no HIP call; AS_ERR_INVALID on non-positive sizes or bad flags. */
+AS_API as_status attn_fwd_plan_info(int64_t batch, int64_t Lq, uint32_t flags, int32_t* queries_per_workgroup,
+                                    int32_t* keys_per_stage, int64_t* workgroups);
 
 /*
  * Tile fan-out microbenchmark.  `consumers` workgroups (a multiple of 8, at

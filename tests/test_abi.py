@@ -287,7 +287,9 @@ def test_attn_fwd_argument_checks():
     assert st(O=0) == asl.AS_ERR_INVALID                                   # null
     assert st(scale=float("inf")) == asl.AS_ERR_INVALID
     assert st(o_t=7) == asl.AS_ERR_INVALID
-    assert st(flags=0x2) == asl.AS_ERR_INVALID                              # unknown flag
+    assert st(flags=0x8) == asl.AS_ERR_INVALID                              # unknown flag
+    assert st(flags=asl.AS_ATTN_QUERIES_256 | asl.AS_ATTN_QUERIES_128) == asl.AS_ERR_INVALID   # exclusive
+
     assert st(flags=asl.AS_ATTN_CAUSAL, Lk=1024) == asl.AS_ERR_INVALID      # causal needs Lk >= Lq
     assert st(q=(-128, 1, 0)) == asl.AS_ERR_INVALID
     assert st(o=(64, 1, 2048 * 64)) == asl.AS_ERR_INVALID                  # O rows overlap
@@ -300,3 +302,20 @@ def test_attn_fwd_argument_checks():
     assert st(Q=24) == asl.AS_ERR_UNSUPPORTED                              # misaligned
     assert st(k=(1 << 24, 1, 0)) == asl.AS_ERR_UNSUPPORTED                 # 32-bit tile offsets
     assert "16-byte" not in asl.as_last_error()
+
+
+def test_attention_work_items():
+    # 256-query items fill whole rounds of the 256 CUs; 128-query items when
+    # they fill the rounds better, and always under the causal mask
+    info = asl.attn_fwd_plan_info
+    assert info(32, 2048) == (256, 64, 256)
+    assert info(64, 2048) == (256, 64, 512)
+    assert info(4, 8192) == (128, 128, 256)                    # 128 items of 256 would leave half the CUs idle
+    assert info(48, 2048) == (128, 128, 768)                   # 1.5 rounds of 256-query items
+    assert info(32, 2048, asl.AS_ATTN_CAUSAL) == (128, 128, 512)
+    assert info(32, 2048, asl.AS_ATTN_QUERIES_128) == (128, 128, 512)
+    assert info(4, 8192, asl.AS_ATTN_QUERIES_256) == (256, 64, 128)
+    assert info(3, 129, asl.AS_ATTN_QUERIES_256 | asl.AS_ATTN_CAUSAL) == (256, 64, 3)
+    for bad in ((0, 10, 0), (1, 0, 0), (1, 10, 0x8), (1, 10, 0x6)):
+        with pytest.raises(asl.AsError):
+            info(*bad)

@@ -37,8 +37,12 @@ def _say(msg):
     print("[case] " + msg, flush=True)
 
 
-def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0, causal=False):
-    """Q, K, V: CPU bf16 [b, L, d]; returns the decoded output [b, Lq, dv] and the raw buffer."""
+ITEMS = {None: 0, 256: 0x2, 128: 0x4}   # work-item shape: the library's choice, or forced
+
+
+def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0, causal=False, items=None):
+    """Q, K, V: CPU bf16 [b, L, d]; returns the decoded output [b, Lq, dv] and the raw buffer.
+    items: None (the library's choice), 256 or 128 queries per work item."""
     b, Lq, d = Q.shape
     Lk, dv = V.shape[1], V.shape[2]
     ldo = ldo or dv
@@ -48,7 +52,8 @@ def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0, causal=False):
     asl.attn_fwd_run(Qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), Ob.data_ptr(), b, Lq, Lk, d, dv,
                      (d, 1, Lq * d), (d, 1, Lk * d), (dv, 1, Lk * dv), (ldo, 1, (Lq + rows_pad) * ldo), scale,
                      asl.AS_BF16, asl.AS_BF16 if out == "bf16" else asl.AS_F32,
-                     flags=asl.AS_ATTN_CAUSAL if causal else 0, stream=torch.cuda.current_stream().cuda_stream)
+                     flags=(asl.AS_ATTN_CAUSAL if causal else 0) | ITEMS[items],
+                     stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     raw = Ob.float().cpu().numpy().astype(np.float64)
     return raw[:, :Lq, :dv], raw
@@ -80,13 +85,14 @@ EXACT = [  # (batch, Lq, Lk, d)
 ]
 
 
+@pytest.mark.parametrize("items", [256, 128])
 @pytest.mark.parametrize("b,Lq,Lk,d", EXACT)
-def test_exact_power_of_two_probabilities(b, Lq, Lk, d):
-    _say("attn exact b=%d Lq=%d Lk=%d d=%d" % (b, Lq, Lk, d))
+def test_exact_power_of_two_probabilities(b, Lq, Lk, d, items):
+    _say("attn exact b=%d Lq=%d Lk=%d d=%d items=%d" % (b, Lq, Lk, d, items))
     Q = _sparse_q(b, Lq, d, 900 + Lq)
     K = draw((b, Lk, d), "int", -1, 1, 901 + Lk)
     V = draw((b, Lk, d), "int", -4, 4, 902 + d)
-    got, _ = _run(Q, K, V, math.log(2.0), out="f32")
+    got, _ = _run(Q, K, V, math.log(2.0), out="f32", items=items)
     ref, TO = _ref(Q, K, V, math.log(2.0))
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got))
@@ -103,14 +109,15 @@ RANDOM = [  # (batch, Lq, Lk, d, out)
 ]
 
 
+@pytest.mark.parametrize("items", [256, 128])
 @pytest.mark.parametrize("b,Lq,Lk,d,out", RANDOM)
-def test_random_data_within_tolerance(b, Lq, Lk, d, out):
-    _say("attn random b=%d Lq=%d Lk=%d d=%d out=%s" % (b, Lq, Lk, d, out))
+def test_random_data_within_tolerance(b, Lq, Lk, d, out, items):
+    _say("attn random b=%d Lq=%d Lk=%d d=%d out=%s items=%d" % (b, Lq, Lk, d, out, items))
     Q = draw((b, Lq, d), "normal", 0, 1, 910 + Lq)
     K = draw((b, Lk, d), "normal", 0, 1, 911 + Lk)
     V = draw((b, Lk, d), "normal", 0, 1, 912 + d)
     scale = d ** -0.5
-    got, _ = _run(Q, K, V, scale, out=out)
+    got, _ = _run(Q, K, V, scale, out=out, items=items)
     ref, TO = _ref(Q, K, V, scale)
     nfail, util = oracle.check_attention(got, ref, TO, out_bf16=(out == "bf16"))
     assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
@@ -130,12 +137,13 @@ def test_padded_output_leaves_the_rest_untouched():
     assert np.all(np.isnan(raw[mask]))
 
 
-def test_workload_sampled_rows_and_determinism():
+@pytest.mark.parametrize("items", [None, 128])
+def test_workload_sampled_rows_and_determinism(items):
     w = ATTN_WORKLOADS["attn32x2048"]
-    _say("attn workload %s sampled" % w.name)
+    _say("attn workload %s sampled items=%s" % (w.name, items))
     Q, K, V = attn_operands(w)
-    got, _ = _run(Q, K, V, w.scale, out=w.out)
-    again, _ = _run(Q, K, V, w.scale, out=w.out)
+    got, _ = _run(Q, K, V, w.scale, out=w.out, items=items)
+    again, _ = _run(Q, K, V, w.scale, out=w.out, items=items)
     assert np.array_equal(got, again)
     rng = np.random.default_rng(930)
     rows = np.stack([rng.integers(0, w.batch, 96), rng.integers(0, w.Lq, 96)], axis=1)
@@ -171,39 +179,57 @@ CAUSAL = [  # (batch, Lq, Lk, d)
 ]
 
 
+@pytest.mark.parametrize("items", [256, 128])
 @pytest.mark.parametrize("b,Lq,Lk,d", CAUSAL)
-def test_causal_exact_power_of_two_probabilities(b, Lq, Lk, d):
-    _say("attn causal exact b=%d Lq=%d Lk=%d d=%d" % (b, Lq, Lk, d))
+def test_causal_exact_power_of_two_probabilities(b, Lq, Lk, d, items):
+    _say("attn causal exact b=%d Lq=%d Lk=%d d=%d items=%d" % (b, Lq, Lk, d, items))
     Q = _sparse_q(b, Lq, d, 940 + Lq)
     K = draw((b, Lk, d), "int", -1, 1, 941 + Lk)
     V = draw((b, Lk, d), "int", -4, 4, 942 + d)
-    got, _ = _run(Q, K, V, math.log(2.0), out="f32", causal=True)
+    got, _ = _run(Q, K, V, math.log(2.0), out="f32", causal=True, items=items)
     ref, TO = _ref(Q, K, V, math.log(2.0), causal=True)
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got))
     assert np.all(err <= 2.0 ** -18 * TO), "max err/TO %.3g" % (err / TO).max()
 
 
+@pytest.mark.parametrize("items", [256, 128])
 @pytest.mark.parametrize("b,Lq,Lk,d", CAUSAL)
-def test_causal_random_data_within_tolerance(b, Lq, Lk, d):
-    _say("attn causal random b=%d Lq=%d Lk=%d d=%d" % (b, Lq, Lk, d))
+def test_causal_random_data_within_tolerance(b, Lq, Lk, d, items):
+    _say("attn causal random b=%d Lq=%d Lk=%d d=%d items=%d" % (b, Lq, Lk, d, items))
     Q = draw((b, Lq, d), "normal", 0, 1, 950 + Lq)
     K = draw((b, Lk, d), "normal", 0, 1, 951 + Lk)
     V = draw((b, Lk, d), "normal", 0, 1, 952 + d)
-    got, _ = _run(Q, K, V, d ** -0.5, out="bf16", causal=True)
+    got, _ = _run(Q, K, V, d ** -0.5, out="bf16", causal=True, items=items)
     ref, TO = _ref(Q, K, V, d ** -0.5, causal=True)
     nfail, util = oracle.check_attention(got, ref, TO, out_bf16=True)
     assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
 
 
-def test_causal_workload_sampled_rows():
+@pytest.mark.parametrize("items", [None, 256])
+def test_causal_workload_sampled_rows(items):
     w = ATTN_WORKLOADS["attn32x2048"]
-    _say("attn causal workload sampled")
+    _say("attn causal workload sampled items=%s" % items)
     Q, K, V = attn_operands(w)
-    got, _ = _run(Q, K, V, w.scale, out=w.out, causal=True)
+    got, _ = _run(Q, K, V, w.scale, out=w.out, causal=True, items=items)
     rng = np.random.default_rng(960)
     rows = np.stack([rng.integers(0, w.batch, 96), rng.integers(0, w.Lq, 96)], axis=1)
     rows = np.concatenate([rows, [[0, 0], [0, 1], [3, 63], [3, 64], [w.batch - 1, w.Lq - 1], [7, 255], [7, 256]]])
     ref, TO = _ref(Q, K, V, w.scale, rows=rows, causal=True)
     nfail, util = oracle.check_attention(got[rows[:, 0], rows[:, 1]], ref, TO, out_bf16=True)
     assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
+
+
+def test_item_shapes_agree_and_each_is_deterministic():
+    # the two work-item shapes sum in different orders: equal within the
+    # bound, each bitwise repeatable
+    b, Lq, Lk, d = 2, 700, 900, 128
+    Q = draw((b, Lq, d), "normal", 0, 1, 970)
+    K = draw((b, Lk, d), "normal", 0, 1, 971)
+    V = draw((b, Lk, d), "normal", 0, 1, 972)
+    ref, TO = _ref(Q, K, V, 0.09)
+    for items in (256, 128):
+        got, _ = _run(Q, K, V, 0.09, out="f32", items=items)
+        again, _ = _run(Q, K, V, 0.09, out="f32", items=items)
+        assert np.array_equal(got, again)
+        assert oracle.check_attention(got, ref, TO)[0] == 0
