@@ -30,6 +30,8 @@ AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
 AS_ATTN_CAUSAL = 0x1
 AS_ATTN_QUERIES_256 = 0x2
 AS_ATTN_QUERIES_128 = 0x4
+AS_ATTN_SCHED_STATIC = 0x8
+AS_ATTN_SCHED_QUEUE = 0x10
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
             "sscore_run", "attn_fwd_run", "attn_fwd_plan_info", "tilecast_run", "as_status_str",

@@ -187,6 +187,26 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     return AS_OK;
 }
 
+as_status check_attn_flags(uint32_t flags) {
+    constexpr uint32_t kAttnFlags = AS_ATTN_CAUSAL | AS_ATTN_QUERIES_256 | AS_ATTN_QUERIES_128 |
+                                    AS_ATTN_SCHED_STATIC | AS_ATTN_SCHED_QUEUE;
+    if (flags & ~kAttnFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kAttnFlags);
+    if ((flags & AS_ATTN_QUERIES_256) && (flags & AS_ATTN_QUERIES_128))
+        return fail(AS_ERR_INVALID, "AS_ATTN_QUERIES_256 and AS_ATTN_QUERIES_128 are exclusive");
+    if ((flags & AS_ATTN_SCHED_STATIC) && (flags & AS_ATTN_SCHED_QUEUE))
+        return fail(AS_ERR_INVALID, "AS_ATTN_SCHED_STATIC and AS_ATTN_SCHED_QUEUE are exclusive");
+    return AS_OK;
+}
+
+// Attention schedule: one workgroup per item (the dispatcher starts them in
+// id order as CUs free up), or a persistent grid of one workgroup per CU
+// that walks items by a static stride or claims them from a queue.
+int attn_sched(uint32_t flags) {
+    if (flags & AS_ATTN_SCHED_STATIC) return 1;
+    if (flags & AS_ATTN_SCHED_QUEUE) return 2;
+    return 0;
+}
+
 // Attention work items: 256 queries, or 128 with each stage's keys split
 // over the two waves of a SIMD (returns 1 or 2).  One workgroup runs per CU,
 // so the grid runs in rounds of kCus items; a 128-query item takes 0.565 of
@@ -319,10 +339,7 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
     for (as_dtype t : {qkv_t, o_t})
         if (t != AS_BF16 && t != AS_F32) return fail(AS_ERR_INVALID, "unknown dtype %d", (int)t);
     if (!std::isfinite(scale)) return fail(AS_ERR_INVALID, "scale must be finite");
-    constexpr uint32_t kAttnFlags = AS_ATTN_CAUSAL | AS_ATTN_QUERIES_256 | AS_ATTN_QUERIES_128;
-    if (flags & ~kAttnFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kAttnFlags);
-    if ((flags & AS_ATTN_QUERIES_256) && (flags & AS_ATTN_QUERIES_128))
-        return fail(AS_ERR_INVALID, "AS_ATTN_QUERIES_256 and AS_ATTN_QUERIES_128 are exclusive");
+    if (as_status st = check_attn_flags(flags); st != AS_OK) return st;
     const bool causal = (flags & AS_ATTN_CAUSAL) != 0;
     if (causal && Lk < Lq)
         return fail(AS_ERR_INVALID, "causal attention needs Lk >= Lq (Lq=%" PRId64 " Lk=%" PRId64 ")", Lq, Lk);
@@ -362,6 +379,8 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
     ad.qtiles = (Lq + bq - 1) / bq;
     if (ad.qtiles > INT32_MAX / batch) return fail(AS_ERR_UNSUPPORTED, "too many query tiles");
     ad.tiles = batch * ad.qtiles;
+    ad.sched = attn_sched(flags);
+    ad.grid = ad.sched == 0 ? ad.tiles : std::min<int64_t>(ad.tiles, kCus);
     int e = asl::launch_attn(ad, Q, K, V, O, hip_stream);
     if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
     return ok();
@@ -370,15 +389,13 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
 as_status attn_fwd_plan_info(int64_t batch, int64_t Lq, uint32_t flags, int32_t* queries_per_workgroup,
                              int32_t* keys_per_stage, int64_t* workgroups) {
     if (batch <= 0 || Lq <= 0) return fail(AS_ERR_INVALID, "sizes must be positive");
-    constexpr uint32_t kAttnFlags = AS_ATTN_CAUSAL | AS_ATTN_QUERIES_256 | AS_ATTN_QUERIES_128;
-    if (flags & ~kAttnFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kAttnFlags);
-    if ((flags & AS_ATTN_QUERIES_256) && (flags & AS_ATTN_QUERIES_128))
-        return fail(AS_ERR_INVALID, "AS_ATTN_QUERIES_256 and AS_ATTN_QUERIES_128 are exclusive");
+    if (as_status st = check_attn_flags(flags); st != AS_OK) return st;
     const int ks = attn_key_split(batch, Lq, flags);
     const int64_t bq = asl::attn_queries_per_workgroup(ks);
+    const int64_t items = batch * ((Lq + bq - 1) / bq);
     if (queries_per_workgroup) *queries_per_workgroup = (int32_t)bq;
     if (keys_per_stage) *keys_per_stage = 64 * ks;
-    if (workgroups) *workgroups = batch * ((Lq + bq - 1) / bq);
+    if (workgroups) *workgroups = attn_sched(flags) == 0 ? items : std::min<int64_t>(items, kCus);
     return ok();
 }
 

@@ -49,6 +49,7 @@
 // longest-first greedy assignment.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "internal.hpp"
@@ -64,9 +65,18 @@ struct AttnArgs {
     int64_t q_ld, q_bs, k_ld, k_bs, v_ld, v_bs, o_ld, o_bs;
     int32_t batch, Lq, Lk, qtiles, tiles;
     int32_t causal;       // query i sees keys j <= i + (Lk - Lq) only
-    int32_t heavy_first;  // workgroup g takes query tile qtiles-1 - g/batch of slice g%batch
+    int32_t heavy_first;  // items in heaviest-first order (below)
+    int32_t sched;        // 0: one workgroup per item; 1: persistent, static stride; 2: persistent, queue
+    int32_t qslot;        // queue counters used by this launch (sched 2)
     float c;   // scale * log2(e)
 };
+
+// Work-queue counters for the persistent schedule: per launch slot and
+// queue (XCD), a claim counter and a done counter, each in its own 128-byte
+// line.  Zero at load; the last workgroup of a queue to finish sets both back
+// to zero, so a launch leaves its slot as it found it.
+constexpr int kQueueSlots = 64;
+__device__ __attribute__((aligned(128))) uint32_t g_attn_queue[kQueueSlots][kXcds][2][32];
 
 constexpr int kBN = 64;               // keys per wave per stage
 constexpr int kNW = 8;                // waves per workgroup
@@ -112,7 +122,10 @@ __device__ __forceinline__ void issue_kv_stage(const AttnArgs& a, const uint16_t
 // CPOS: the scale is positive (c > 0; a zero scale arrives as the smallest
 // positive normal float, which leaves every 2^(c*s - m) at 1 to fp32
 // precision); otherwise negative.  KS: key groups per workgroup (above).
-template <int D, bool OUT_BF16, bool CPOS, int KS>
+// PERSIST: the grid is persistent and each workgroup walks several items
+// (compiled separately, so that one workgroup per item keeps the simpler
+// straight-line code and its lower scalar-register pressure).
+template <int D, bool OUT_BF16, bool CPOS, int KS, bool PERSIST>
 __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
     constexpr int QB = kNW / KS;                  // 32-query blocks per workgroup
     constexpr int BQ = 32 * QB;                   // queries per workgroup
@@ -129,26 +142,54 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
     constexpr int kMergeO = (VT / 2) * 4 * 64 * 16;
     constexpr int kML = KS == 2 ? kNW * 2 * 32 * 4 : 0;
     static_assert(KS == 1 || kNW * kMergeO <= 2 * kStage, "merge buffer must fit in the ring");
-    __shared__ __attribute__((aligned(1024))) char smem[2 * kStage + kML];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * kStage + kML + 16];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, col = lane & 31;
     const int qb = w % QB, kg = w / QB;           // query block, key group (waves w, w+4 share a SIMD)
 
-    // (slice, query tile) of this workgroup.
-    int bb, u;
+    // Stage loads: K halves then V, each lane's 16-byte pieces.
+    uint32_t koff[OpK::kLoadsPerWave], voff[OpV::kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < OpK::kLoadsPerWave; ++i) koff[i] = OpK::src_offset(w, i, lane, a.k_ld);
+#pragma unroll
+    for (int i = 0; i < OpV::kLoadsPerWave; ++i) voff[i] = OpV::src_offset(w, i, lane, a.v_ld);
+
+    // Work items.  Queue x = blockIdx mod 8 (the workgroup's XCD) lists its
+    // items in order k = 0, 1, ...: with heavy_first the items g = x + 8k of
+    // the heaviest-first list (item g is query tile qtiles-1 - g/batch of
+    // slice g mod batch), otherwise the XCD's contiguous range of the
+    // (slice, query tile) list, so a slice's K and V stay in one L2.  The
+    // nx workgroups of a queue start at k = their index on it; with one
+    // workgroup per item that is their only item.  A persistent workgroup
+    // then moves on by the static formula k += nx, or (sched 2) asks the
+    // queue for its next k two key stages before the current item ends: late
+    // enough that the workgroups which run dry first ask first (so the
+    // heaviest remaining items go to the earliest free CUs), early enough
+    // that the answer arrives while the last stages compute (lesson 07,
+    // "The work-stealing loop -- ask first, then compute").
+    const int x = blockIdx.x % kXcds, sidx = blockIdx.x / kXcds;
+    const int nx = (int)gridDim.x / kXcds + (x < (int)gridDim.x % kXcds ? 1 : 0);
+    int qstart = 0, cnt;
+    if (a.heavy_first) cnt = x < a.tiles ? (a.tiles - x + kXcds - 1) / kXcds : 0;
+    else xcd_range<int>(x, a.tiles, qstart, cnt);
+    uint32_t* const claim_ctr = &g_attn_queue[a.qslot][x][0][0];
+    uint32_t* const done_ctr = &g_attn_queue[a.qslot][x][1][0];
+    __attribute__((address_space(3))) int* const next_k =
+        (__attribute__((address_space(3))) int*)(smem + 2 * kStage + kML);
+
+    for (int k = sidx; k < cnt;) {
+    uint32_t claim = 0;
+    int bb, u;                                     // slice, query tile
     if (a.heavy_first) {
-        const int g = blockIdx.x;
+        const int g = x + kXcds * k;
         bb = g % a.batch;
         u = a.qtiles - 1 - g / a.batch;
     } else {
-        // An XCD runs a contiguous range of (slice, query tile) items.
-        int first, stride, end;
-        tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, true, first, stride, end);
-        if (first >= end) return;
-        bb = first / a.qtiles;
-        u = first - bb * a.qtiles;
+        const int L = qstart + k;
+        bb = L / a.qtiles;
+        u = L - bb * a.qtiles;
     }
     const int qt0 = u * BQ;                        // the workgroup's first query
     const int q0 = qt0 + 32 * qb;                  // this wave's first query
@@ -159,12 +200,6 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
     if (a.causal) kend = (qt0 + BQ < a.Lq ? qt0 + BQ : a.Lq) + off;   // keys 0 .. kend-1
     const int nst = (kend + BN - 1) / BN;
 
-    // Stage loads: K halves then V, each lane's 16-byte pieces.
-    uint32_t koff[OpK::kLoadsPerWave], voff[OpV::kLoadsPerWave];
-#pragma unroll
-    for (int i = 0; i < OpK::kLoadsPerWave; ++i) koff[i] = OpK::src_offset(w, i, lane, a.k_ld);
-#pragma unroll
-    for (int i = 0; i < OpV::kLoadsPerWave; ++i) voff[i] = OpV::src_offset(w, i, lane, a.v_ld);
     const uint16_t* kb = a.K + bb * a.k_bs;
     const uint16_t* vb = a.V + bb * a.v_bs;
 
@@ -204,9 +239,12 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
     // tiles can hold a visible key (queries past Lq are never stored).
     const int qlast = (q0 + 31 < a.Lq ? q0 + 31 : a.Lq - 1);
 
+    const int claim_at = nst > 2 ? nst - 2 : 0;
     for (int j = 0; j < nst; ++j) {
         const char* st = smem + (j & 1) * kStage;
         const char* sv = st + kKBytes;
+        if (PERSIST && a.sched == 2 && j == claim_at && w == 0 && lane == 0)
+            claim = __hip_atomic_fetch_add(claim_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         const int kb0 = j * BN + kBN * kg;         // first key of this wave's 64
         const bool act = kb0 < a.Lk && (!a.causal || kb0 <= qlast + off);
 
@@ -352,26 +390,46 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
     // O = O^T / l for the lane's query.
     const float inv = 1.0f / lt;
     const int q = q0 + col;
-    if (q >= a.Lq) return;
-    char* orow = (char*)a.O + ((int64_t)bb * a.o_bs + (int64_t)q * a.o_ld) * (OUT_BF16 ? 2 : 4);
+    if (q < a.Lq) {
+        char* orow = (char*)a.O + ((int64_t)bb * a.o_bs + (int64_t)q * a.o_ld) * (OUT_BF16 ? 2 : 4);
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-        if (vt < vt0 || vt >= vt1) continue;
+        for (int vt = 0; vt < VT; ++vt) {
+            if (vt < vt0 || vt >= vt1) continue;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int c0 = 32 * vt + 8 * g + 4 * h;
-            f32x4 x;
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = 32 * vt + 8 * g + 4 * h;
+                f32x4 y;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = o[vt][4 * g + i] * inv;
-            if constexpr (OUT_BF16) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                bf16x4 y;
+                for (int i = 0; i < 4; ++i) y[i] = o[vt][4 * g + i] * inv;
+                if constexpr (OUT_BF16) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    bf16x4 z;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = (__bf16)x[i];
-                *(bf16x4*)(orow + c0 * 2) = y;
-            } else {
-                *(f32x4*)(orow + c0 * 4) = x;
+                    for (int i = 0; i < 4; ++i) z[i] = (__bf16)y[i];
+                    *(bf16x4*)(orow + c0 * 2) = z;
+                } else {
+                    *(f32x4*)(orow + c0 * 4) = y;
+                }
             }
+        }
+    }
+
+    if constexpr (!PERSIST) break;
+    // Next item.  The barrier also keeps the next item's stage loads out of
+    // the ring until every wave has finished reading the merge data.
+    if (a.sched == 2 && w == 0 && lane == 0) *next_k = nx + (int)claim;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    asm volatile("s_barrier" ::: "memory");
+    k = a.sched == 2 ? __builtin_amdgcn_readfirstlane(*next_k) : k + nx;
+    }
+
+    // Queue bookkeeping: every workgroup reports once after its last
+    // (failed) claim; the last one of the queue resets both counters.
+    if (PERSIST && a.sched == 2 && w == 0 && lane == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (done == (uint32_t)nx - 1) {
+            __hip_atomic_store(claim_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(done_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
 }
@@ -379,8 +437,14 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
 template <int D, bool OUT_BF16, int KS>
 int launch_attn_t(const AttnDesc& d, const AttnArgs& k, hipStream_t s) {
     constexpr unsigned threads = 64 * kNW;
-    if (k.c > 0.f) attn_fwd_kernel<D, OUT_BF16, true, KS><<<dim3((unsigned)d.tiles), dim3(threads), 0, s>>>(k);
-    else attn_fwd_kernel<D, OUT_BF16, false, KS><<<dim3((unsigned)d.tiles), dim3(threads), 0, s>>>(k);
+    const dim3 grid((unsigned)(k.sched == 0 ? d.tiles : d.grid)), block(threads);
+    if (k.sched == 0) {
+        if (k.c > 0.f) attn_fwd_kernel<D, OUT_BF16, true, KS, false><<<grid, block, 0, s>>>(k);
+        else attn_fwd_kernel<D, OUT_BF16, false, KS, false><<<grid, block, 0, s>>>(k);
+    } else {
+        if (k.c > 0.f) attn_fwd_kernel<D, OUT_BF16, true, KS, true><<<grid, block, 0, s>>>(k);
+        else attn_fwd_kernel<D, OUT_BF16, false, KS, true><<<grid, block, 0, s>>>(k);
+    }
     return (int)hipGetLastError();
 }
 
@@ -414,6 +478,9 @@ int launch_attn(const AttnDesc& d, const void* Q, const void* K, const void* V, 
     k.tiles = (int32_t)d.tiles;
     k.causal = d.causal ? 1 : 0;
     k.heavy_first = d.causal ? 1 : 0;
+    k.sched = d.sched;
+    static std::atomic<uint32_t> launches{0};
+    k.qslot = (int32_t)(launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
     // A zero scale makes every probability 1: the smallest positive normal
     // c keeps c*s - m at 0 to fp32 precision and masked keys at -inf.
     k.c = d.c == 0.f ? 1.17549435e-38f : d.c;

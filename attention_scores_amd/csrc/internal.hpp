@@ -44,7 +44,9 @@ struct AttnDesc {
     bool causal;                     // query i sees keys j <= i + (Lk - Lq)
     float c;                         // scale * log2(e)
     int key_split;                   // 1 or 2
-    int64_t qtiles, tiles;           // query tiles per slice, workgroups
+    int sched;                       // 0: one workgroup per item; 1: persistent, static; 2: persistent, queue
+    int64_t qtiles, tiles;           // query tiles per slice, work items (batch * qtiles)
+    int64_t grid;                    // workgroups launched
 };
 
 int launch_attn(const AttnDesc& d, const void* Q, const void* K, const void* V, void* O, void* stream);

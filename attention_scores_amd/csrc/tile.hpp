@@ -154,8 +154,16 @@ struct OperandTile {
 // voff land at LDS address m0 + 16*l.  Issued as inline assembly so that the
 // compiler does not insert its own (conservative) vmcnt waits before later
 // LDS reads; the kernel orders these loads explicitly (s_waitcnt vmcnt + s_barrier).
+// The compiler's hazard checks do not look inside inline assembly, and it
+// may build the resource with v_readfirstlane (or reload spilled SGPRs with
+// v_readlane) right before the load: an SGPR written by a VALU instruction
+// needs 5 wait states before a VMEM instruction reads it (and M0 one before
+// an LDS-DMA load), or the load may use the old value -- a wrong range
+// check or LDS address.  The s_nop 4 in front supplies them whatever the
+// compiler schedules there.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+                 : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {

@@ -189,10 +189,23 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
  * force one shape (AS_ERR_INVALID if both).  The shapes sum in different
  * orders, so their results differ within the rounding bound; each is
  * deterministic run to run.
+ * Schedule: by default one workgroup per item, which the dispatcher starts
+ * in id order as CUs free up (with the causal mask the ids run heaviest
+ * item first).  AS_ATTN_SCHED_STATIC / AS_ATTN_SCHED_QUEUE launch instead a
+ * persistent grid of one workgroup per CU that walks the items by a static
+ * stride, or claims each next item from a per-XCD queue two key stages
+ * before its current item ends (lesson 07 "Clusters, distributed shared
+ * memory & cluster launch control": "The second wall: the static
+ * schedule's tail" and "The work-stealing loop").  Every schedule gives
+ * bitwise the same O.  The queue counters live in the library (64 slots per
+ * device, taken in turn by successive launches; each launch leaves its slot
+ * at zero): at most 64 queue launches may run at once on one device.
  */
 #define AS_ATTN_CAUSAL 0x1u   /* attn_fwd_run: query i sees keys j <= i + (Lk - Lq) only */
 #define AS_ATTN_QUERIES_256 0x2u  /* force work items of 256 queries (each wave sweeps all keys) */
 #define AS_ATTN_QUERIES_128 0x4u  /* force work items of 128 queries (two waves split each key stage) */
+#define AS_ATTN_SCHED_STATIC 0x8u /* persistent grid (one workgroup per CU), items by a static stride */
+#define AS_ATTN_SCHED_QUEUE 0x10u /* persistent grid, items claimed from a per-XCD work queue */
 
 AS_API as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O,
                               int64_t batch, int64_t Lq, int64_t Lk, int64_t d, int64_t dv,

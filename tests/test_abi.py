@@ -287,7 +287,8 @@ def test_attn_fwd_argument_checks():
     assert st(O=0) == asl.AS_ERR_INVALID                                   # null
     assert st(scale=float("inf")) == asl.AS_ERR_INVALID
     assert st(o_t=7) == asl.AS_ERR_INVALID
-    assert st(flags=0x8) == asl.AS_ERR_INVALID                              # unknown flag
+    assert st(flags=0x20) == asl.AS_ERR_INVALID                             # unknown flag
+    assert st(flags=asl.AS_ATTN_SCHED_STATIC | asl.AS_ATTN_SCHED_QUEUE) == asl.AS_ERR_INVALID  # exclusive
     assert st(flags=asl.AS_ATTN_QUERIES_256 | asl.AS_ATTN_QUERIES_128) == asl.AS_ERR_INVALID   # exclusive
 
     assert st(flags=asl.AS_ATTN_CAUSAL, Lk=1024) == asl.AS_ERR_INVALID      # causal needs Lk >= Lq
@@ -316,6 +317,8 @@ def test_attention_work_items():
     assert info(32, 2048, asl.AS_ATTN_QUERIES_128) == (128, 128, 512)
     assert info(4, 8192, asl.AS_ATTN_QUERIES_256) == (256, 64, 128)
     assert info(3, 129, asl.AS_ATTN_QUERIES_256 | asl.AS_ATTN_CAUSAL) == (256, 64, 3)
-    for bad in ((0, 10, 0), (1, 0, 0), (1, 10, 0x8), (1, 10, 0x6)):
+    assert info(32, 2048, asl.AS_ATTN_CAUSAL | asl.AS_ATTN_SCHED_QUEUE) == (128, 128, 256)   # persistent
+    assert info(3, 129, asl.AS_ATTN_SCHED_STATIC) == (128, 128, 6)
+    for bad in ((0, 10, 0), (1, 0, 0), (1, 10, 0x20), (1, 10, 0x6), (1, 10, 0x18)):
         with pytest.raises(asl.AsError):
             info(*bad)

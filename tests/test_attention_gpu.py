@@ -40,9 +40,13 @@ def _say(msg):
 ITEMS = {None: 0, 256: 0x2, 128: 0x4}   # work-item shape: the library's choice, or forced
 
 
-def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0, causal=False, items=None):
+SCHED = {"one": 0, "static": 0x8, "queue": 0x10}   # one workgroup per item, or persistent
+
+
+def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0, causal=False, items=None, sched="one"):
     """Q, K, V: CPU bf16 [b, L, d]; returns the decoded output [b, Lq, dv] and the raw buffer.
-    items: None (the library's choice), 256 or 128 queries per work item."""
+    items: None (the library's choice), 256 or 128 queries per work item; sched: one
+    workgroup per item, or a persistent grid walking items by a static stride or a queue."""
     b, Lq, d = Q.shape
     Lk, dv = V.shape[1], V.shape[2]
     ldo = ldo or dv
@@ -52,7 +56,7 @@ def _run(Q, K, V, scale, out="bf16", ldo=None, rows_pad=0, causal=False, items=N
     asl.attn_fwd_run(Qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), Ob.data_ptr(), b, Lq, Lk, d, dv,
                      (d, 1, Lq * d), (d, 1, Lk * d), (dv, 1, Lk * dv), (ldo, 1, (Lq + rows_pad) * ldo), scale,
                      asl.AS_BF16, asl.AS_BF16 if out == "bf16" else asl.AS_F32,
-                     flags=(asl.AS_ATTN_CAUSAL if causal else 0) | ITEMS[items],
+                     flags=(asl.AS_ATTN_CAUSAL if causal else 0) | ITEMS[items] | SCHED[sched],
                      stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     raw = Ob.float().cpu().numpy().astype(np.float64)
@@ -233,3 +237,56 @@ def test_item_shapes_agree_and_each_is_deterministic():
         again, _ = _run(Q, K, V, 0.09, out="f32", items=items)
         assert np.array_equal(got, again)
         assert oracle.check_attention(got, ref, TO)[0] == 0
+
+
+PERSISTENT = [  # (batch, Lq, Lk, d, items): more items than the 256 resident workgroups
+    (300, 128, 128, 64, 128),
+    (150, 200, 260, 128, 128),      # ragged: 2 query tiles per slice, partial key stages
+    (520, 100, 130, 64, 256),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("b,Lq,Lk,d,items", PERSISTENT)
+def test_persistent_schedules_equal_one_workgroup_per_item(b, Lq, Lk, d, items, causal):
+    # each item's arithmetic is the same whichever workgroup runs it, so the
+    # three schedules agree bit for bit; the exact pin checks the result
+    _say("attn persistent b=%d Lq=%d Lk=%d d=%d items=%d causal=%d" % (b, Lq, Lk, d, items, causal))
+    Q = _sparse_q(b, Lq, d, 980 + Lq)
+    K = draw((b, Lk, d), "int", -1, 1, 981 + Lk)
+    V = draw((b, Lk, d), "int", -4, 4, 982 + d)
+    one, _ = _run(Q, K, V, math.log(2.0), out="f32", causal=causal, items=items, sched="one")
+    ref, TO = _ref(Q, K, V, math.log(2.0), causal=causal)
+    assert np.all(np.abs(one - ref) <= 2.0 ** -18 * TO)
+    for sched in ("static", "queue", "queue"):
+        got, _ = _run(Q, K, V, math.log(2.0), out="f32", causal=causal, items=items, sched=sched)
+        assert np.array_equal(got, one), sched
+
+
+def test_queue_counters_reset_between_launches():
+    # back-to-back queue launches of shrinking size: a launch that left its
+    # counters behind would make a later one skip items (NaN rows remain)
+    w = ATTN_WORKLOADS["attn32x2048"]
+    Q, K, V = attn_operands(w)
+    full, _ = _run(Q, K, V, w.scale, out="f32", causal=True, sched="one")
+    for nb in (32, 31, 9, 32):
+        got, _ = _run(Q[:nb].contiguous(), K[:nb].contiguous(), V[:nb].contiguous(), w.scale, out="f32",
+                      causal=True, sched="queue")
+        assert np.array_equal(got, full[:nb]), nb
+    # every launch takes the next of 64 counter slots: 150 more launches reuse
+    # each slot at least twice
+    Qs, Ks, Vs = Q[:3].contiguous(), K[:3].contiguous(), V[:3].contiguous()
+    Qd, Kd, Vd = Qs.to(DEV), Ks.to(DEV), Vs.to(DEV)
+    Ob = torch.empty((3, w.Lq, w.dv), dtype=torch.float32, device=DEV)
+    ref = torch.from_numpy(full[:3]).float().to(DEV)
+    bad = []
+    for i in range(150):
+        Ob.fill_(float("nan"))
+        asl.attn_fwd_run(Qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), Ob.data_ptr(), 3, w.Lq, w.Lk, w.d, w.dv,
+                         (w.d, 1, w.Lq * w.d), (w.d, 1, w.Lk * w.d), (w.dv, 1, w.Lk * w.dv),
+                         (w.dv, 1, w.Lq * w.dv), w.scale, asl.AS_BF16, asl.AS_F32,
+                         flags=asl.AS_ATTN_CAUSAL | asl.AS_ATTN_SCHED_QUEUE,
+                         stream=torch.cuda.current_stream().cuda_stream)
+        if not torch.equal(Ob, ref):
+            bad.append(i)
+    assert not bad, "launches %s differ" % bad[:10]
