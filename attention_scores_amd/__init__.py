@@ -27,13 +27,14 @@ AS_FLAG_NO_GROUPING = 0x1
 AS_FLAG_TILE_128 = 0x2
 AS_FLAG_TILE_256 = 0x4
 AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
+AS_FLAG_NO_SPLIT_K = 0x10
 AS_ATTN_CAUSAL = 0x1
 AS_ATTN_QUERIES_256 = 0x2
 AS_ATTN_QUERIES_128 = 0x4
 AS_ATTN_SCHED_STATIC = 0x8
 AS_ATTN_SCHED_QUEUE = 0x10
 
-EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of",
+EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of", "gemm_plan_split_k",
             "sscore_run", "attn_fwd_run", "attn_fwd_plan_info", "tilecast_run", "as_status_str",
             "as_last_error")
 
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_plan_info.restype = ctypes.c_int
         L.gemm_plan_tile_of.argtypes = [vp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.gemm_plan_tile_of.restype = ctypes.c_int
+        L.gemm_plan_split_k.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        L.gemm_plan_split_k.restype = ctypes.c_int
         L.sscore_run.argtypes = [vp, vp, vp, i64, i64, i64, i64, Strides, Strides, Strides,
                                  ctypes.c_int, ctypes.c_int, vp]
         L.sscore_run.restype = ctypes.c_int
@@ -140,6 +143,13 @@ def gemm_plan_info(plan: int):
     _check(lib().gemm_plan_info(plan, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(tk), ctypes.byref(nt),
                                 ctypes.byref(wg)))
     return tm.value, tn.value, tk.value, nt.value, wg.value
+
+
+def gemm_plan_split_k(plan: int):
+    """(K chunks, workspace bytes) of a plan; (1, 0) when it does not split K."""
+    sp, wb = ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().gemm_plan_split_k(plan, ctypes.byref(sp), ctypes.byref(wb)))
+    return sp.value, wb.value
 
 
 def gemm_plan_tile_of(plan: int, slot: int):

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_scores.so")
-SOURCES = ["api.cpp", "gemm.hip", "attn.hip", "tilecast.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "splitk.hip", "attn.hip", "tilecast.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.

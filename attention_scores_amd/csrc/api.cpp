@@ -15,11 +15,18 @@
 #include <string>
 #include <unordered_set>
 
+#include <hip/hip_runtime_api.h>
+
 #include "internal.hpp"
 #include "schedule.hpp"
 
 struct as_gemm_plan {
     asl::GemmDesc d;
+    // Split-K workspace (device memory of d.ws_bytes), allocated by the first
+    // run on a device and kept until the plan is destroyed.
+    std::mutex ws_mu;
+    void* ws = nullptr;
+    int ws_dev = -1;
 };
 
 namespace {
@@ -51,9 +58,10 @@ as_status ok() {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 |
-                                 AS_FLAG_ONE_TILE_PER_WORKGROUP;
+                                 AS_FLAG_ONE_TILE_PER_WORKGROUP | AS_FLAG_NO_SPLIT_K;
 constexpr int64_t kBK = asl::kTileK;
 constexpr int64_t kCus = 256;   // MI355X compute units
+constexpr int64_t kMinSplitK = 1024;   // shallowest K chunk of a split product
 
 // Rows of tiles per group.  The cost of a candidate is the operand-panel
 // traffic one XCD's L2 would take from memory, estimated on XCD 0's share
@@ -175,14 +183,36 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
     d.tiles = batch * d.tiles_m * d.tiles_n;
     d.grouped = !(flags & AS_FLAG_NO_GROUPING);
+    // Split K when the output tiles leave CUs idle (fewer tiles than CUs):
+    // into 2, 4, 8 or 16 chunks, each a multiple of the K stage and at least
+    // kMinSplitK deep, as many as keep tiles x chunks within the resident
+    // grid.  The fp32 partial sums then cost 8 bytes per output element and
+    // chunk (written, then read back by the reduction), against 2*kc flop
+    // per element and chunk.  (With a tile per CU already, a second
+    // workgroup per CU gained nothing: 2048^2 x 4096 ran 43.3 us unsplit,
+    // 44.4 us in two chunks.)
+    d.splits = 1;
+    d.kc = K;
+    if (!(flags & AS_FLAG_NO_SPLIT_K) && batch == 1 && d.tiles < kCus) {
+        const int64_t resident = (tile == 256 ? 1 : 2) * kCus;
+        int64_t s = 1;
+        while (s < 16 && d.tiles * s * 2 <= resident && K % (kBK * s * 2) == 0 && K / (s * 2) >= kMinSplitK) s *= 2;
+        if (s > 1) {
+            d.splits = (int32_t)s;
+            d.kc = K / s;
+            d.ws_ld = (N + 3) & ~INT64_C(3);
+            d.ws_bytes = s * M * d.ws_ld * 4;
+        }
+    }
     // As many workgroups as stay resident (one per CU for the 256 tile's
     // 145 KiB of LDS, two for the 128 tile), each walking its XCD's tiles
     // with the LDS ring streaming across tile boundaries, so one tile's
     // stores drain while the next tile computes; or, for the ablation, one
     // workgroup per tile.
     const int64_t resident = (tile == 256 ? 1 : 2) * kCus;
-    d.grid = !(flags & AS_FLAG_ONE_TILE_PER_WORKGROUP) && d.tiles > resident ? resident : d.tiles;
-    d.group_m = choose_group_m(d.tiles, d.tiles_m, d.tiles_n, tile, K);
+    const int64_t launched = d.tiles * d.splits;   // split: every (chunk, tile) pair
+    d.grid = !(flags & AS_FLAG_ONE_TILE_PER_WORKGROUP) && launched > resident ? resident : launched;
+    d.group_m = choose_group_m(launched, d.tiles_m, d.tiles_n, tile, d.kc);
     *out = d;
     return AS_OK;
 }
@@ -221,6 +251,23 @@ int attn_key_split(int64_t batch, int64_t Lq, uint32_t flags) {
     const int64_t n256 = batch * ((Lq + 255) / 256), n128 = batch * ((Lq + 127) / 128);
     const int64_t r256 = (n256 + kCus - 1) / kCus, r128 = (n128 + kCus - 1) / kCus;
     return 565 * r128 < 1000 * r256 ? 2 : 1;
+}
+
+// The product kernel launch of a split plan: `splits` products over the K
+// chunks (chunk s of A and B starts s*kc along K), each into its own fp32
+// slice of the workspace.
+asl::GemmDesc split_launch_desc(const asl::GemmDesc& d) {
+    asl::GemmDesc e = d;
+    e.batch = d.splits;
+    e.K = d.kc;
+    e.a_batch = d.kc * d.a_col;        // A[i, k] at i*a_row + k*a_col
+    e.b_batch = d.kc * d.b_row;        // B[k, j] at k*b_row + j*b_col
+    e.c_row = d.ws_ld;
+    e.c_batch = d.M * d.ws_ld;
+    e.c_bf16 = false;
+    e.tiles = d.tiles * d.splits;
+    e.splits = 1;
+    return e;
 }
 
 bool plan_live(const as_gemm_plan* p) {
@@ -262,13 +309,49 @@ as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t b
 
 as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream) {
     if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
-    return run_desc(plan->d, A, B, C, hip_stream);
+    const asl::GemmDesc& d = plan->d;
+    if (d.splits == 1) return run_desc(d, A, B, C, hip_stream);
+    if (!A || !B || !C) return fail(AS_ERR_INVALID, "null device pointer");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C))
+        return fail(AS_ERR_UNSUPPORTED, "device pointers must be 16-byte aligned");
+    void* ws;
+    {
+        std::lock_guard<std::mutex> lk(plan->ws_mu);
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return fail(AS_ERR_HIP, "hipGetDevice failed");
+        if (!plan->ws || plan->ws_dev != dev) {
+            if (plan->ws) {
+                (void)hipSetDevice(plan->ws_dev);
+                (void)hipFree(plan->ws);
+                (void)hipSetDevice(dev);
+                plan->ws = nullptr;
+            }
+            if (hipMalloc(&plan->ws, (size_t)d.ws_bytes) != hipSuccess) {
+                plan->ws = nullptr;
+                (void)hipGetLastError();
+                return fail(AS_ERR_NOMEM, "split-K workspace of %" PRId64 " bytes", d.ws_bytes);
+            }
+            plan->ws_dev = dev;
+        }
+        ws = plan->ws;
+    }
+    int e = asl::launch_gemm(split_launch_desc(d), A, B, ws, hip_stream);
+    if (e == 0) e = asl::launch_splitk_reduce(d, ws, C, hip_stream);
+    if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
+    return ok();
 }
 
 as_status gemm_destroy(as_gemm_t plan) {
     {
         std::lock_guard<std::mutex> lk(g_plans_mu);
         if (!plan || !plans().erase(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
+    }
+    if (plan->ws) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(plan->ws_dev);
+        (void)hipFree(plan->ws);
+        (void)hipSetDevice(cur);
     }
     delete plan;
     return ok();
@@ -288,10 +371,18 @@ as_status gemm_plan_info(as_gemm_t plan, int32_t* tile_m, int32_t* tile_n, int32
 as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* batch, int64_t* tile_row,
                             int64_t* tile_col) {
     if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
-    if (workgroup < 0 || workgroup >= plan->d.tiles || !batch || !tile_row || !tile_col)
+    const asl::GemmDesc L = plan->d.splits > 1 ? split_launch_desc(plan->d) : plan->d;
+    if (workgroup < 0 || workgroup >= L.tiles || !batch || !tile_row || !tile_col)
         return fail(AS_ERR_INVALID, "execution slot out of range or null output");
-    if (!asl::tile_of_slot(plan->d, workgroup, batch, tile_row, tile_col))
+    if (!asl::tile_of_slot(L, workgroup, batch, tile_row, tile_col))
         return fail(AS_ERR_INVALID, "execution slot %" PRId64 " is empty", workgroup);
+    return ok();
+}
+
+as_status gemm_plan_split_k(as_gemm_t plan, int32_t* splits, int64_t* workspace_bytes) {
+    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
+    if (splits) *splits = plan->d.splits;
+    if (workspace_bytes) *workspace_bytes = plan->d.splits > 1 ? plan->d.ws_bytes : 0;
     return ok();
 }
 
@@ -319,7 +410,7 @@ as_status sscore_run(const void* Q, const void* K, void* S,
     for (int i = 0; i < cached; ++i)
         if (std::memcmp(cache[i].key, key, sizeof key) == 0) return run_desc(cache[i].d, Q, K, S, hip_stream);
     asl::GemmDesc d;
-    as_status st = plan_desc(&d, Lq, Lk, dim, batch, a, b, s, qk_t, qk_t, s_t, 0);
+    as_status st = plan_desc(&d, Lq, Lk, dim, batch, a, b, s, qk_t, qk_t, s_t, AS_FLAG_NO_SPLIT_K);
     if (st != AS_OK) return st;
     Cached& slot = cache[next_slot];
     std::memcpy(slot.key, key, sizeof key);

@@ -23,10 +23,20 @@ struct GemmDesc {
     bool grouped;                    // XCD-aware grouped order (false: identity)
     int64_t tiles_m, tiles_n, tiles; // output tiles
     int64_t grid;                    // workgroups launched (tiles, or fewer: persistent)
+    // Split K (batch 1 only): the product runs as `splits` products over
+    // consecutive K chunks of kc, each writing fp32 partial sums to its own
+    // slice of a workspace (row stride ws_ld, ws_bytes in all); a second
+    // kernel adds the slices in chunk order into C.  splits == 1: no split.
+    int32_t splits;
+    int64_t kc, ws_ld, ws_bytes;
 };
 
 // Launch the planned product.  Returns 0 or a hipError_t value.
 int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* stream);
+
+// C = sum over chunks s = 0 .. splits-1 (in that order) of workspace slice s,
+// rounded to C's type.  Returns 0 or a hipError_t value.
+int launch_splitk_reduce(const GemmDesc& d, const void* ws, void* C, void* stream);
 
 // Tile computed in execution slot i (round i div grid of workgroup i mod
 // grid; the device schedule, shared with the kernels).  False if empty.

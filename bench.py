@@ -36,8 +36,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 HEADLINE = "gemm8192"
 KERNEL_SOURCES = {kind: [os.path.join(ROOT, "attention_scores_amd", "csrc", f)
-                          for f in (main, "schedule.hpp", "tile.hpp")]
-                  for kind, main in (("gemm", "gemm.hip"), ("attn", "attn.hip"))}
+                          for f in mains + ("schedule.hpp", "tile.hpp")]
+                  for kind, mains in (("gemm", ("gemm.hip", "splitk.hip")), ("attn", ("attn.hip",)))}
 
 
 def kernel_kind(name: str) -> str:
@@ -172,14 +172,14 @@ def time_workload(w, steps, warmup, flags=0):
         sq, sk, ss = w.a_strides(), w.b_strides(), (w.N, 1, w.M * w.N)
         # the plan sscore_run makes internally, for reporting only
         plan = asl.gemm_create(w.M, w.N, w.K, w.batch, sq, (1, sk[0], sk[2]), ss, asl.AS_BF16, asl.AS_BF16, s_t)
-        info = asl.gemm_plan_info(plan)
+        info = asl.gemm_plan_info(plan) + (1,)
         asl.gemm_destroy(plan)
 
         def run():
             asl.sscore_run(a, b, c, w.batch, w.M, w.N, w.K, sq, sk, ss, asl.AS_BF16, s_t, sh)
     else:
         plan = _plan(asl, w, flags)
-        info = asl.gemm_plan_info(plan)
+        info = asl.gemm_plan_info(plan) + (asl.gemm_plan_split_k(plan)[0],)
 
         def run():
             asl.gemm_run(plan, a, b, c, sh)
@@ -412,6 +412,7 @@ def main():
         "data": "synthetic (seeded, %s)" % w.dist,
         "config": {"workload": w.description, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "tile": "%dx%dx%d" % (info[0], info[1], info[2]), "tiles": info[3], "workgroups": info[4],
+                   "split_k": info[5],
                    "grouping": "none" if args.flags & asl.AS_FLAG_NO_GROUPING else "xcd-grouped"},
         "roofline": roofline,
         "mfma_util": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -94,6 +94,7 @@ typedef struct {
 #define AS_FLAG_TILE_256    0x4u  /* force 256x256 output tiles */
 #define AS_FLAG_ONE_TILE_PER_WORKGROUP 0x8u  /* ablation: one workgroup per output tile instead of a resident
                                                * (persistent) grid whose workgroups walk several tiles */
+#define AS_FLAG_NO_SPLIT_K  0x10u /* never split K over workgroups (no workspace) */
 
 typedef struct as_gemm_plan* as_gemm_t;
 
@@ -113,16 +114,35 @@ typedef struct as_gemm_plan* as_gemm_t;
  * grouping and the grid: by default as many workgroups as stay resident
  * (256 for the 256x256 tile, 512 for 128x128; fewer if there are fewer
  * tiles), each walking several tiles.  Makes no HIP call.
+ * Split K: when batch == 1 and there are fewer output tiles than the 256
+ * CUs, the plan splits K into 2, 4, 8 or 16 equal chunks
+ * (each a multiple of 64 and at least 1024 deep), as many as keep tiles x
+ * chunks within the resident grid.  Each chunk's product goes to an fp32
+ * slice of a workspace and a second kernel adds the slices in chunk order
+ * into C (deterministic; the sum is ordered differently from an unsplit
+ * product, within the same rounding bound).  The workspace
+ * (gemm_plan_split_k) is device memory that the plan allocates on its first
+ * gemm_run on a device and frees in gemm_destroy; runs of one plan share it,
+ * so they must not overlap (the same stream, or ordered streams).
+ * AS_FLAG_NO_SPLIT_K turns splitting off.
  */
 AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t batch,
                       as_strides a, as_strides b, as_strides c,
                       as_dtype a_t, as_dtype b_t, as_dtype c_t, uint32_t flags);
 
 /* Launch the planned product on `hip_stream`.  A, B: device bf16; C: device
- * fp32 or bf16 as planned.  Pointers must be 16-byte aligned. */
+ * fp32 or bf16 as planned.  Pointers must be 16-byte aligned.  A split plan
+ * launches two kernels and, on its first run on a device, allocates its
+ * workspace (AS_ERR_NOMEM if that fails). */
 AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream);
 
-/* Release a plan created by gemm_create (NULL or unknown -> AS_ERR_INVALID). */
+/* Whether a plan splits K: number of K chunks (1: no split) and the bytes
+ * of device workspace its runs use (0 without a split).  Any output pointer
+ * may be NULL.  AS_ERR_INVALID on a bad plan. */
+AS_API as_status gemm_plan_split_k(as_gemm_t plan, int32_t* splits, int64_t* workspace_bytes);
+
+/* Release a plan created by gemm_create (NULL or unknown -> AS_ERR_INVALID).
+ * Frees a split plan's workspace (hipFree, which waits for the device). */
 AS_API as_status gemm_destroy(as_gemm_t plan);
 
 /* What a plan chose (for reporting): output tile shape and K stage depth,

@@ -322,3 +322,38 @@ def test_attention_work_items():
     for bad in ((0, 10, 0), (1, 0, 0), (1, 10, 0x20), (1, 10, 0x6), (1, 10, 0x18)):
         with pytest.raises(asl.AsError):
             info(*bad)
+
+
+def test_split_k_plans():
+    # K is split only for a single product with fewer tiles than CUs, into
+    # chunks that are multiples of 64 and >= 1024 deep
+    def plan(M, N, K, batch=1, flags=0):
+        p = asl.gemm_create(M, N, K, batch, (K, 1, M * K), (N, 1, K * N), (N, 1, M * N), flags=flags)
+        try:
+            return asl.gemm_plan_info(p), asl.gemm_plan_split_k(p)
+        finally:
+            asl.gemm_destroy(p)
+    assert plan(1024, 1024, 8192) == ((128, 128, 64, 64, 512), (8, 8 * 1024 * 1024 * 4))
+    assert plan(4096, 2048, 8192) == ((256, 256, 64, 128, 256), (2, 2 * 4096 * 2048 * 4))
+    assert plan(1000, 3000, 4096)[1] == (2, 2 * 1000 * 3000 * 4)       # ragged tiles
+    assert plan(256, 256, 65536)[1][0] == 16                          # at most 16 chunks
+    assert plan(512, 512, 512)[1] == (1, 0)                           # chunks would be < 1024 deep
+    assert plan(8192, 8192, 8192)[1] == (1, 0)                        # the tiles fill the grid
+    assert plan(2048, 2048, 4096)[1] == (1, 0)                        # 256 tiles of 128: one per CU
+    assert plan(1024, 1024, 8192, batch=2)[1] == (1, 0)               # batched: no split
+    assert plan(1024, 1024, 8200)[1] == (1, 0)                        # K not a multiple of 128
+    assert plan(1024, 1024, 8192, flags=asl.AS_FLAG_NO_SPLIT_K) == ((128, 128, 64, 64, 64), (1, 0))
+
+
+def test_split_plan_slots_cover_every_chunk_and_tile():
+    M, N, K = 1000, 700, 4096
+    p = asl.gemm_create(M, N, K, 1, (K, 1, M * K), (1, K, K * N), (N, 1, M * N))     # K-major B
+    try:
+        tm, _, _, tiles, grid = asl.gemm_plan_info(p)
+        splits, _ = asl.gemm_plan_split_k(p)
+        assert splits == 4 and grid == tiles * splits
+        seen = {asl.gemm_plan_tile_of(p, h) for h in range(grid)}   # (chunk, tile row, tile column)
+        assert seen == {(s, r, c) for s in range(splits) for r in range(-(-M // tm)) for c in range(-(-N // tm))}
+        assert _status(asl.gemm_plan_tile_of, p, grid) == asl.AS_ERR_INVALID
+    finally:
+        asl.gemm_destroy(p)

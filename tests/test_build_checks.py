@@ -58,7 +58,7 @@ def test_every_lds_dma_load_follows_its_wait_states(src, asm):
 
 
 def test_kernels_use_no_scratch_memory(asm):
-    for src in ("gemm.hip", "attn.hip"):
+    for src in ("gemm.hip", "splitk.hip", "attn.hip"):
         text = "\n".join(asm(src))
         sizes = [int(v) for v in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)]
         spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]

@@ -126,6 +126,66 @@ def test_batch_broadcast_of_B():
     assert np.array_equal(_decode(C), Cref)
 
 
+# ------------------------------------------------------------ split K --
+
+SPLIT = [  # (M, N, K, a_k, b_k): tiles fill at most half the grid, K deep enough to split
+    (512, 768, 4096, True, False),      # 24 tiles of 128, 4 chunks
+    (1000, 696, 4096, True, True),      # ragged M and N (696 = 5 x 128 + 56), K-major B
+    (768, 512, 4096, False, False),     # column-major A
+]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K,a_k,b_k", SPLIT)
+def test_split_k_integer_data_bit_exact(M, N, K, a_k, b_k, out):
+    # integer data: every partial sum, chunk sum and their total is exact in
+    # fp32, so the split product equals the oracle bit for bit (bf16: its RNE)
+    _say("split-K int exact %dx%dx%d a_k=%s b_k=%s out=%s" % (M, N, K, a_k, b_k, out))
+    a_shape, sa, b_shape, sb = _layout(M, N, K, 1, a_k, b_k)
+    A = draw(a_shape, "int", -4, 4, 61 + M)
+    B = draw(b_shape, "int", -4, 4, 62 + N)
+    plan = asl.gemm_create(M, N, K, 1, sa, sb, (N, 1, M * N))
+    assert asl.gemm_plan_split_k(plan)[0] > 1
+    asl.gemm_destroy(plan)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    C = _run_gemm(A, B, M, N, K, 1, sa, sb, od)
+    Cref, _ = oracle.gemm(bits(A), bits(B), 1, M, N, K, sa, sb, want_T=False)
+    if out == "f32":
+        assert np.array_equal(_decode(C), Cref)
+    else:
+        assert np.array_equal(bits(C), oracle.f64_to_bf16_rne_array(Cref))
+
+
+@pytest.mark.parametrize("M,N,K,a_k,b_k", SPLIT[:2])
+def test_split_k_random_data_within_tolerance_and_deterministic(M, N, K, a_k, b_k):
+    _say("split-K random %dx%dx%d" % (M, N, K))
+    a_shape, sa, b_shape, sb = _layout(M, N, K, 1, a_k, b_k)
+    A = draw(a_shape, "uniform", -1, 1, 71 + M)
+    B = draw(b_shape, "uniform", -1, 1, 72 + N)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    plan = asl.gemm_create(M, N, K, 1, sa, sb, (N, 1, M * N))
+    C1 = torch.empty((1, M, N), dtype=torch.float32, device=DEV)
+    C2 = torch.full((1, M, N), float("nan"), dtype=torch.float32, device=DEV)
+    try:
+        st = torch.cuda.current_stream().cuda_stream
+        asl.gemm_run(plan, Ad.data_ptr(), Bd.data_ptr(), C1.data_ptr(), st)
+        asl.gemm_run(plan, Ad.data_ptr(), Bd.data_ptr(), C2.data_ptr(), st)    # workspace reused
+        torch.cuda.synchronize()
+    finally:
+        asl.gemm_destroy(plan)
+    assert torch.equal(C1, C2)
+    Cref, T = oracle.gemm(bits(A), bits(B), 1, M, N, K, sa, sb)
+    _check_full(C1, Cref, T)
+    unsplit = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, asl.AS_FLAG_NO_SPLIT_K)
+    _check_full(unsplit, Cref, T)
+
+
+def test_split_k_shard_workload_sampled():
+    w = WORKLOADS["gemm4096x2048x8192"]
+    _say("%s full size, sampled" % w.name)
+    _sampled_gemm(w)
+
+
 # -------------------------------------------------- workloads, full checks --
 
 def _check_full(C, Cref, T):

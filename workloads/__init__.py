@@ -97,9 +97,13 @@ WORKLOADS: Dict[str, Workload] = {
     "gemm16384x8192x2048_colA": Workload(
         "gemm16384x8192x2048_colA", "gemm", 1, 16384, 8192, 2048, "col", "row", "uniform", -0.5, 0.5,
         (501, 502), "bf16", "bf16 GEMM M=16384 N=8192 K=2048, A column-major, B row-major, U[-0.5,0.5], bf16 out"),
+    "gemm4096x2048x8192": Workload(
+        "gemm4096x2048x8192", "gemm", 1, 4096, 2048, 8192, "row", "row", "uniform", -1.0, 1.0, (311, 312), "bf16",
+        "one GPU's share of the 8192^3 GEMM on a 2 x 4 grid of 8 GPUs: M=4096, N=2048, K=8192, row-major, "
+        "U[-1,1], bf16 out (128 tiles of 256^2: split K)"),
 }
-
-ORDER = ["gemm512", "sscore32x2048", "gemm8192", "gemm65536x256x4096", "gemm16384x8192x2048_colA"]
+ORDER = ["gemm512", "sscore32x2048", "gemm8192", "gemm65536x256x4096", "gemm16384x8192x2048_colA",
+         "gemm4096x2048x8192"]
 
 
 @dataclasses.dataclass(frozen=True)
