@@ -13,6 +13,7 @@ read shapes, strides and dtypes from torch tensors.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 import threading
@@ -223,18 +224,27 @@ def _require_cuda(*ts):
             raise AsError(AS_ERR_INVALID, "tensors must be on the GPU")
 
 
-_plan_cache = {}
+_PLAN_CACHE_SIZE = 64
+_plan_cache = collections.OrderedDict()
 _plan_cache_lock = threading.Lock()
 
 
-def plan_for(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags=0) -> int:
-    """Cached gemm_create for a shape/stride/dtype/flags key."""
-    key = (M, N, K, batch, tuple(sa), tuple(sb), tuple(sc), a_t, b_t, c_t, flags)
+def plan_for(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags=0, stream=0) -> int:
+    """Cached gemm_create for a shape/stride/dtype/flags/stream key: the last
+    64 plans are kept, the least recently used is destroyed (with its split-K
+    workspace, if any).  The stream is part of the key because a split plan's
+    runs share its workspace: calls on different streams get their own plans."""
+    key = (M, N, K, batch, tuple(sa), tuple(sb), tuple(sc), a_t, b_t, c_t, flags, stream)
     with _plan_cache_lock:
         p = _plan_cache.get(key)
-        if p is None:
-            p = gemm_create(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags)
-            _plan_cache[key] = p
+        if p is not None:
+            _plan_cache.move_to_end(key)
+            return p
+        p = gemm_create(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags)
+        _plan_cache[key] = p
+        while len(_plan_cache) > _PLAN_CACHE_SIZE:
+            _, old = _plan_cache.popitem(last=False)
+            gemm_destroy(old)
         return p
 
 
@@ -261,9 +271,10 @@ def gemm(A, B, out=None, out_dtype=None, flags: int = 0):
         out = torch.empty((batch, M, N) if batched else (M, N), dtype=od, device=A.device)
     _require_cuda(out)
     sc = _strides3(out)
+    stream = _stream_handle(A)
     plan = plan_for(M, N, K, batch, sa, sb, sc, _dtype_code(A.dtype), _dtype_code(B.dtype),
-                    _dtype_code(out.dtype), flags)
-    gemm_run(plan, A.data_ptr(), B.data_ptr(), out.data_ptr(), _stream_handle(A))
+                    _dtype_code(out.dtype), flags, stream)
+    gemm_run(plan, A.data_ptr(), B.data_ptr(), out.data_ptr(), stream)
     return out
 
 

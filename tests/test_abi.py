@@ -357,3 +357,15 @@ def test_split_plan_slots_cover_every_chunk_and_tile():
         assert _status(asl.gemm_plan_tile_of, p, grid) == asl.AS_ERR_INVALID
     finally:
         asl.gemm_destroy(p)
+
+
+def test_python_plan_cache_is_bounded_and_keyed_by_stream():
+    # the cache keeps the last 64 plans and destroys the rest (their split-K
+    # workspaces with them); a different stream gets its own plan
+    asl._plan_cache.clear()
+    first = asl.plan_for(256, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
+    assert asl.plan_for(256, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1, stream=1) != first
+    for i in range(1, 70):
+        asl.plan_for(256 + 8 * i, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
+    assert len(asl._plan_cache) == asl._PLAN_CACHE_SIZE
+    assert _status(asl.gemm_plan_info, first) == asl.AS_ERR_INVALID      # evicted and destroyed
