@@ -365,7 +365,13 @@ def test_python_plan_cache_is_bounded_and_keyed_by_stream():
     asl._plan_cache.clear()
     first = asl.plan_for(256, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
     assert asl.plan_for(256, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1, stream=1) != first
-    for i in range(1, 70):
-        asl.plan_for(256 + 8 * i, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
+    destroyed = []
+    real_destroy = asl.gemm_destroy
+    asl.gemm_destroy = lambda p: (destroyed.append(p), real_destroy(p))
+    try:
+        for i in range(1, 70):
+            asl.plan_for(256 + 8 * i, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
+    finally:
+        asl.gemm_destroy = real_destroy
     assert len(asl._plan_cache) == asl._PLAN_CACHE_SIZE
-    assert _status(asl.gemm_plan_info, first) == asl.AS_ERR_INVALID      # evicted and destroyed
+    assert destroyed[0] == first and len(destroyed) == 70 + 1 - asl._PLAN_CACHE_SIZE   # oldest first
