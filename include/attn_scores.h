@@ -142,7 +142,8 @@ AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C,
 AS_API as_status gemm_plan_split_k(as_gemm_t plan, int32_t* splits, int64_t* workspace_bytes);
 
 /* Release a plan created by gemm_create (NULL or unknown -> AS_ERR_INVALID).
- * Frees a split plan's workspace (hipFree, which waits for the device). */
+ * Frees a split plan's workspace (hipFree, which waits for the device).  The
+ * handle is dead afterwards; a later gemm_create may return the same value. */
 AS_API as_status gemm_destroy(as_gemm_t plan);
 
 /* What a plan chose (for reporting): output tile shape and K stage depth,

@@ -78,7 +78,7 @@ def _load():
     lib.oracle_sscore_points.argtypes = [u16p, u16p, ctypes.c_void_p, i64, dp, dp, i64] + [i64] * 6 + [i32]
     lib.oracle_sscore_points.restype = i32
     lib.oracle_attention.argtypes = [u16p, u16p, u16p, ctypes.c_void_p, i64, dp, dp] + [i64] * 5 + [i64] * 9 + \
-        [ctypes.c_double, i32, i32]
+        [ctypes.c_double, i32, i64, i32]
     lib.oracle_attention.restype = i32
     lib.oracle_tilecast_bytes.argtypes = [i64, i64, i64]
     lib.oracle_tilecast_bytes.restype = ctypes.c_double
@@ -212,10 +212,12 @@ def sscore_points(Q: np.ndarray, Kt: np.ndarray, pts: np.ndarray, d: int,
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, batch: int, Lq: int, Lk: int, d: int, dv: int,
               sq: Tuple[int, int, int], sk: Tuple[int, int, int], sv: Tuple[int, int, int], scale: float,
-              rows: Optional[np.ndarray] = None, nthreads: int = 0, causal: bool = False):
+              rows: Optional[np.ndarray] = None, nthreads: int = 0, causal: bool = False, kv_group: int = 1):
     """O = softmax(scale * Q K^T) V per (b, i) row in fp64; returns (O, TO).
 
     causal: query i sees keys j <= i + (Lk - Lq) only (needs Lk >= Lq).
+    kv_group: query slice b reads K and V slice b // kv_group (K and V hold
+    batch // kv_group slices).
 
     Q [b,i,d], K [b,j,d], V [b,j,c] addressed by (row, col, batch) element
     strides.  ``rows``: optional [n, 2] array of (b, i) pairs; then O and TO
@@ -225,8 +227,10 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, batch: int, Lq: int, 
     K = np.ascontiguousarray(_as_bits(K)).reshape(-1)
     V = np.ascontiguousarray(_as_bits(V)).reshape(-1)
     _span_ok(Q, (batch, Lq, d), (sq[2], sq[0], sq[1]))
-    _span_ok(K, (batch, Lk, d), (sk[2], sk[0], sk[1]))
-    _span_ok(V, (batch, Lk, dv), (sv[2], sv[0], sv[1]))
+    if kv_group <= 0 or batch % kv_group:
+        raise ValueError("kv_group must divide batch")
+    _span_ok(K, (batch // kv_group, Lk, d), (sk[2], sk[0], sk[1]))
+    _span_ok(V, (batch // kv_group, Lk, dv), (sv[2], sv[0], sv[1]))
     if rows is not None:
         r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
         if r.size and (r[:, 0].min() < 0 or r[:, 0].max() >= batch or r[:, 1].min() < 0 or r[:, 1].max() >= Lq):
@@ -242,7 +246,7 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, batch: int, Lq: int, 
     rc = _load().oracle_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(r) if r is not None else None, n,
                                   _ptr(O), _ptr(TO), batch, Lq, Lk, d, dv, sq[0], sq[1], sq[2],
                                   sk[0], sk[1], sk[2], sv[0], sv[1], sv[2], float(scale), int(bool(causal)),
-                                  nthreads)
+                                  int(kv_group), nthreads)
     if rc != 0:
         raise RuntimeError("oracle_attention failed")
     return O, TO

@@ -269,6 +269,10 @@ int oracle_sscore_points(const uint16_t* Q, const uint16_t* Kt, const int64_t* p
  * different amounts; the mask itself is the textbook one, aligned to the
  * last key so that a query block appended after a key cache sees the cache.
  * Requires Lk >= Lq, so that every query sees at least one key.
+ *
+ * kv_group: query slice b reads key/value slice b / kv_group (grouped
+ * key/value heads; 1: each query slice has its own).  The grouping only
+ * decides which K and V a slice reads; the arithmetic above is unchanged.
  */
 typedef struct {
     const uint16_t *Q, *K, *V;
@@ -278,6 +282,7 @@ typedef struct {
     int64_t q_row, q_col, q_batch, k_row, k_col, k_batch, v_row, v_col, v_batch;
     double scale;
     int causal;
+    int64_t kv_group;
     int64_t begin, end;
 } attn_job;
 
@@ -290,10 +295,11 @@ static void* attn_worker(void* arg) {
         if (g->rows) { b = g->rows[2 * r]; i = g->rows[2 * r + 1]; }
         else { b = r / g->Lq; i = r % g->Lq; }
         const uint16_t* q = g->Q + b * g->q_batch + i * g->q_row;
+        const int64_t bk = b / g->kv_group;                                /* key/value slice */
         const int64_t nk = g->causal ? i + (g->Lk - g->Lq) + 1 : g->Lk;   /* keys 0 .. nk-1 */
         double m = -INFINITY;
         for (int64_t j = 0; j < nk; ++j) {
-            const uint16_t* k = g->K + b * g->k_batch + j * g->k_row;
+            const uint16_t* k = g->K + bk * g->k_batch + j * g->k_row;
             double s = 0.0;
             for (int64_t x = 0; x < g->d; ++x)
                 s += oracle_bf16_to_f64(q[x * g->q_col]) * oracle_bf16_to_f64(k[x * g->k_col]);
@@ -310,7 +316,7 @@ static void* attn_worker(void* arg) {
         for (int64_t c = 0; c < g->dv; ++c) {
             double acc = 0.0, mag = 0.0;
             for (int64_t j = 0; j < nk; ++j) {
-                double v = oracle_bf16_to_f64(g->V[b * g->v_batch + j * g->v_row + c * g->v_col]);
+                double v = oracle_bf16_to_f64(g->V[bk * g->v_batch + j * g->v_row + c * g->v_col]);
                 acc += t[j] * v;
                 mag += t[j] * fabs(v);
             }
@@ -326,8 +332,10 @@ int oracle_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, co
                      int64_t npairs, double* O, double* TO, int64_t batch, int64_t Lq, int64_t Lk,
                      int64_t d, int64_t dv, int64_t q_row, int64_t q_col, int64_t q_batch,
                      int64_t k_row, int64_t k_col, int64_t k_batch,
-                     int64_t v_row, int64_t v_col, int64_t v_batch, double scale, int causal, int nthreads) {
+                     int64_t v_row, int64_t v_col, int64_t v_batch, double scale, int causal, int64_t kv_group,
+                     int nthreads) {
     if (!Q || !K || !V || !O || batch <= 0 || Lq <= 0 || Lk <= 0 || d <= 0 || dv <= 0) return -1;
+    if (kv_group <= 0 || batch % kv_group) return -1;
     if (causal && Lk < Lq) return -1;
     int64_t n = rows ? npairs : batch * Lq;
     if (n < 0) return -1;
@@ -340,7 +348,7 @@ int oracle_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, co
     int rc = 0;
     for (int w = 0; w < nt; ++w) {
         attn_job g = {Q, K, V, rows, O, TO, Lq, Lk, d, dv, q_row, q_col, q_batch, k_row, k_col, k_batch,
-                      v_row, v_col, v_batch, scale, causal ? 1 : 0, n * w / nt, n * (w + 1) / nt};
+                      v_row, v_col, v_batch, scale, causal ? 1 : 0, kv_group, n * w / nt, n * (w + 1) / nt};
         jobs[w] = g;
         if (pthread_create(&th[w], NULL, attn_worker, &jobs[w]) != 0) { jobs[w].end = -1; rc = -1; }
     }

@@ -290,3 +290,65 @@ def test_queue_counters_reset_between_launches():
         if not torch.equal(Ob, ref):
             bad.append(i)
     assert not bad, "launches %s differ" % bad[:10]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("items", [256, 128])
+def test_negative_scale_exact_power_of_two_probabilities(items, causal):
+    # scale -ln 2: the scale's sign flips the max into a min (the kernel's
+    # second specialisation); probabilities are again powers of two
+    b, Lq, Lk, d = 2, 300, 333, 128
+    _say("attn negative scale items=%d causal=%d" % (items, causal))
+    Q = _sparse_q(b, Lq, d, 990)
+    K = draw((b, Lk, d), "int", -1, 1, 991)
+    V = draw((b, Lk, d), "int", -4, 4, 992)
+    got, _ = _run(Q, K, V, -math.log(2.0), out="f32", causal=causal, items=items)
+    ref, TO = _ref(Q, K, V, -math.log(2.0), causal=causal)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -18 * TO)
+
+
+@pytest.mark.parametrize("items", [256, 128])
+def test_negative_scale_random_data_within_tolerance(items):
+    b, Lq, Lk, d = 2, 512, 640, 64
+    Q = draw((b, Lq, d), "normal", 0, 1, 993)
+    K = draw((b, Lk, d), "normal", 0, 1, 994)
+    V = draw((b, Lk, d), "normal", 0, 1, 995)
+    got, _ = _run(Q, K, V, -0.2, out="bf16", items=items)
+    ref, TO = _ref(Q, K, V, -0.2)
+    assert oracle.check_attention(got, ref, TO, out_bf16=True)[0] == 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_is_the_mean_of_the_visible_values(causal):
+    # every probability is 1: O_i is the plain mean of the V rows query i sees
+    b, Lq, Lk, d = 2, 200, 260, 128
+    Q = draw((b, Lq, d), "normal", 0, 1, 996)
+    K = draw((b, Lk, d), "normal", 0, 1, 997)
+    V = draw((b, Lk, d), "int", -4, 4, 998)
+    for items in (256, 128):
+        got, _ = _run(Q, K, V, 0.0, out="f32", causal=causal, items=items)
+        v = V.double().numpy()
+        off = Lk - Lq
+        for i in (0, 1, Lq // 2, Lq - 1):
+            n = i + off + 1 if causal else Lk
+            assert np.allclose(got[:, i], v[:, :n].mean(axis=1), rtol=0, atol=1e-6), (items, i)
+
+
+def test_one_key_value_head_shared_by_all_slices():
+    # multi-query attention: K and V with batch stride 0 serve every slice
+    b, Lq, Lk, d = 6, 256, 320, 128
+    Q = draw((b, Lq, d), "normal", 0, 1, 999)
+    K1 = draw((1, Lk, d), "normal", 0, 1, 1000)
+    V1 = draw((1, Lk, d), "normal", 0, 1, 1001)
+    Qd, Kd, Vd = Q.to(DEV), K1.to(DEV), V1.to(DEV)
+    for items in (256, 128):
+        Ob = torch.full((b, Lq, d), float("nan"), dtype=torch.float32, device=DEV)
+        asl.attn_fwd_run(Qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), Ob.data_ptr(), b, Lq, Lk, d, d,
+                         (d, 1, Lq * d), (d, 1, 0), (d, 1, 0), (d, 1, Lq * d), 0.1, asl.AS_BF16, asl.AS_F32,
+                         flags=ITEMS[items], stream=torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        got = Ob.double().cpu().numpy()
+        ref, TO = oracle.attention(bits(Q), bits(K1), bits(V1), b, Lq, Lk, d, d, (d, 1, Lq * d), (d, 1, 0),
+                                   (d, 1, 0), 0.1)
+        assert oracle.check_attention(got, ref, TO)[0] == 0

@@ -601,3 +601,28 @@ def test_causal_attention_ignores_masked_keys_and_catches_off_by_one():
     # one key too few: all 8 queries against the first 7 keys are refused (Lk < Lq)
     with pytest.raises(RuntimeError):
         _attn_c(Q, K[:, :7], V[:, :7], 0.6)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_key_value_heads_equal_materialised_repeats(causal):
+    # kv_group g: query slice b reads K/V slice b // g.  The same result comes
+    # from the ungrouped oracle fed K and V with each slice repeated g times
+    # (an independent layout: every slice then has its own copy), bit for bit.
+    b, g, Lq, Lk, d, dv = 6, 3, 7, 9, 8, 5
+    Q, _, _ = _attn_inputs(b, Lq, Lk, d, dv, 810)
+    _, K, V = _attn_inputs(b // g, Lq, Lk, d, dv, 811)
+    Kr = K.repeat_interleave(g, dim=0).contiguous()
+    Vr = V.repeat_interleave(g, dim=0).contiguous()
+    O, TO = oracle.attention(bits(Q), bits(K), bits(V), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
+                             (dv, 1, Lk * dv), 0.3, causal=causal, kv_group=g)
+    Or, TOr = oracle.attention(bits(Q), bits(Kr), bits(Vr), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
+                               (dv, 1, Lk * dv), 0.3, causal=causal)
+    assert np.array_equal(O, Or) and np.array_equal(TO, TOr)
+    # a grouping that sends the last group to the first K/V slice is caught
+    Kw = torch.cat([Kr[:-g], Kr[:g]]).contiguous()
+    Ow, _ = oracle.attention(bits(Q), bits(Kw), bits(Vr), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
+                             (dv, 1, Lk * dv), 0.3, causal=causal)
+    assert not np.allclose(O, Ow)
+    with pytest.raises(ValueError):
+        oracle.attention(bits(Q), bits(K), bits(V), b, Lq, Lk, d, dv, (d, 1, Lq * d), (d, 1, Lk * d),
+                         (dv, 1, Lk * dv), 0.3, kv_group=4)
