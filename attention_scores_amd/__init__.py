@@ -36,7 +36,7 @@ AS_ATTN_SCHED_STATIC = 0x8
 AS_ATTN_SCHED_QUEUE = 0x10
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of", "gemm_plan_split_k",
-            "sscore_run", "attn_fwd_run", "attn_fwd_plan_info", "tilecast_run", "as_status_str",
+            "sscore_run", "attn_fwd_run", "attn_fwd_run_gqa", "attn_fwd_plan_info", "tilecast_run", "as_status_str",
             "as_last_error")
 
 
@@ -93,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, Strides, Strides, Strides, Strides,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp]
         L.attn_fwd_run.restype = ctypes.c_int
+        L.attn_fwd_run_gqa.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, Strides, Strides, Strides,
+                                       Strides, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp]
+        L.attn_fwd_run_gqa.restype = ctypes.c_int
         L.attn_fwd_plan_info.argtypes = [i64, i64, u32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64)]
         L.attn_fwd_plan_info.restype = ctypes.c_int
         L.tilecast_run.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, i64, i64, i64, vp, vp]
@@ -167,6 +170,15 @@ def attn_fwd_run(Q: int, K: int, V: int, O: int, batch: int, Lq: int, Lk: int, d
     """O = softmax(scale Q K^T) V on device pointers (see attn_fwd_run in attn_scores.h)."""
     _check(lib().attn_fwd_run(Q, K, V, O, batch, Lq, Lk, d, dv, Strides(*q), Strides(*k), Strides(*v),
                               Strides(*o), float(scale), qkv_t, o_t, flags, stream))
+
+
+def attn_fwd_run_gqa(Q: int, K: int, V: int, O: int, batch: int, kv_group: int, Lq: int, Lk: int, d: int, dv: int,
+                     q: Tuple[int, int, int], k: Tuple[int, int, int], v: Tuple[int, int, int],
+                     o: Tuple[int, int, int], scale: float, qkv_t: int = AS_BF16, o_t: int = AS_BF16,
+                     flags: int = 0, stream: int = 0) -> None:
+    """attn_fwd_run with query slice b reading K/V slice b // kv_group (see attn_scores.h)."""
+    _check(lib().attn_fwd_run_gqa(Q, K, V, O, batch, kv_group, Lq, Lk, d, dv, Strides(*q), Strides(*k),
+                                  Strides(*v), Strides(*o), float(scale), qkv_t, o_t, flags, stream))
 
 
 def attn_fwd_plan_info(batch: int, Lq: int, flags: int = 0):
@@ -298,16 +310,17 @@ def sscore(Q, K, out=None, out_dtype=None):
 
 
 def attention(Q, K, V, scale=None, out=None, out_dtype=None, causal=False):
-    """O = softmax(scale Q K^T) V per slice: Q [b,Lq,d], K [b,Lk,d], V [b,Lk,dv]
-    bf16 -> O [b,Lq,dv] (default scale 1/sqrt(d), bf16 output); causal: query
-    i sees keys j <= i + Lk - Lq only."""
+    """O = softmax(scale Q K^T) V per slice: Q [b,Lq,d], K [bk,Lk,d], V [bk,Lk,dv]
+    bf16 -> O [b,Lq,dv] (default scale 1/sqrt(d), bf16 output).  bk may divide b
+    (grouped key/value heads: query slice i reads K/V slice i // (b // bk)).
+    causal: query i sees keys j <= i + Lk - Lq only."""
     torch = _torch()
     _require_cuda(Q, K, V)
     if Q.dim() != 3 or K.dim() != 3 or V.dim() != 3:
         raise AsError(AS_ERR_INVALID, "Q, K and V must be [batch, L, d]")
     b, Lq, d = Q.shape
-    Lk, dv = V.shape[1], V.shape[2]
-    if K.shape[0] != b or V.shape[0] != b or K.shape[2] != d or K.shape[1] != Lk:
+    bk, Lk, dv = V.shape
+    if K.shape[0] != bk or K.shape[2] != d or K.shape[1] != Lk or bk <= 0 or b % bk:
         raise AsError(AS_ERR_INVALID, "Q, K and V shapes do not match")
     if scale is None:
         scale = d ** -0.5
@@ -315,9 +328,9 @@ def attention(Q, K, V, scale=None, out=None, out_dtype=None, causal=False):
         od = out_dtype if out_dtype is not None else torch.bfloat16
         out = torch.empty((b, Lq, dv), dtype=od, device=Q.device)
     _require_cuda(out)
-    attn_fwd_run(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), b, Lq, Lk, d, dv, _strides3(Q),
-                 _strides3(K), _strides3(V), _strides3(out), scale, _dtype_code(Q.dtype), _dtype_code(out.dtype),
-                 AS_ATTN_CAUSAL if causal else 0, _stream_handle(Q))
+    attn_fwd_run_gqa(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), b, b // bk, Lq, Lk, d, dv,
+                     _strides3(Q), _strides3(K), _strides3(V), _strides3(out), scale, _dtype_code(Q.dtype),
+                     _dtype_code(out.dtype), AS_ATTN_CAUSAL if causal else 0, _stream_handle(Q))
     return out
 
 

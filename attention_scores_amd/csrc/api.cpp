@@ -424,6 +424,16 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
                        int64_t Lk, int64_t d, int64_t dv, as_strides q, as_strides k, as_strides v,
                        as_strides o, float scale, as_dtype qkv_t, as_dtype o_t, uint32_t flags,
                        void* hip_stream) {
+    return attn_fwd_run_gqa(Q, K, V, O, batch, 1, Lq, Lk, d, dv, q, k, v, o, scale, qkv_t, o_t, flags, hip_stream);
+}
+
+as_status attn_fwd_run_gqa(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t kv_group,
+                           int64_t Lq, int64_t Lk, int64_t d, int64_t dv, as_strides q, as_strides k,
+                           as_strides v, as_strides o, float scale, as_dtype qkv_t, as_dtype o_t, uint32_t flags,
+                           void* hip_stream) {
+    if (kv_group <= 0 || (batch > 0 && batch % kv_group))
+        return fail(AS_ERR_INVALID, "kv_group must be positive and divide batch (batch=%" PRId64 " kv_group=%" PRId64
+                    ")", batch, kv_group);
     if (batch <= 0 || Lq <= 0 || Lk <= 0 || d <= 0 || dv <= 0)
         return fail(AS_ERR_INVALID, "sizes must be positive (batch=%" PRId64 " Lq=%" PRId64 " Lk=%" PRId64
                     " d=%" PRId64 " dv=%" PRId64 ")", batch, Lq, Lk, d, dv);
@@ -464,6 +474,7 @@ as_status attn_fwd_run(const void* Q, const void* K, const void* V, void* O, int
     ad.o_row = o.row; ad.o_batch = o.batch;
     ad.o_bf16 = (o_t == AS_BF16);
     ad.causal = causal;
+    ad.kv_group = kv_group;
     ad.c = (float)((double)scale * 1.4426950408889634);   // log2(e)
     ad.key_split = attn_key_split(batch, Lq, flags);
     const int64_t bq = asl::attn_queries_per_workgroup(ad.key_split);

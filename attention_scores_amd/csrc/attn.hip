@@ -66,6 +66,7 @@ struct AttnArgs {
     int32_t batch, Lq, Lk, qtiles, tiles;
     int32_t causal;       // query i sees keys j <= i + (Lk - Lq) only
     int32_t heavy_first;  // items in heaviest-first order (below)
+    int32_t kv_group;     // query slice b reads K and V slice b / kv_group
     int32_t sched;        // 0: one workgroup per item; 1: persistent, static stride; 2: persistent, queue
     int32_t qslot;        // queue counters used by this launch (sched 2)
     float c;   // scale * log2(e)
@@ -184,7 +185,11 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
     int bb, u;                                     // slice, query tile
     if (a.heavy_first) {
         const int g = x + kXcds * k;
-        bb = g % a.batch;
+        const int r = g % a.batch;
+        // With batch a multiple of 8, item g runs on XCD g mod 8 = r mod 8:
+        // give that XCD the contiguous slices x*(batch/8) .. so that query
+        // slices sharing K and V (a key/value group) share its L2.
+        bb = a.batch % kXcds == 0 ? (r % kXcds) * (a.batch / kXcds) + r / kXcds : r;
         u = a.qtiles - 1 - g / a.batch;
     } else {
         const int L = qstart + k;
@@ -200,8 +205,9 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_fwd_kernel(AttnArgs a) {
     if (a.causal) kend = (qt0 + BQ < a.Lq ? qt0 + BQ : a.Lq) + off;   // keys 0 .. kend-1
     const int nst = (kend + BN - 1) / BN;
 
-    const uint16_t* kb = a.K + bb * a.k_bs;
-    const uint16_t* vb = a.V + bb * a.v_bs;
+    const int bkv = bb / a.kv_group;               // key/value slice
+    const uint16_t* kb = a.K + bkv * a.k_bs;
+    const uint16_t* vb = a.V + bkv * a.v_bs;
 
     // Q fragments (B operand of K Q^T): query q0 + col, d 16*s + 8*h ..+7.
     bf16x8 qf[DS];
@@ -478,6 +484,7 @@ int launch_attn(const AttnDesc& d, const void* Q, const void* K, const void* V, 
     k.tiles = (int32_t)d.tiles;
     k.causal = d.causal ? 1 : 0;
     k.heavy_first = d.causal ? 1 : 0;
+    k.kv_group = (int32_t)d.kv_group;
     k.sched = d.sched;
     static std::atomic<uint32_t> launches{0};
     k.qslot = (int32_t)(launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);

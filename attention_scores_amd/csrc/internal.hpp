@@ -54,6 +54,7 @@ struct AttnDesc {
     bool causal;                     // query i sees keys j <= i + (Lk - Lq)
     float c;                         // scale * log2(e)
     int key_split;                   // 1 or 2
+    int64_t kv_group;                // query slice b reads K and V slice b / kv_group
     int sched;                       // 0: one workgroup per item; 1: persistent, static; 2: persistent, queue
     int64_t qtiles, tiles;           // query tiles per slice, work items (batch * qtiles)
     int64_t grid;                    // workgroups launched

@@ -142,11 +142,11 @@ def time_attention(w, steps, warmup):
     stream = torch.cuda.current_stream(dev)
     sq, sk, sv, so = w.strides()
     o_t = asl.AS_BF16 if w.out == "bf16" else asl.AS_F32
-    args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), w.batch, w.Lq, w.Lk, w.d, w.dv,
+    args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), w.batch, w.kv_group, w.Lq, w.Lk, w.d, w.dv,
             sq, sk, sv, so, w.scale, asl.AS_BF16, o_t, asl.AS_ATTN_CAUSAL if w.causal else 0, stream.cuda_stream)
 
     def run():
-        asl.attn_fwd_run(*args)
+        asl.attn_fwd_run_gqa(*args)
     out = _timed(run, steps, warmup, stream)
     del Q, K, V, O
     return out
@@ -238,7 +238,7 @@ def cpu_baseline_attn(w, target_s=12.0):
         rows = np.stack([flat // w.Lq, flat % w.Lq], axis=1)
         t = time.perf_counter()
         oracle.attention(Q, K, V, w.batch, w.Lq, w.Lk, w.d, w.dv, sq, sk, sv, w.scale, rows=rows,
-                         nthreads=threads, causal=w.causal)
+                         nthreads=threads, causal=w.causal, kv_group=w.kv_group)
         secs = time.perf_counter() - t
         keys = (rows[:, 1] + (w.Lk - w.Lq) + 1).sum() if w.causal else n * w.Lk   # keys each row sees
         return secs, 2.0 * float(keys) * (w.d + w.dv)
@@ -330,7 +330,8 @@ def attention_line(w, args):
         "dtype": "bf16",
         "data": "synthetic (seeded, %s)" % w.dist,
         "config": {"workload": w.description, "batch": w.batch, "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "dv": w.dv,
-                   "causal": w.causal, "queries_per_workgroup": qw, "keys_per_stage": kps, "workgroups": wgs},
+                   "causal": w.causal, "kv_group": w.kv_group, "queries_per_workgroup": qw, "keys_per_stage": kps,
+                   "workgroups": wgs},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": (traffic["read_bytes"] + traffic["write_bytes"]) if traffic else None,

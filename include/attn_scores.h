@@ -234,6 +234,22 @@ AS_API as_status attn_fwd_run(const void* Q, const void* K, const void* V, void*
                               float scale, as_dtype qkv_t, as_dtype o_t, uint32_t flags,
                               void* hip_stream);
 
+/*
+ * Attention forward with grouped key/value heads: as attn_fwd_run, but query
+ * slice b (0 <= b < batch) attends to key/value slice b / kv_group, so K and
+ * V hold batch / kv_group slices (their batch strides step over those).
+ * kv_group must be positive and divide batch (AS_ERR_INVALID otherwise);
+ * kv_group == 1 is attn_fwd_run.  Query slices sharing K and V are many
+ * consumers of the same key/value tiles, the reuse the deep-dive's
+ * Attention/GEMM use-case describes: with the causal mask and batch a
+ * multiple of 8 each XCD runs a contiguous block of slices, so a group's
+ * K and V come from HBM once per XCD.
+ */
+AS_API as_status attn_fwd_run_gqa(const void* Q, const void* K, const void* V, void* O,
+                                  int64_t batch, int64_t kv_group, int64_t Lq, int64_t Lk, int64_t d, int64_t dv,
+                                  as_strides q, as_strides k, as_strides v, as_strides o,
+                                  float scale, as_dtype qkv_t, as_dtype o_t, uint32_t flags, void* hip_stream);
+
 /* The work items attn_fwd_run chooses for `batch` slices of Lq queries under
  * `flags`: queries per workgroup (256 or 128), keys per LDS stage (64 or
  * 128) and workgroups launched.  Any output pointer may be NULL.  Host-only,

@@ -375,3 +375,13 @@ def test_python_plan_cache_is_bounded_and_keyed_by_stream():
         asl.gemm_destroy = real_destroy
     assert len(asl._plan_cache) == asl._PLAN_CACHE_SIZE
     assert destroyed[0] == first and len(destroyed) == 70 + 1 - asl._PLAN_CACHE_SIZE   # oldest first
+
+
+def test_attn_gqa_argument_checks():
+    q = (128, 1, 128 * 256)
+    def st(batch=4, kv_group=2):
+        return _status(asl.attn_fwd_run_gqa, 16, 32, 48, 64, batch, kv_group, 256, 256, 128, 128, q, q, q, q, 0.1,
+                       asl.AS_BF16, asl.AS_BF16, 0)
+    assert st(kv_group=0) == asl.AS_ERR_INVALID
+    assert st(kv_group=-2) == asl.AS_ERR_INVALID
+    assert st(batch=6, kv_group=4) == asl.AS_ERR_INVALID     # must divide batch

@@ -352,3 +352,48 @@ def test_one_key_value_head_shared_by_all_slices():
         ref, TO = oracle.attention(bits(Q), bits(K1), bits(V1), b, Lq, Lk, d, d, (d, 1, Lq * d), (d, 1, 0),
                                    (d, 1, 0), 0.1)
         assert oracle.check_attention(got, ref, TO)[0] == 0
+
+
+GQA = [  # (batch, kv_group, Lq, Lk, d)
+    (8, 4, 300, 300, 128),
+    (16, 8, 256, 384, 64),
+    (6, 3, 129, 200, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("items", [256, 128])
+@pytest.mark.parametrize("b,g,Lq,Lk,d", GQA)
+def test_grouped_key_value_heads(b, g, Lq, Lk, d, items, causal):
+    # the grouped launch equals the ungrouped one on materialised repeats bit
+    # for bit (each item's arithmetic is the same), and the exact pin holds
+    _say("attn gqa b=%d g=%d Lq=%d Lk=%d d=%d items=%d causal=%d" % (b, g, Lq, Lk, d, items, causal))
+    Q = _sparse_q(b, Lq, d, 1010 + Lq)
+    K = draw((b // g, Lk, d), "int", -1, 1, 1011 + Lk)
+    V = draw((b // g, Lk, d), "int", -4, 4, 1012 + d)
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    Ob = torch.full((b, Lq, d), float("nan"), dtype=torch.float32, device=DEV)
+    flags = (asl.AS_ATTN_CAUSAL if causal else 0) | ITEMS[items]
+    asl.attn_fwd_run_gqa(Qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), Ob.data_ptr(), b, g, Lq, Lk, d, d,
+                         (d, 1, Lq * d), (d, 1, Lk * d), (d, 1, Lk * d), (d, 1, Lq * d), math.log(2.0),
+                         asl.AS_BF16, asl.AS_F32, flags=flags, stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = Ob.double().cpu().numpy()
+    rep, _ = _run(Q, K.repeat_interleave(g, dim=0).contiguous(), V.repeat_interleave(g, dim=0).contiguous(),
+                  math.log(2.0), out="f32", causal=causal, items=items)
+    assert np.array_equal(got, rep)
+    ref, TO = oracle.attention(bits(Q), bits(K), bits(V), b, Lq, Lk, d, d, (d, 1, Lq * d), (d, 1, Lk * d),
+                               (d, 1, Lk * d), math.log(2.0), causal=causal, kv_group=g)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -18 * TO)
+
+
+def test_attention_helper_with_grouped_heads():
+    b, g, L, d = 8, 4, 256, 128
+    Q = draw((b, L, d), "normal", 0, 1, 1020).to(DEV)
+    K = draw((b // g, L, d), "normal", 0, 1, 1021).to(DEV)
+    V = draw((b // g, L, d), "normal", 0, 1, 1022).to(DEV)
+    O = asl.attention(Q, K, V, causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, TO = oracle.attention(bits(Q.cpu()), bits(K.cpu()), bits(V.cpu()), b, L, L, d, d, (d, 1, L * d),
+                               (d, 1, L * d), (d, 1, L * d), d ** -0.5, causal=True, kv_group=g)
+    assert oracle.check_attention(O.double().cpu().numpy(), ref, TO)[0] == 0

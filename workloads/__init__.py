@@ -125,6 +125,7 @@ class AttnWorkload:
     out: str                      # "f32" or "bf16"
     description: str
     causal: bool = False          # query i sees keys j <= i + Lk - Lq only
+    kv_group: int = 1             # query slice b reads K/V slice b // kv_group
 
     @property
     def flop(self) -> float:
@@ -142,8 +143,12 @@ class AttnWorkload:
                 (self.dv, 1, self.Lk * self.dv), (self.dv, 1, self.Lq * self.dv))
 
     @property
+    def kv_batch(self) -> int:
+        return self.batch // self.kv_group
+
+    @property
     def bytes_in(self) -> int:
-        return 2 * self.batch * (self.Lq * self.d + self.Lk * self.d + self.Lk * self.dv)
+        return 2 * (self.batch * self.Lq * self.d + self.kv_batch * (self.Lk * self.d + self.Lk * self.dv))
 
     @property
     def bytes_out(self) -> int:
@@ -160,14 +165,18 @@ ATTN_WORKLOADS: Dict[str, AttnWorkload] = {
         "attn32x2048_causal", 32, 2048, 2048, 128, 128, "normal", 0.0, 1.0, (201, 202, 203), 128 ** -0.5, "bf16",
         "causal attention forward (query i sees keys 0..i), 32 slices of Q,K,V [2048,128], N(0,1), bf16 O",
         causal=True),
+    "attn32x2048_gqa8_causal": AttnWorkload(
+        "attn32x2048_gqa8_causal", 32, 2048, 2048, 128, 128, "normal", 0.0, 1.0, (201, 202, 203), 128 ** -0.5,
+        "bf16", "causal attention forward with grouped key/value heads: 32 query slices [2048,128] over 4 K,V "
+        "slices (8 query slices per K,V), N(0,1), bf16 O", causal=True, kv_group=8),
 }
 
 
 def attn_operands(w: AttnWorkload):
     """(Q, K, V) bf16 CPU tensors [batch, L, d] for attention workload ``w``."""
     Q = draw((w.batch, w.Lq, w.d), w.dist, w.lo, w.hi, w.seeds[0])
-    K = draw((w.batch, w.Lk, w.d), w.dist, w.lo, w.hi, w.seeds[1])
-    V = draw((w.batch, w.Lk, w.dv), w.dist, w.lo, w.hi, w.seeds[2])
+    K = draw((w.kv_batch, w.Lk, w.d), w.dist, w.lo, w.hi, w.seeds[1])
+    V = draw((w.kv_batch, w.Lk, w.dv), w.dist, w.lo, w.hi, w.seeds[2])
     return Q, K, V
 
 
