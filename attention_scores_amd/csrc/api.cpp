@@ -205,7 +205,7 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         }
     }
     // As many workgroups as stay resident (one per CU for the 256 tile's
-    // 145 KiB of LDS, two for the 128 tile), each walking its XCD's tiles
+    // 146 KiB of LDS, two for the 128 tile's 73 KiB), each walking its XCD's tiles
     // with the LDS ring streaming across tile boundaries, so one tile's
     // stores drain while the next tile computes; or, for the ablation, one
     // workgroup per tile.

@@ -1,8 +1,9 @@
 // gemm.hip -- bf16 GEMM / attention-score kernels for gfx950 (MI355X).
 //
-// C[b] = A[b].B[b] with fp32 accumulation, one square output tile (256x256 or
-// 128x128) per workgroup of 4 waves laid out 2x2; each wave owns a
-// (TILE/2)x(TILE/2) block of 32x32 MFMA tiles.  The pages compute the same
+// C[b] = A[b].B[b] with fp32 accumulation, one square output tile per
+// workgroup: 256x256 with 8 waves laid out 2x4 (each wave a 128x64 block of
+// 32x32 MFMA tiles, two waves per SIMD), or 128x128 with 4 waves laid out
+// 2x2 (64x64 each).  The pages compute the same
 // contraction with shared operand tiles fanned out to several consumers
 // (lesson 07 "Clusters, distributed shared memory & cluster launch control",
 // sections "Two CTAs, one MMA" and "TMA multicast"; "Hopper TMA Multicast"
@@ -156,40 +157,41 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, T
     for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
 }
 
-// Epilogue staging region of one wave: ROWS rows of the wave's quadrant as
+// Epilogue staging region of one wave: ROWS rows of the wave's block as
 // fp32 with a padded row stride (rows r and r+4 -- the two halves of one wave
 // write -- start 128 bytes apart modulo 256, so the writes are conflict
 // free).  A tile followed by another tile of the same workgroup stages 8 rows
 // at a time in a region past the LDS ring, so the next tile's stages can
 // stream in meanwhile; a workgroup's last tile stages 32 rows at a time in
 // the then idle ring (fewer LDS round trips per tile).
-template <int TILE, int ROWS>
+template <int WTN, int ROWS>
 struct EpiRegion {
-    static constexpr int kStride = (TILE / 2) * 4 + 32;
+    static constexpr int kStride = WTN * 4 + 32;
     static constexpr int kBytes = ROWS * kStride;
 };
 
-// Write a wave's (WT x WT) accumulator quadrant to C (row r0.., column c0..)
+// Write a wave's (WTM x WTN) accumulator block to C (row r0.., column c0..)
 // through its LDS region, ROWS rows at a time.  Element e of lane l of MFMA
 // tile (mi, ni) is row 32*mi + 8*(e/4) + 4*(l/32) + e%4, column 32*ni + l%32
-// of the quadrant: a lane holds 4 consecutive rows of one column, so direct
+// of the block: a lane holds 4 consecutive rows of one column, so direct
 // stores would write only 32 contiguous elements per row.  Staged, every row
-// goes out as contiguous 16-byte pieces: 512-byte (fp32) or 256-byte (bf16,
-// rounded to nearest even right before its store) runs.  The stores are
+// goes out as contiguous 16-byte pieces: WTN*4-byte (fp32) or WTN*2-byte
+// (bf16, rounded to nearest even right before its store) runs, whole
+// 128-byte lines for WTN >= 64.  The stores are
 // non-temporal: C is written once and not re-read, so it should not push A
 // and B out of L2.
 //
 // EDGE (a tile that extends past C): only rows < m_lim and columns < n_lim
-// of the quadrant (counted from r0, c0) are stored; a 16-byte piece that
+// of the block (counted from r0, c0) are stored; a 16-byte piece that
 // straddles column n_lim goes out element by element.
-template <int TILE, int ROWS, bool OUT_BF16, bool EDGE = false>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[TILE / 64][TILE / 64], char* region, void* Cv,
+template <int WTM, int WTN, int ROWS, bool OUT_BF16, bool EDGE = false>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[WTM / 32][WTN / 32], char* region, void* Cv,
                                          int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane,
                                          int64_t m_lim = 0, int64_t n_lim = 0) {
-    constexpr int WT = TILE / 2, TM = WT / 32, TN = WT / 32;
-    constexpr int STRIDE = EpiRegion<TILE, ROWS>::kStride;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int STRIDE = EpiRegion<WTN, ROWS>::kStride;
     constexpr int ELEMS = OUT_BF16 ? 8 : 4;          // elements per lane per store (16 bytes out)
-    constexpr int PPR = WT / ELEMS;                  // pieces per row
+    constexpr int PPR = WTN / ELEMS;                 // pieces per row
     constexpr int PIECES = ROWS * PPR;
     constexpr int H = 32 / ROWS;                     // chunks per MFMA row block
     static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "chunks are whole 8-row groups of a row block");
@@ -247,10 +249,10 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TILE / 64][TILE / 6
     }
 }
 
-// Global stores one wave issues in epilogue<TILE, ROWS, OUT_BF16>.
-template <int TILE, int ROWS, bool OUT_BF16>
+// Global stores one wave issues in epilogue<WTM, WTN, ROWS, OUT_BF16>.
+template <int WTM, int WTN, int ROWS, bool OUT_BF16>
 constexpr int epilogue_stores() {
-    return (TILE / 64) * (32 / ROWS) * (ROWS * (TILE / 2) / (OUT_BF16 ? 8 : 4)) / 64;
+    return (WTM / 32) * (32 / ROWS) * (ROWS * WTN / (OUT_BF16 ? 8 : 4)) / 64;
 }
 
 // Cursor over the stream of stages a workgroup loads: tile t (logical),
@@ -338,29 +340,31 @@ struct StageCursor {
 // resources then cover exactly the valid bytes, the last partial K stage
 // masks its K-contiguous chunks, and edge tiles use the predicated epilogue;
 // otherwise none of that code is compiled in.
-template <int TILE, int BK, int S, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED>
-__global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
-    constexpr int WT = TILE / 2;         // wave tile
-    constexpr int TM = WT / 32;          // MFMA tiles per wave along M
-    constexpr int TN = WT / 32;          // ... along N
+template <int TILE, int BK, int S, int WGM, int WGN, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
+    constexpr int NW = WGM * WGN;        // waves, WGM along M by WGN along N
+    constexpr int WTM = TILE / WGM;      // wave tile rows
+    constexpr int WTN = TILE / WGN;      // wave tile columns
+    constexpr int TM = WTM / 32;         // MFMA tiles per wave along M
+    constexpr int TN = WTN / 32;         // ... along N
     constexpr int NS = BK / 16;          // k16 substeps per stage
     static_assert(NS % 2 == 0, "fragment sets alternate; NS must be even");
-    using OpA = OperandTile<TILE, A_K, BK>;
-    using OpB = OperandTile<TILE, B_K, BK>;
+    using OpA = OperandTile<TILE, A_K, BK, NW>;
+    using OpB = OperandTile<TILE, B_K, BK, NW>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
-    constexpr int kEpiStores = epilogue_stores<TILE, 8, OUT_BF16>();
+    constexpr int kEpiStores = epilogue_stores<WTM, WTN, 8, OUT_BF16>();
     constexpr int kWaitAfterEpi = L * (S - 2) + kEpiStores < 63 ? L * (S - 2) + kEpiStores : 63;
-    using Epi8 = EpiRegion<TILE, 8>;
-    using Epi32 = EpiRegion<TILE, 32>;
-    static_assert(kWaves * Epi32::kBytes <= S * kStage, "last-tile epilogue must fit in the ring");
-    __shared__ __attribute__((aligned(1024))) char smem[S * kStage + kWaves * Epi8::kBytes];
+    using Epi8 = EpiRegion<WTN, 8>;
+    using Epi32 = EpiRegion<WTN, 32>;
+    static_assert(NW * Epi32::kBytes <= S * kStage, "last-tile epilogue must fit in the ring");
+    __shared__ __attribute__((aligned(1024))) char smem[S * kStage + NW * Epi8::kBytes];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int wm = w >> 1, wn = w & 1;
-    const int m0 = wm * WT, n0 = wn * WT;
+    const int wm = w / WGN, wn = w % WGN;
+    const int m0 = wm * WTM, n0 = wn * WTN;
     char* const epi = smem + S * kStage + w * Epi8::kBytes;
 
     // The logical tiles this workgroup visits: first, first + stride, ... < end.
@@ -436,7 +440,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
         logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
         const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
         const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
-        const int64_t m_lim = a.M - r0, n_lim = a.N - c0;   // rows / columns of the quadrant inside C
+        const int64_t m_lim = a.M - r0, n_lim = a.N - c0;   // rows / columns of the wave's block inside C
         const bool last = t + stride >= end;
         if (last) {
             // Last tile: only loads past the end (which fetch nothing but
@@ -452,11 +456,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
         int el = lane;
         if constexpr (RAGGED) asm volatile("" : "+v"(el));
         if (RAGGED && !full)
-            epilogue<TILE, 8, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
+            epilogue<WTM, WTN, 8, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
         else if (last)
-            epilogue<TILE, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+            epilogue<WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
         else
-            epilogue<TILE, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+            epilogue<WTM, WTN, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
         prev_full = full;
     }
 }
@@ -466,15 +470,30 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(KArgs a) {
 constexpr int kBK = 64;
 constexpr int kStages = 2;
 
+// Wave grid of a workgroup.  The 256 tile runs 2 x 4 waves of 128 x 64,
+// two waves per SIMD: while one waits on its fragment reads or the stage
+// barrier, the other's MFMAs keep the matrix unit busy (1 % faster at
+// 8192^3, 5 % on the 65536 x 256 x 4096 A stream than 2 x 2 waves of
+// 128 x 128, for 1.5x the LDS fragment reads per MFMA).  A 4 x 2 grid of
+// 64 x 128 waves does not fit: its epilogue rows are twice as long.  The
+// 128 tile keeps 2 x 2 waves of 64 x 64 (8 waves would leave 2 MFMAs per
+// k16 substep).
+template <int TILE>
+struct WaveGrid {
+    static constexpr int M = 2, N = TILE == 256 ? 4 : 2;
+};
+
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
 int launch_t(const GemmDesc& d, KArgs k, hipStream_t s) {
+    constexpr int WGM = WaveGrid<TILE>::M, WGN = WaveGrid<TILE>::N;
     k.ktiles = (int32_t)((d.K + kBK - 1) / kBK);
     k.krem = (int32_t)(d.K % kBK);
     const bool ragged = d.M % TILE || d.N % TILE || d.K % kBK;
+    const dim3 grid((unsigned)d.grid), block(64 * WGM * WGN);
     if (ragged)
-        gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16, true><<<dim3((unsigned)d.grid), dim3(kThreads), 0, s>>>(k);
+        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, true><<<grid, block, 0, s>>>(k);
     else
-        gemm_kernel<TILE, kBK, kStages, A_K, B_K, OUT_BF16, false><<<dim3((unsigned)d.grid), dim3(kThreads), 0, s>>>(k);
+        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, false><<<grid, block, 0, s>>>(k);
     return (int)hipGetLastError();
 }
 

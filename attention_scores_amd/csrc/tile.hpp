@@ -30,9 +30,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) i16x8 lds_i16x8_t;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
 
-constexpr int kWaves = 4;      // 2 x 2
-constexpr int kThreads = 64 * kWaves;
-
 // Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
 // no swizzle, offsets checked against num_records.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -80,7 +77,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 
 // One operand tile of R (M or N extent) x BK (K) bf16 per pipeline stage,
 // loaded by the NW waves of a workgroup.
-template <int R, bool KMAJ, int BK, int NW = kWaves>
+template <int R, bool KMAJ, int BK, int NW>
 struct OperandTile {
     static constexpr int kBytes = R * BK * 2;
     static constexpr int kCHR = BK / 8;                              // chunks per row (K-major)

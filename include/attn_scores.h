@@ -110,7 +110,7 @@ typedef struct as_gemm_plan* as_gemm_t;
  *   a_t, b_t     must be AS_BF16
  *   c_t          AS_F32, or AS_BF16 (round-to-nearest-even)
  *   flags        AS_FLAG_* bits
- * Chooses the output tile (256x256 or 128x128, 4 waves), the workgroup
+ * Chooses the output tile (256x256 with 8 waves or 128x128 with 4), the workgroup
  * grouping and the grid: by default as many workgroups as stay resident
  * (256 for the 256x256 tile, 512 for 128x128; fewer if there are fewer
  * tiles), each walking several tiles.  Makes no HIP call.
