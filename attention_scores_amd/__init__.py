@@ -29,6 +29,10 @@ AS_FLAG_TILE_128 = 0x2
 AS_FLAG_TILE_256 = 0x4
 AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
 AS_FLAG_NO_SPLIT_K = 0x10
+AS_FLAG_NT_A = 0x20
+AS_FLAG_NO_NT_A = 0x40
+AS_FLAG_ROTATE_K = 0x80
+AS_FLAG_NO_ROTATE_K = 0x100
 AS_ATTN_CAUSAL = 0x1
 AS_ATTN_QUERIES_256 = 0x2
 AS_ATTN_QUERIES_128 = 0x4

@@ -58,7 +58,8 @@ as_status ok() {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 |
-                                 AS_FLAG_ONE_TILE_PER_WORKGROUP | AS_FLAG_NO_SPLIT_K;
+                                 AS_FLAG_ONE_TILE_PER_WORKGROUP | AS_FLAG_NO_SPLIT_K | AS_FLAG_NT_A |
+                                 AS_FLAG_NO_NT_A | AS_FLAG_ROTATE_K | AS_FLAG_NO_ROTATE_K;
 constexpr int64_t kBK = asl::kTileK;
 constexpr int64_t kCus = 256;   // MI355X compute units
 constexpr int64_t kMinSplitK = 1024;   // shallowest K chunk of a split product
@@ -116,6 +117,10 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     if (flags & ~kKnownFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kKnownFlags);
     if ((flags & AS_FLAG_TILE_128) && (flags & AS_FLAG_TILE_256))
         return fail(AS_ERR_INVALID, "AS_FLAG_TILE_128 and AS_FLAG_TILE_256 are exclusive");
+    if ((flags & AS_FLAG_NT_A) && (flags & AS_FLAG_NO_NT_A))
+        return fail(AS_ERR_INVALID, "AS_FLAG_NT_A and AS_FLAG_NO_NT_A are exclusive");
+    if ((flags & AS_FLAG_ROTATE_K) && (flags & AS_FLAG_NO_ROTATE_K))
+        return fail(AS_ERR_INVALID, "AS_FLAG_ROTATE_K and AS_FLAG_NO_ROTATE_K are exclusive");
     for (as_dtype t : {a_t, b_t, c_t})
         if (t != AS_BF16 && t != AS_F32) return fail(AS_ERR_INVALID, "unknown dtype %d", (int)t);
     if (a_t != AS_BF16 || b_t != AS_BF16)
@@ -183,6 +188,16 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
     d.tiles = batch * d.tiles_m * d.tiles_n;
     d.grouped = !(flags & AS_FLAG_NO_GROUPING);
+    // With one tile column every A row panel has a single consumer: A
+    // streams from HBM once while every tile re-reads all of B.  A's loads
+    // then carry the non-temporal hint (its lines leave L2 before B's), and
+    // the K loop is rotated: otherwise all running workgroups read the same
+    // 128-byte column block of every A row at once (rows 2*K bytes apart),
+    // an access pattern that HBM serves at about 4.4 TB/s against 6.1 TB/s
+    // for rotated columns.
+    const bool streams_a = d.tiles_n == 1;
+    d.nt_a = (flags & AS_FLAG_NT_A) ? true : (flags & AS_FLAG_NO_NT_A) ? false : streams_a;
+    d.rotate_k = (flags & AS_FLAG_ROTATE_K) ? true : (flags & AS_FLAG_NO_ROTATE_K) ? false : streams_a;
     // Split K when the output tiles leave CUs idle (fewer tiles than CUs):
     // into 2, 4, 8 or 16 chunks, each a multiple of the K stage and at least
     // kMinSplitK deep, as many as keep tiles x chunks within the resident

@@ -59,6 +59,7 @@ struct KArgs {
     int32_t ktiles;       // ceil(K / BK) stages per tile
     int32_t krem;         // K mod BK: valid k of the last stage (0: the last stage is full)
     int32_t tiles, tiles_m, tiles_n, group_m, grouped;
+    int32_t rotate;       // tile row tm starts its K loop at stage tm mod ktiles
 };
 
 // Per-lane source offsets of a wave's stage loads.  For the last, partial K
@@ -80,7 +81,7 @@ struct LaneOffsets {
 // dead stage (past the workgroup's last tile) they cover nothing: the loads
 // fetch nothing and only keep the per-stage load count uniform.  `klim` is
 // the stage's valid k (BK except in a partial last stage).
-template <class OpA, class OpB, bool RAGGED>
+template <class OpA, class OpB, bool RAGGED, bool NT_A>
 struct StageLoads {
     static constexpr int kCount = OpA::kLoadsPerWave + OpB::kLoadsPerWave;
     static_assert(OpA::kLoadsPerWave % 2 == 0 && OpB::kLoadsPerWave % 2 == 0,
@@ -102,7 +103,8 @@ struct StageLoads {
         if (i < OpA::kLoadsPerWave) {
             uint32_t v = o.a[i];
             if constexpr (RAGGED && OpA::kKMaj) v = o.akc[i & 1] < klim ? v : kOob;
-            lds_dma16(ra, v, sa + i * 1024);
+            if constexpr (NT_A) lds_dma16_nt(ra, v, sa + i * 1024);
+            else lds_dma16(ra, v, sa + i * 1024);
         } else {
             const int j = i - OpA::kLoadsPerWave;
             uint32_t v = o.b[j];
@@ -132,13 +134,13 @@ __device__ __forceinline__ void read_unit(Frags<TM, TN>& f, int u, const char* s
 // stage per MFMA.  Scheduling barriers keep that order, so every MFMA has
 // independent work issued next to it and the LDS sees a steady stream of
 // requests rather than bursts.
-template <class OpA, class OpB, int TM, int TN, bool LOADS, bool RAGGED>
+template <class OpA, class OpB, int TM, int TN, bool LOADS, bool RAGGED, bool NT_A>
 __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, TN>& f, Frags<TM, TN>& g,
                                         const char* rd, int j, int m0, int n0, int lane,
-                                        const StageLoads<OpA, OpB, RAGGED>& ld, const LaneOffsets<OpA, OpB>& off) {
+                                        const StageLoads<OpA, OpB, RAGGED, NT_A>& ld, const LaneOffsets<OpA, OpB>& off) {
     constexpr int kMfma = TM * TN;
     constexpr int kUnits = TM + TN;
-    constexpr int kLoads = StageLoads<OpA, OpB, RAGGED>::kCount;
+    constexpr int kLoads = StageLoads<OpA, OpB, RAGGED, NT_A>::kCount;
 #pragma unroll
     for (int t = 0; t < kMfma; ++t) {
         const int mi = t / TN, ni = t % TN;
@@ -260,7 +262,7 @@ constexpr int epilogue_stores() {
 template <int TILE, int BK, bool A_K, bool B_K, bool RAGGED>
 struct StageCursor {
     const KArgs& a;
-    int t, k, stride, end;
+    int t, k, ks, stride, end;   // tile, stages of it so far, the stage's K index
     int tm, tn;
     int64_t a_step, b_step;
     const uint16_t *pa, *pb;
@@ -275,14 +277,21 @@ struct StageCursor {
     __device__ void origins() {
         int bb;
         logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
-        pa = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE);
-        pb = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE);
+        ks = a.rotate ? tm % a.ktiles : 0;
+        pa = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE) + ks * a_step;
+        pb = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE) + ks * b_step;
     }
+    // Stages of a tile run ks, ks+1, ..., ktiles-1, 0, ..., ks-1 (rotated
+    // start; without rotation ks starts at 0 and never wraps).
     __device__ void advance() {
         if (++k == a.ktiles) {
             k = 0;
             t += stride;
             if (t < end) origins();
+        } else if (++ks == a.ktiles) {
+            ks = 0;
+            pa -= (int64_t)(a.ktiles - 1) * a_step;
+            pb -= (int64_t)(a.ktiles - 1) * b_step;
         } else {
             pa += a_step;
             pb += b_step;
@@ -302,17 +311,17 @@ struct StageCursor {
     __device__ int a_bytes() const {
         if (!live()) return 0;
         if constexpr (!RAGGED) return 0x7fffffff;
-        const int64_t mr = a.M - (int64_t)tm * TILE, kr = a.K - (int64_t)k * BK;
+        const int64_t mr = a.M - (int64_t)tm * TILE, kr = a.K - (int64_t)ks * BK;
         return A_K ? extent(mr, kr, a.a_ld) : extent(kr, mr, a.a_ld);
     }
     __device__ int b_bytes() const {
         if (!live()) return 0;
         if constexpr (!RAGGED) return 0x7fffffff;
-        const int64_t nr = a.N - (int64_t)tn * TILE, kr = a.K - (int64_t)k * BK;
+        const int64_t nr = a.N - (int64_t)tn * TILE, kr = a.K - (int64_t)ks * BK;
         return B_K ? extent(nr, kr, a.b_ld) : extent(kr, nr, a.b_ld);
     }
     // Valid k of the stage: BK, or K mod BK in a partial last stage.
-    __device__ int klim() const { return (a.krem != 0 && k == a.ktiles - 1) ? a.krem : BK; }
+    __device__ int klim() const { return (a.krem != 0 && ks == a.ktiles - 1) ? a.krem : BK; }
 };
 
 // Pipeline (S LDS buffers; a stage is BK deep in K, NS = BK/16 MFMA
@@ -336,11 +345,14 @@ struct StageCursor {
 // the same number of loads (stages past the end fetch nothing), so the wait
 // count is a constant.
 //
+// NT_A (an A that streams from HBM, e.g. one tile column): A's loads carry
+// the non-temporal hint, so its lines leave L2 first and B stays resident.
+//
 // RAGGED: M or N is not a multiple of TILE or K not of BK.  The stage
 // resources then cover exactly the valid bytes, the last partial K stage
 // masks its K-contiguous chunks, and edge tiles use the predicated epilogue;
 // otherwise none of that code is compiled in.
-template <int TILE, int BK, int S, int WGM, int WGN, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED>
+template <int TILE, int BK, int S, int WGM, int WGN, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED, bool NT_A>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int NW = WGM * WGN;        // waves, WGM along M by WGN along N
     constexpr int WTM = TILE / WGM;      // wave tile rows
@@ -354,8 +366,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
+    constexpr int kWaitStage = L * (S - 2);                       // loads issued after the awaited stage's
     constexpr int kEpiStores = epilogue_stores<WTM, WTN, 8, OUT_BF16>();
-    constexpr int kWaitAfterEpi = L * (S - 2) + kEpiStores < 63 ? L * (S - 2) + kEpiStores : 63;
+    constexpr int kWaitAfterEpi = kWaitStage + kEpiStores < 63 ? kWaitStage + kEpiStores : 63;
     using Epi8 = EpiRegion<WTN, 8>;
     using Epi32 = EpiRegion<WTN, 32>;
     static_assert(NW * Epi32::kBytes <= S * kStage, "last-tile epilogue must fit in the ring");
@@ -385,7 +398,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     }
 
     const int KT = a.ktiles;
-    StageLoads<OpA, OpB, RAGGED> ld;
+    StageLoads<OpA, OpB, RAGGED, NT_A> ld;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim());
@@ -414,7 +427,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
             const int nxt = (cur + 1 == S) ? 0 : cur + 1;
 #pragma unroll
             for (int j = 0; j + 1 < NS; ++j)
-                substep<OpA, OpB, TM, TN, false, RAGGED>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, off);
+                substep<OpA, OpB, TM, TN, false, RAGGED, NT_A>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, off);
             // the next stage landed everywhere; nobody reads buffer `cur` any more
             __builtin_amdgcn_sched_barrier(0);
             if (kt == 0 && t != first && (!RAGGED || prev_full)) {
@@ -424,12 +437,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
                 // order, so they may stay in flight.
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWaitAfterEpi, 0));
             } else {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 2), 0));
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWaitStage, 0));
             }
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim());
-            substep<OpA, OpB, TM, TN, true, RAGGED>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
+            substep<OpA, OpB, TM, TN, true, RAGGED, NT_A>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
                                             off);
             __builtin_amdgcn_sched_barrier(0);
             cur_ld.advance();
@@ -483,17 +496,23 @@ struct WaveGrid {
     static constexpr int M = 2, N = TILE == 256 ? 4 : 2;
 };
 
-template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
-int launch_t(const GemmDesc& d, KArgs k, hipStream_t s) {
+template <int TILE, bool A_K, bool B_K, bool OUT_BF16, bool NT_A>
+void launch_nt(const GemmDesc& d, const KArgs& k, hipStream_t s) {
     constexpr int WGM = WaveGrid<TILE>::M, WGN = WaveGrid<TILE>::N;
-    k.ktiles = (int32_t)((d.K + kBK - 1) / kBK);
-    k.krem = (int32_t)(d.K % kBK);
     const bool ragged = d.M % TILE || d.N % TILE || d.K % kBK;
     const dim3 grid((unsigned)d.grid), block(64 * WGM * WGN);
     if (ragged)
-        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, true><<<grid, block, 0, s>>>(k);
+        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, true, NT_A><<<grid, block, 0, s>>>(k);
     else
-        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, false><<<grid, block, 0, s>>>(k);
+        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, false, NT_A><<<grid, block, 0, s>>>(k);
+}
+
+template <int TILE, bool A_K, bool B_K, bool OUT_BF16>
+int launch_t(const GemmDesc& d, KArgs k, hipStream_t s) {
+    k.ktiles = (int32_t)((d.K + kBK - 1) / kBK);
+    k.krem = (int32_t)(d.K % kBK);
+    if (d.nt_a) launch_nt<TILE, A_K, B_K, OUT_BF16, true>(d, k, s);
+    else launch_nt<TILE, A_K, B_K, OUT_BF16, false>(d, k, s);
     return (int)hipGetLastError();
 }
 
@@ -545,6 +564,7 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
     k.tiles_n = (int32_t)d.tiles_n;
     k.group_m = d.group_m;
     k.grouped = d.grouped ? 1 : 0;
+    k.rotate = d.rotate_k ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
     if (d.tile == 256) return launch_tile<256>(d, k, s);
     return launch_tile<128>(d, k, s);

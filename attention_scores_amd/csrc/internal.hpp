@@ -21,6 +21,8 @@ struct GemmDesc {
     int tile;                        // 256 or 128 (square output tile)
     int group_m;                     // rows of tiles per group in the grouped order
     bool grouped;                    // XCD-aware grouped order (false: identity)
+    bool nt_a;                       // A's loads carry the non-temporal hint (A streams)
+    bool rotate_k;                   // tile row tm starts its K loop at stage tm mod (K stages)
     int64_t tiles_m, tiles_n, tiles; // output tiles
     int64_t grid;                    // workgroups launched (tiles, or fewer: persistent)
     // Split K (batch 1 only): the product runs as `splits` products over

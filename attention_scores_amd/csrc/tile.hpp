@@ -163,6 +163,14 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
                  : "memory");
 }
 
+// The same load with the non-temporal hint: lines of an operand that is
+// read once (streamed) are the first that L2 evicts, so they do not push out
+// operands that other workgroups re-read.
+__device__ __forceinline__ void lds_dma16_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+                 : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }

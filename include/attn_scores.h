@@ -95,6 +95,12 @@ typedef struct {
 #define AS_FLAG_ONE_TILE_PER_WORKGROUP 0x8u  /* ablation: one workgroup per output tile instead of a resident
                                                * (persistent) grid whose workgroups walk several tiles */
 #define AS_FLAG_NO_SPLIT_K  0x10u /* never split K over workgroups (no workspace) */
+#define AS_FLAG_NT_A        0x20u /* load A with the non-temporal hint (the default when every A row panel
+                                   * feeds a single output tile) */
+#define AS_FLAG_NO_NT_A     0x40u /* ablation: ordinary loads for A */
+#define AS_FLAG_ROTATE_K    0x80u /* tile row tm starts its K loop at K stage tm mod (K / 64): concurrent tiles read
+                                   * different K columns (the default when every A row panel feeds a single tile) */
+#define AS_FLAG_NO_ROTATE_K 0x100u /* ablation: every tile walks K from 0 */
 
 typedef struct as_gemm_plan* as_gemm_t;
 
@@ -125,6 +131,15 @@ typedef struct as_gemm_plan* as_gemm_t;
  * gemm_run on a device and frees in gemm_destroy; runs of one plan share it,
  * so they must not overlap (the same stream, or ordered streams).
  * AS_FLAG_NO_SPLIT_K turns splitting off.
+ * Streaming A: when N fits one output tile, each A row panel is read by one
+ * workgroup only and streams from HBM.  The plan then (1) loads A with the
+ * non-temporal hint, so its lines leave L2 before B's, which every tile
+ * re-reads, and (2) rotates the K loop: tile row tm accumulates its K
+ * stages starting at stage tm mod (K / 64), so the workgroups running at
+ * one time read different K columns of A instead of one column block of
+ * every row.  Rotation changes only the order of the fp32 accumulation.
+ * AS_FLAG_NT_A / AS_FLAG_NO_NT_A and AS_FLAG_ROTATE_K / AS_FLAG_NO_ROTATE_K
+ * override the two choices; each pair is exclusive.
  */
 AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t batch,
                       as_strides a, as_strides b, as_strides c,

@@ -60,9 +60,13 @@ def test_create_rejects_bad_sizes(M, N, K, batch):
 
 def test_create_rejects_bad_flags_and_dtypes():
     args = (512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512))
-    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, asl.AS_F32, 0x100) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, asl.AS_F32, 0x1000) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, asl.AS_F32,
                    asl.AS_FLAG_TILE_128 | asl.AS_FLAG_TILE_256) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, asl.AS_F32,
+                   asl.AS_FLAG_NT_A | asl.AS_FLAG_NO_NT_A) == asl.AS_ERR_INVALID
+    assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, asl.AS_F32,
+                   asl.AS_FLAG_ROTATE_K | asl.AS_FLAG_NO_ROTATE_K) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_BF16, 7, 0) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_create, *args, asl.AS_F32, asl.AS_BF16, asl.AS_F32, 0) == asl.AS_ERR_UNSUPPORTED
     assert _status(asl.gemm_create, *args, asl.AS_BF16, asl.AS_F32, asl.AS_F32, 0) == asl.AS_ERR_UNSUPPORTED

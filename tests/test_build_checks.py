@@ -47,7 +47,7 @@ def test_every_lds_dma_load_follows_its_wait_states(src, asm):
     lines = asm(src)
     loads = 0
     for n, line in enumerate(lines):
-        if not re.match(r"\s+buffer_load_dwordx4 .* lds\s*$", line):
+        if not re.match(r"\s+buffer_load_dword(x4)? .* lds\s*$", line):
             continue
         loads += 1
         k = n - 1

@@ -522,3 +522,63 @@ def test_ragged_attention_scores():
     got = S.cpu().numpy()
     assert np.array_equal(got[:, :, :Lk].astype(np.float64), Sref)
     assert np.all(np.isnan(got[:, :, Lk:]))
+
+
+# ------------------------------------------ non-temporal A loads (A streams) --
+
+NT_A = [  # (M, N, K, batch, flags, a_k, b_k), run with the non-temporal hint on A forced on
+    (1024, 256, 1024, 1, asl.AS_FLAG_TILE_256, True, False),     # one tile column (the default choice)
+    (1024, 512, 576, 2, asl.AS_FLAG_TILE_256, False, True),      # two tile columns, column-major A, batch
+    (300, 200, 200, 1, asl.AS_FLAG_TILE_128, True, True),        # ragged, partial last stage
+    (512, 256, 8192, 1, asl.AS_FLAG_TILE_256, True, False),      # 2 tiles: split into 8 K chunks
+]
+
+
+@pytest.mark.parametrize("M,N,K,batch,flags,a_k,b_k", NT_A)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_nontemporal_a_bit_exact(M, N, K, batch, flags, a_k, b_k, out):
+    """The hint changes only what L2 keeps: integer data give the oracle's
+    result bit for bit, and nothing outside C is written."""
+    _say("nt_a M=%d N=%d K=%d batch=%d flags=0x%x a_k=%s b_k=%s out=%s" % (M, N, K, batch, flags, a_k, b_k, out))
+    _ragged(M, N, K, batch, a_k, b_k, out, flags | asl.AS_FLAG_NT_A | asl.AS_FLAG_NO_ROTATE_K, 4100 + M + K)
+
+
+# ----------------------------------------------- rotated K loop (A streams) --
+
+ROTATE = [  # (M, N, K, batch, flags, a_k, b_k), run with the K rotation forced on
+    (1024, 256, 1024, 1, asl.AS_FLAG_TILE_256, True, False),     # 4 tile rows start at stages 0..3 of 16
+    (300, 200, 200, 1, asl.AS_FLAG_TILE_128, True, True),        # the partial stage (8 deep) mid-sequence
+    (257, 260, 136, 1, asl.AS_FLAG_TILE_256, False, False),      # column-major A, partial stage
+    (512, 256, 8192, 1, asl.AS_FLAG_TILE_256, True, False),      # split into 8 chunks: rotation inside each
+    (384, 384, 200, 64, asl.AS_FLAG_TILE_128 | asl.AS_FLAG_NT_A, True, False),  # 576 tiles walked
+]
+
+
+@pytest.mark.parametrize("M,N,K,batch,flags,a_k,b_k", ROTATE)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_rotated_k_bit_exact(M, N, K, batch, flags, a_k, b_k, out):
+    """Each tile accumulates every K stage exactly once whatever stage it
+    starts at: integer data give the oracle's result bit for bit."""
+    _say("rotate M=%d N=%d K=%d batch=%d flags=0x%x a_k=%s b_k=%s out=%s" % (M, N, K, batch, flags, a_k, b_k, out))
+    _ragged(M, N, K, batch, a_k, b_k, out, flags | asl.AS_FLAG_ROTATE_K, 5200 + M + K)
+
+
+def test_rotated_k_random_data_within_tolerance_and_deterministic():
+    """The tall-skinny shape at reduced height with N(0,1) data: the default
+    plan (rotated, non-temporal A) and the unrotated ablation are both within
+    tolerance of the oracle, and the default plan repeats bit for bit."""
+    M, N, K = 4096, 256, 4096
+    A = draw((1, M, K), "normal", 0, 1, 411)
+    B = draw((1, K, N), "normal", 0, 1, 412)
+    sa, sb = (K, 1, M * K), (N, 1, K * N)
+    pts = sample_points(1, M, N, 768, 78)
+    Cref, T = oracle.gemm_points(bits(A), bits(B), pts, K, sa, sb, dims=(1, M, N))
+    runs = []
+    for flags in (0, 0, asl.AS_FLAG_NO_ROTATE_K):
+        _say("rotate tolerance flags=0x%x" % flags)
+        C = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, flags)
+        got = C.double().cpu().numpy()[0][pts[:, 1], pts[:, 2]]
+        nfail, util = oracle.check(got, Cref, T)
+        assert nfail == 0, "flags 0x%x: %d sampled elements outside tolerance (max util %.3g)" % (flags, nfail, util)
+        runs.append(C)
+    assert torch.equal(runs[0].view(torch.int32), runs[1].view(torch.int32))
