@@ -2,16 +2,16 @@
 //
 // C[b] = A[b].B[b] with fp32 accumulation, one square output tile per
 // workgroup: 256x256 with 8 waves laid out 2x4 (each wave a 128x64 block of
-// 32x32 MFMA tiles, two waves per SIMD), or 128x128 with 4 waves laid out
-// 2x2 (64x64 each).  The pages compute the same
+// 16x16 MFMA tiles, two waves per SIMD), or 128x128 with 4 waves laid out
+// 2x2 (64x64 blocks of 32x32 MFMA tiles); WaveGrid below.  The pages compute the same
 // contraction with shared operand tiles fanned out to several consumers
 // (lesson 07 "Clusters, distributed shared memory & cluster launch control",
 // sections "Two CTAs, one MMA" and "TMA multicast"; "Hopper TMA Multicast"
 // deep-dive, Attention/GEMM reuse use-case, S_i = Q_i K^T).  On gfx950 the
 // reuse comes from the workgroup->tile map in schedule.hpp (consumers of a
 // panel co-run on one XCD and share its L2) and, inside a workgroup, from
-// the large output tile: every A element staged in LDS feeds TILE/32 MFMA
-// columns and every B element TILE/32 MFMA rows.
+// the large output tile: every A element staged in LDS feeds the MFMA
+// columns of a whole wave tile and every B element its MFMA rows.
 //
 // Data path of one K step (BK = 64):
 //   global -> LDS   buffer_load_dwordx4 ... lds (no registers in between),
@@ -23,7 +23,8 @@
 //                   row per lane); MN-contiguous operands: two
 //                   ds_read_b64_tr_b16, which transpose 4x16 blocks on the way
 //                   out of LDS so each lane still receives 8 consecutive k.
-//   MFMA            v_mfma_f32_32x32x16_bf16, fp32 accumulators.
+//   MFMA            v_mfma_f32_16x16x32_bf16 (256 tile) or
+//                   v_mfma_f32_32x32x16_bf16 (128 tile), fp32 accumulators.
 //   epilogue        fp32 stores, or round-to-nearest-even to bf16.
 //
 // Lane maps and the operand tile's LDS layout: tile.hpp.
@@ -120,22 +121,48 @@ struct Frags {
     bf16x8 b[TN];
 };
 
+// The MFMA of an MI x MI output block: 32x32x16 (16 fp32 results per lane)
+// or 16x16x32 (4 per lane), both bf16 in, fp32 accumulate.
+template <int MI>
+struct Mfma;
+template <>
+struct Mfma<32> {
+    using Acc = f32x16;
+    static constexpr int kK = 16;        // k per instruction
+    static __device__ __forceinline__ Acc run(bf16x8 a, bf16x8 b, Acc c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<16> {
+    using Acc = f32x4;
+    static constexpr int kK = 32;
+    static __device__ __forceinline__ Acc run(bf16x8 a, bf16x8 b, Acc c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
 // Fragment unit u of a substep: u < TM is A tile u, else B tile u - TM.
-template <class OpA, class OpB, int TM, int TN>
+template <class OpA, class OpB, int MI, int TM, int TN>
 __device__ __forceinline__ void read_unit(Frags<TM, TN>& f, int u, const char* stage, int j, int m0, int n0,
                                           int lane) {
-    if (u < TM) f.a[u] = OpA::frag(stage, m0 + 32 * u, j, lane);
-    else f.b[u - TM] = OpB::frag(stage + OpA::kBytes, n0 + 32 * (u - TM), j, lane);
+    if constexpr (MI == 32) {
+        if (u < TM) f.a[u] = OpA::frag(stage, m0 + 32 * u, j, lane);
+        else f.b[u - TM] = OpB::frag(stage + OpA::kBytes, n0 + 32 * (u - TM), j, lane);
+    } else {
+        if (u < TM) f.a[u] = OpA::frag16(stage, m0 + 16 * u, j, lane);
+        else f.b[u - TM] = OpB::frag16(stage + OpA::kBytes, n0 + 16 * (u - TM), j, lane);
+    }
 }
 
-// One k16 substep: TM*TN MFMAs on fragments `f`; woven between them, one
+// One substep (the k of one MFMA): TM*TN MFMAs on fragments `f`; woven between them, one
 // fragment unit of the next set `g` (stage `rd`, substep `j`) per MFMA and,
 // when `LOADS` is set, one of this wave's global -> LDS loads of a future
 // stage per MFMA.  Scheduling barriers keep that order, so every MFMA has
 // independent work issued next to it and the LDS sees a steady stream of
 // requests rather than bursts.
-template <class OpA, class OpB, int TM, int TN, bool LOADS, bool RAGGED, bool NT_A>
-__device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, TN>& f, Frags<TM, TN>& g,
+template <class OpA, class OpB, int MI, int TM, int TN, bool LOADS, bool RAGGED, bool NT_A>
+__device__ __forceinline__ void substep(typename Mfma<MI>::Acc (&acc)[TM][TN], const Frags<TM, TN>& f, Frags<TM, TN>& g,
                                         const char* rd, int j, int m0, int n0, int lane,
                                         const StageLoads<OpA, OpB, RAGGED, NT_A>& ld, const LaneOffsets<OpA, OpB>& off) {
     constexpr int kMfma = TM * TN;
@@ -144,11 +171,11 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, T
 #pragma unroll
     for (int t = 0; t < kMfma; ++t) {
         const int mi = t / TN, ni = t % TN;
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = Mfma<MI>::run(f.a[mi], f.b[ni], acc[mi][ni]);
         if constexpr (LOADS) {
             if (t < kLoads) ld.issue(t, off);
         }
-        if (t < kUnits) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
+        if (t < kUnits) read_unit<OpA, OpB, MI>(g, t, rd, j, m0, n0, lane);
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (LOADS) {
@@ -156,7 +183,46 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[TM][TN], const Frags<TM, T
         for (int t = kMfma; t < kLoads; ++t) ld.issue(t, off);
     }
 #pragma unroll
-    for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
+    for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB, MI>(g, t, rd, j, m0, n0, lane);
+}
+
+// Fragments of the 16x16x32 path.  A row block's fragment is replaced by
+// the next substep's right after the row's MFMAs have issued (one set of A
+// fragments); B has two sets, the one in use and the next.  With 16 units
+// per substep in a 128x128 wave tile, two full sets of both would not fit
+// next to the 256 accumulators.
+template <int TM, int TN>
+struct Frags16 {
+    bf16x8 a[TM];
+    bf16x8 b[2][TN];
+};
+
+// One k32 substep of the 16x16x32 path: TM*TN MFMAs row block by row block
+// on B set P; woven between them, the next substep's B unit u at the first
+// MFMA of row u (into set 1-P), the next A fragment of row mi at the second
+// MFMA of row mi+1 (the last row's after the loop), and, when `LOADS` is
+// set, this wave's global -> LDS loads of a future stage, evenly spread.
+template <class OpA, class OpB, int TM, int TN, int P, bool LOADS, bool RAGGED, bool NT_A>
+__device__ __forceinline__ void substep16(f32x4 (&acc)[TM][TN], Frags16<TM, TN>& f, const char* rd, int j, int m0,
+                                          int n0, int lane, const StageLoads<OpA, OpB, RAGGED, NT_A>& ld,
+                                          const LaneOffsets<OpA, OpB>& off) {
+    constexpr int kMfma = TM * TN;
+    constexpr int kLoads = StageLoads<OpA, OpB, RAGGED, NT_A>::kCount;
+    static_assert(TN <= TM && TN >= 2, "B units ride on the first MFMA of a row, A on the second");
+    static_assert(kLoads <= kMfma, "at most one load per MFMA");
+    constexpr int kEvery = kMfma / kLoads;
+#pragma unroll
+    for (int t = 0; t < kMfma; ++t) {
+        const int mi = t / TN, ni = t % TN;
+        acc[mi][ni] = Mfma<16>::run(f.a[mi], f.b[P][ni], acc[mi][ni]);
+        if constexpr (LOADS) {
+            if (t % kEvery == kEvery - 1) ld.issue(t / kEvery, off);
+        }
+        if (ni == 0 && mi < TN) f.b[1 - P][mi] = OpB::frag16(rd + OpA::kBytes, n0 + 16 * mi, j, lane);
+        if (ni == 1 && mi > 0) f.a[mi - 1] = OpA::frag16(rd, m0 + 16 * (mi - 1), j, lane);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    f.a[TM - 1] = OpA::frag16(rd, m0 + 16 * (TM - 1), j, lane);
 }
 
 // Epilogue staging region of one wave: ROWS rows of the wave's block as
@@ -173,88 +239,117 @@ struct EpiRegion {
 };
 
 // Write a wave's (WTM x WTN) accumulator block to C (row r0.., column c0..)
-// through its LDS region, ROWS rows at a time.  Element e of lane l of MFMA
-// tile (mi, ni) is row 32*mi + 8*(e/4) + 4*(l/32) + e%4, column 32*ni + l%32
-// of the block: a lane holds 4 consecutive rows of one column, so direct
-// stores would write only 32 contiguous elements per row.  Staged, every row
-// goes out as contiguous 16-byte pieces: WTN*4-byte (fp32) or WTN*2-byte
-// (bf16, rounded to nearest even right before its store) runs, whole
-// 128-byte lines for WTN >= 64.  The stores are
-// non-temporal: C is written once and not re-read, so it should not push A
-// and B out of L2.
+// through its LDS region, ROWS rows at a time.  With 32x32 MFMAs element e
+// of lane l of MFMA tile (mi, ni) is row 32*mi + 8*(e/4) + 4*(l/32) + e%4,
+// column 32*ni + l%32 of the block; with 16x16 MFMAs it is row
+// 16*mi + 4*(l/16) + e, column 16*ni + l%16.  Either way a lane holds 4
+// consecutive rows of one column, so direct stores would write only 32 or 16
+// contiguous elements per row.  Staged, every row goes out as contiguous
+// 16-byte pieces: WTN*4-byte (fp32) or WTN*2-byte (bf16, rounded to nearest
+// even right before its store) runs, whole 128-byte lines for WTN >= 64.
+// The stores are non-temporal: C is written once and not re-read, so it
+// should not push A and B out of L2.
 //
 // EDGE (a tile that extends past C): only rows < m_lim and columns < n_lim
 // of the block (counted from r0, c0) are stored; a 16-byte piece that
 // straddles column n_lim goes out element by element.
-template <int WTM, int WTN, int ROWS, bool OUT_BF16, bool EDGE = false>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[WTM / 32][WTN / 32], char* region, void* Cv,
-                                         int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane,
-                                         int64_t m_lim = 0, int64_t n_lim = 0) {
-    constexpr int TM = WTM / 32, TN = WTN / 32;
+template <int MI, int WTM, int WTN, int ROWS>
+__device__ __forceinline__ void epilogue_stage(const typename Mfma<MI>::Acc (&acc)[WTM / MI][WTN / MI], int qc,
+                                               char* region, int lane) {
+    constexpr int TN = WTN / MI;
     constexpr int STRIDE = EpiRegion<WTN, ROWS>::kStride;
-    constexpr int ELEMS = OUT_BF16 ? 8 : 4;          // elements per lane per store (16 bytes out)
-    constexpr int PPR = WTN / ELEMS;                 // pieces per row
-    constexpr int PIECES = ROWS * PPR;
-    constexpr int H = 32 / ROWS;                     // chunks per MFMA row block
-    static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "chunks are whole 8-row groups of a row block");
-    static_assert(PIECES % 64 == 0, "epilogue pieces must fill whole wave stores");
-    const int lr = 4 * (lane >> 5), lc = lane & 31;
+    auto put = [&](int row, int col, float x) {
+        *(__attribute__((address_space(3))) float*)(lds_void_t*)(region + row * STRIDE + col * 4) = x;
+    };
+    if constexpr (MI == 32) {
+        constexpr int H = 32 / ROWS;                 // chunks per MFMA row block
+        const int mi = qc / H, h = qc % H;           // rows ROWS*h .. +ROWS-1 of row block mi
+        const int lr = 4 * (lane >> 5), lc = lane & 31;
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
+        for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-        for (int h = 0; h < H; ++h) {            // rows ROWS*h .. ROWS*h+ROWS-1 of MFMA row block mi
+            for (int e = (ROWS / 8) * 4 * h; e < (ROWS / 8) * 4 * (h + 1); ++e)
+                put(8 * (e >> 2) - ROWS * h + lr + (e & 3), 32 * ni + lc, acc[mi][ni][e]);
+    } else if constexpr (ROWS >= 16) {
+        const int lr = 4 * (lane >> 4), lc = lane & 15;   // whole 16-row blocks per chunk
+#pragma unroll
+        for (int b = 0; b < ROWS / 16; ++b)
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                for (int e = (ROWS / 8) * 4 * h; e < (ROWS / 8) * 4 * (h + 1); ++e) {
-                    const int row = 8 * (e >> 2) - ROWS * h + lr + (e & 3), col = 32 * ni + lc;
-                    *(__attribute__((address_space(3))) float*)(lds_void_t*)(region + row * STRIDE + col * 4) =
-                        acc[mi][ni][e];
-                }
+                for (int e = 0; e < 4; ++e) put(16 * b + lr + e, 16 * ni + lc, acc[qc * (ROWS / 16) + b][ni][e]);
+    } else {
+        // 8-row chunks: half h of row block mi is held by lanes 32h .. 32h+31
+        const int mi = qc / 2, h = qc % 2;
+        if ((lane >> 5) == h) {
+            const int lr = 4 * ((lane >> 4) & 1), lc = lane & 15;
 #pragma unroll
-            for (int q = 0; q < PIECES / 64; ++q) {
-                const int piece = q * 64 + lane;
-                const int row = piece / PPR, cp = piece % PPR;
-                const char* src = region + row * STRIDE + cp * ELEMS * 4;
-                const int64_t gi = c_off + (r0 + 32 * mi + ROWS * h + row) * ldc + c0 + cp * ELEMS;
-                if constexpr (EDGE) {
-                    const int rl = 32 * mi + ROWS * h + row, cl = cp * ELEMS;
-                    if (rl >= m_lim || cl >= n_lim) continue;
-                    if (cl + ELEMS > n_lim) {
+            for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                        for (int e = 0; e < ELEMS; ++e) {
-                            if (cl + e < n_lim) {
-                                const float x = *(const __attribute__((address_space(3))) float*)(lds_void_t*)(src + 4 * e);
-                                if constexpr (OUT_BF16) ((__bf16*)Cv)[gi + e] = (__bf16)x;
-                                else ((float*)Cv)[gi + e] = x;
-                            }
-                        }
-                        continue;
-                    }
-                }
-                if constexpr (OUT_BF16) {
-                    const f32x4 lo = *(const lds_f32x4_t*)(lds_void_t*)src;
-                    const f32x4 hi = *(const lds_f32x4_t*)(lds_void_t*)(src + 16);
-                    bf16x8 o;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        o[k] = (__bf16)lo[k];
-                        o[k + 4] = (__bf16)hi[k];
-                    }
-                    __builtin_nontemporal_store(__builtin_bit_cast(i16x8, o), (i16x8*)((__bf16*)Cv + gi));
-                } else {
-                    const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)src;
-                    __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
-                }
-            }
+                for (int e = 0; e < 4; ++e) put(lr + e, 16 * ni + lc, acc[mi][ni][e]);
         }
     }
 }
 
-// Global stores one wave issues in epilogue<WTM, WTN, ROWS, OUT_BF16>.
+template <int MI, int WTM, int WTN, int ROWS, bool OUT_BF16, bool EDGE = false>
+__device__ __forceinline__ void epilogue(const typename Mfma<MI>::Acc (&acc)[WTM / MI][WTN / MI], char* region,
+                                         void* Cv, int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane,
+                                         int64_t m_lim = 0, int64_t n_lim = 0) {
+    constexpr int STRIDE = EpiRegion<WTN, ROWS>::kStride;
+    constexpr int ELEMS = OUT_BF16 ? 8 : 4;          // elements per lane per store (16 bytes out)
+    constexpr int PPR = WTN / ELEMS;                 // pieces per row
+    constexpr int PIECES = ROWS * PPR;
+    static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "chunks are whole 8-row groups of a row block");
+    static_assert(MI == 16 || ROWS <= 32, "a 32x32 row block splits into whole chunks");
+    static_assert(PIECES % 64 == 0, "epilogue pieces must fill whole wave stores");
+#pragma unroll
+    for (int qc = 0; qc < WTM / ROWS; ++qc) {        // rows ROWS*qc .. ROWS*qc+ROWS-1 of the block
+        epilogue_stage<MI, WTM, WTN, ROWS>(acc, qc, region, lane);
+        wave_lds_order();                            // other lanes' staged values are read below
+#pragma unroll
+        for (int q = 0; q < PIECES / 64; ++q) {
+            const int piece = q * 64 + lane;
+            const int row = piece / PPR, cp = piece % PPR;
+            const char* src = region + row * STRIDE + cp * ELEMS * 4;
+            const int64_t gi = c_off + (r0 + ROWS * qc + row) * ldc + c0 + cp * ELEMS;
+            if constexpr (EDGE) {
+                const int rl = ROWS * qc + row, cl = cp * ELEMS;
+                if (rl >= m_lim || cl >= n_lim) continue;
+                if (cl + ELEMS > n_lim) {
+#pragma unroll
+                    for (int e = 0; e < ELEMS; ++e) {
+                        if (cl + e < n_lim) {
+                            const float x = *(const __attribute__((address_space(3))) float*)(lds_void_t*)(src + 4 * e);
+                            if constexpr (OUT_BF16) ((__bf16*)Cv)[gi + e] = (__bf16)x;
+                            else ((float*)Cv)[gi + e] = x;
+                        }
+                    }
+                    continue;
+                }
+            }
+            if constexpr (OUT_BF16) {
+                const f32x4 lo = *(const lds_f32x4_t*)(lds_void_t*)src;
+                const f32x4 hi = *(const lds_f32x4_t*)(lds_void_t*)(src + 16);
+                bf16x8 o;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    o[k] = (__bf16)lo[k];
+                    o[k + 4] = (__bf16)hi[k];
+                }
+                __builtin_nontemporal_store(__builtin_bit_cast(i16x8, o), (i16x8*)((__bf16*)Cv + gi));
+            } else {
+                const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)src;
+                __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
+            }
+        }
+        wave_lds_order();                            // the next chunk overwrites what was just read
+    }
+}
+
+// Global stores one wave issues in epilogue<MI, WTM, WTN, ROWS, OUT_BF16>.
 template <int WTM, int WTN, int ROWS, bool OUT_BF16>
 constexpr int epilogue_stores() {
-    return (WTM / 32) * (32 / ROWS) * (ROWS * WTN / (OUT_BF16 ? 8 : 4)) / 64;
+    return (WTM / ROWS) * (ROWS * WTN / (OUT_BF16 ? 8 : 4)) / 64;
 }
 
 // Cursor over the stream of stages a workgroup loads: tile t (logical),
@@ -352,14 +447,15 @@ struct StageCursor {
 // resources then cover exactly the valid bytes, the last partial K stage
 // masks its K-contiguous chunks, and edge tiles use the predicated epilogue;
 // otherwise none of that code is compiled in.
-template <int TILE, int BK, int S, int WGM, int WGN, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED, bool NT_A>
+template <int TILE, int BK, int S, int WGM, int WGN, int MI, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED,
+          bool NT_A>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int NW = WGM * WGN;        // waves, WGM along M by WGN along N
     constexpr int WTM = TILE / WGM;      // wave tile rows
     constexpr int WTN = TILE / WGN;      // wave tile columns
-    constexpr int TM = WTM / 32;         // MFMA tiles per wave along M
-    constexpr int TN = WTN / 32;         // ... along N
-    constexpr int NS = BK / 16;          // k16 substeps per stage
+    constexpr int TM = WTM / MI;         // MFMA tiles per wave along M
+    constexpr int TN = WTN / MI;         // ... along N
+    constexpr int NS = BK / Mfma<MI>::kK;   // MFMA substeps per stage
     static_assert(NS % 2 == 0, "fragment sets alternate; NS must be even");
     using OpA = OperandTile<TILE, A_K, BK, NW>;
     using OpB = OperandTile<TILE, B_K, BK, NW>;
@@ -410,24 +506,38 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     asm volatile("s_barrier" ::: "memory");
 
     Frags<TM, TN> f[2];
+    Frags16<TM, TN> f16;
+    if constexpr (MI == 32) {
 #pragma unroll
-    for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB>(f[0], u, smem, 0, m0, n0, lane);
+        for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB, MI>(f[0], u, smem, 0, m0, n0, lane);
+    } else {
+#pragma unroll
+        for (int u = 0; u < TM; ++u) f16.a[u] = OpA::frag16(smem, m0 + 16 * u, 0, lane);
+#pragma unroll
+        for (int u = 0; u < TN; ++u) f16.b[0][u] = OpB::frag16(smem + OpA::kBytes, n0 + 16 * u, 0, lane);
+    }
 
     int cur = 0;                                  // buffer of the current stage
     bool prev_full = true;                        // the previous tile stored every piece
     for (int t = first; t < end; t += stride) {
-        f32x16 acc[TM][TN];
+        typename Mfma<MI>::Acc acc[TM][TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+            for (int j = 0; j < TN; ++j) acc[i][j] = typename Mfma<MI>::Acc{};
 
         for (int kt = 0; kt < KT; ++kt) {
             char* st = smem + cur * kStage;
             const int nxt = (cur + 1 == S) ? 0 : cur + 1;
+            if constexpr (MI == 32) {
 #pragma unroll
-            for (int j = 0; j + 1 < NS; ++j)
-                substep<OpA, OpB, TM, TN, false, RAGGED, NT_A>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0, lane, ld, off);
+                for (int j = 0; j + 1 < NS; ++j)
+                    substep<OpA, OpB, MI, TM, TN, false, RAGGED, NT_A>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0,
+                                                                     lane, ld, off);
+            } else {
+                static_assert(NS == 2, "the 16x16x32 path runs two k32 substeps per stage");
+                substep16<OpA, OpB, TM, TN, 0, false, RAGGED, NT_A>(acc, f16, st, 1, m0, n0, lane, ld, off);
+            }
             // the next stage landed everywhere; nobody reads buffer `cur` any more
             __builtin_amdgcn_sched_barrier(0);
             if (kt == 0 && t != first && (!RAGGED || prev_full)) {
@@ -442,8 +552,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim());
-            substep<OpA, OpB, TM, TN, true, RAGGED, NT_A>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0, n0, lane, ld,
-                                            off);
+            if constexpr (MI == 32)
+                substep<OpA, OpB, MI, TM, TN, true, RAGGED, NT_A>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0,
+                                                                n0, lane, ld, off);
+            else
+                substep16<OpA, OpB, TM, TN, 1, true, RAGGED, NT_A>(acc, f16, smem + nxt * kStage, 0, m0, n0, lane, ld,
+                                                                 off);
             __builtin_amdgcn_sched_barrier(0);
             cur_ld.advance();
             cur = nxt;
@@ -469,11 +583,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
         int el = lane;
         if constexpr (RAGGED) asm volatile("" : "+v"(el));
         if (RAGGED && !full)
-            epilogue<WTM, WTN, 8, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
+            epilogue<MI, WTM, WTN, 8, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
         else if (last)
-            epilogue<WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+            epilogue<MI, WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
         else
-            epilogue<WTM, WTN, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+            epilogue<MI, WTM, WTN, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
         prev_full = full;
     }
 }
@@ -483,28 +597,37 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
 constexpr int kBK = 64;
 constexpr int kStages = 2;
 
-// Wave grid of a workgroup.  The 256 tile runs 2 x 4 waves of 128 x 64,
-// two waves per SIMD: while one waits on its fragment reads or the stage
-// barrier, the other's MFMAs keep the matrix unit busy (1 % faster at
-// 8192^3, 5 % on the 65536 x 256 x 4096 A stream than 2 x 2 waves of
-// 128 x 128, for 1.5x the LDS fragment reads per MFMA).  A 4 x 2 grid of
-// 64 x 128 waves does not fit: its epilogue rows are twice as long.  The
-// 128 tile keeps 2 x 2 waves of 64 x 64 (8 waves would leave 2 MFMAs per
-// k16 substep).
-template <int TILE>
+// Wave grid and MFMA of a workgroup.
+//   256 tile: 16x16x32 MFMAs; 2 x 4 waves of 128 x 64, two waves per SIMD,
+//     so that while one waits on its fragment reads or the stage barrier
+//     the other's MFMAs keep the matrix unit busy.  Edge-tile (RAGGED)
+//     kernels with fp32 output need a few more registers than two waves
+//     per SIMD leave and run 2 x 2 waves of 128 x 128 instead; every output
+//     element accumulates the same MFMA chain either way, so the bits agree.
+//   128 tile: 32x32x16 MFMAs; 2 x 2 waves of 64 x 64 (8 waves would leave
+//     2 MFMAs per substep).
+// Against 32x32x16, the 16x16x32 MFMA reads and writes half the accumulator
+// bytes per multiply-add; on this power-limited part the clock it keeps
+// makes 8192^3 7 % faster (measured, interleaved: 0.800 -> 0.744 ms).
+template <int TILE, bool RAGGED, bool OUT_BF16>
 struct WaveGrid {
-    static constexpr int M = 2, N = TILE == 256 ? 4 : 2;
+    static constexpr int M = 2;
+    static constexpr int N = TILE == 256 && !(RAGGED && !OUT_BF16) ? 4 : 2;
+    static constexpr int MI = TILE == 256 ? 16 : 32;
 };
 
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16, bool NT_A>
 void launch_nt(const GemmDesc& d, const KArgs& k, hipStream_t s) {
-    constexpr int WGM = WaveGrid<TILE>::M, WGN = WaveGrid<TILE>::N;
+    using WR = WaveGrid<TILE, true, OUT_BF16>;
+    using WF = WaveGrid<TILE, false, OUT_BF16>;
     const bool ragged = d.M % TILE || d.N % TILE || d.K % kBK;
-    const dim3 grid((unsigned)d.grid), block(64 * WGM * WGN);
+    const dim3 grid((unsigned)d.grid);
     if (ragged)
-        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, true, NT_A><<<grid, block, 0, s>>>(k);
+        gemm_kernel<TILE, kBK, kStages, WR::M, WR::N, WR::MI, A_K, B_K, OUT_BF16, true, NT_A>
+            <<<grid, dim3(64 * WR::M * WR::N), 0, s>>>(k);
     else
-        gemm_kernel<TILE, kBK, kStages, WGM, WGN, A_K, B_K, OUT_BF16, false, NT_A><<<grid, block, 0, s>>>(k);
+        gemm_kernel<TILE, kBK, kStages, WF::M, WF::N, WF::MI, A_K, B_K, OUT_BF16, false, NT_A>
+            <<<grid, dim3(64 * WF::M * WF::N), 0, s>>>(k);
 }
 
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16>

@@ -7,6 +7,9 @@
 //   MFMA 32x32x16 bf16: A operand lane l = row l%32, k (l/32)*8+e (e<8);
 //     B operand lane l = column l%32, k (l/32)*8+e; result element e of lane
 //     l = row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+//   MFMA 16x16x32 bf16: A operand lane l = row l%16, k (l/16)*8+e (e<8);
+//     B operand lane l = column l%16, k (l/16)*8+e; result element e (e<4)
+//     of lane l = row 4*(l/16) + e, column l%16.
 //   ds_read_b64_tr_b16: within each 16-lane group, result lane i element j is
 //     element i%4 of the 8 bytes addressed by lane 4j + i/4 of the group.
 //   buffer/global_load ... lds dwordx4: lane l's 16 bytes land at
@@ -126,6 +129,32 @@ struct OperandTile {
         return __builtin_bit_cast(bf16x8, v);
     }
 
+    // Fragment of the 16x16x32 MFMA for operand rows/columns [mn0, mn0+16)
+    // and k32 substep j (< BK/32): lane l receives k 32*j + 8*(l/16) .. +7
+    // of row/column mn0 + l%16.
+    __device__ static bf16x8 frag16(const char* lds, int mn0, int j, int lane) {
+        if constexpr (KMAJ) {
+            const int r = mn0 + (lane & 15), c = 4 * j + (lane >> 4);
+            const lds_i16x8_t* p = (const lds_i16x8_t*)(lds + r * (BK * 2) + ((c ^ swz_k<kCHR>(r)) << 4));
+            i16x8 v = *p;
+            return __builtin_bit_cast(bf16x8, v);
+        } else {
+            // Each 16-lane group reads 4 rows of 16 columns, transposed: lane
+            // i of the group receives column mn0 + i of the group's 4 rows.
+            int g = lane >> 4, s = lane & 15;
+            int col = mn0 + 4 * (s & 3);
+            int cc = col >> 3, sub = (col & 7) * 2;
+            int k0 = 32 * j + g * 8 + (s >> 2);
+            int k1 = k0 + 4;
+            const char* p0 = lds + k0 * (R * 2) + ((cc ^ swz_mn<kCH>(k0)) << 4) + sub;
+            const char* p1 = lds + k1 * (R * 2) + ((cc ^ swz_mn<kCH>(k1)) << 4) + sub;
+            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p1);
+            i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            return __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
     // Fragment for MFMA operand rows/columns [mn0, mn0+32) and k16 substep j
     // (< BK/16): lane l receives 8 consecutive k of row/column mn0 + l%32.
     __device__ static bf16x8 frag(const char* lds, int mn0, int j, int lane) {
@@ -170,6 +199,14 @@ __device__ __forceinline__ void lds_dma16_nt(__amdgpu_buffer_rsrc_t rsrc, uint32
     asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                  : "memory");
 }
+
+// Lanes of one wave that exchange values through LDS (one lane writes, another
+// reads) share no address per lane, so nothing stops the compiler from moving
+// one lane's read ahead of another's write, or a later write ahead of an
+// earlier read of the same bytes.  This compiler barrier keeps the LDS
+// accesses on each side of it in program order.  No wait is needed: LDS
+// executes one wave's instructions in order.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
