@@ -205,7 +205,10 @@ struct Frags16 {
 // next fragment goes into a spare register at the end of the row before it
 // and is moved into place after the loop.  Read after the loop instead, it
 // would still be in flight at the stage barrier's LDS wait that follows the
-// first substep (measured 1-1.7 % slower on the large shapes).
+// first substep (measured 1-1.7 % slower on the large shapes).  The loads
+// go out at the last MFMA of every group of kEvery: all in the first MFMAs
+// (5 % slower at 8192^3: the burst competes with the fragment reads) or at
+// the first of each group (0.3 % slower) measured worse.
 template <class OpA, class OpB, int TM, int TN, int P, bool LOADS, bool RAGGED, bool NT_A>
 __device__ __forceinline__ void substep16(f32x4 (&acc)[TM][TN], Frags16<TM, TN>& f, const char* rd, int j, int m0,
                                           int n0, int lane, const StageLoads<OpA, OpB, RAGGED, NT_A>& ld,
