@@ -142,23 +142,19 @@ struct Mfma<16> {
     }
 };
 
-// Fragment unit u of a substep: u < TM is A tile u, else B tile u - TM.
-template <class OpA, class OpB, int MI, int TM, int TN>
+// Fragment unit u of a 32x32x16 substep: u < TM is A tile u, else B tile
+// u - TM.
+template <class OpA, class OpB, int TM, int TN>
 __device__ __forceinline__ void read_unit(Frags<TM, TN>& f, int u, const char* stage, int j, int m0, int n0,
                                           int lane) {
-    if constexpr (MI == 32) {
-        if (u < TM) f.a[u] = OpA::frag(stage, m0 + 32 * u, j, lane);
-        else f.b[u - TM] = OpB::frag(stage + OpA::kBytes, n0 + 32 * (u - TM), j, lane);
-    } else {
-        if (u < TM) f.a[u] = OpA::frag16(stage, m0 + 16 * u, j, lane);
-        else f.b[u - TM] = OpB::frag16(stage + OpA::kBytes, n0 + 16 * (u - TM), j, lane);
-    }
+    if (u < TM) f.a[u] = OpA::frag(stage, m0 + 32 * u, j, lane);
+    else f.b[u - TM] = OpB::frag(stage + OpA::kBytes, n0 + 32 * (u - TM), j, lane);
 }
 
-// One substep (the k of one MFMA): TM*TN MFMAs on fragments `f`; woven between them, one
-// fragment unit of the next set `g` (stage `rd`, substep `j`) per MFMA and,
-// when `LOADS` is set, one of this wave's global -> LDS loads of a future
-// stage per MFMA.  Scheduling barriers keep that order, so every MFMA has
+// One k16 substep of the 32x32x16 path: TM*TN MFMAs on fragments `f`; woven
+// between them, one fragment unit of the next set `g` (stage `rd`, substep
+// `j`) per MFMA and, when `LOADS` is set, one of this wave's global -> LDS
+// loads of a future stage per MFMA.  Scheduling barriers keep that order, so every MFMA has
 // independent work issued next to it and the LDS sees a steady stream of
 // requests rather than bursts.
 template <class OpA, class OpB, int MI, int TM, int TN, bool LOADS, bool RAGGED, bool NT_A>
@@ -175,7 +171,7 @@ __device__ __forceinline__ void substep(typename Mfma<MI>::Acc (&acc)[TM][TN], c
         if constexpr (LOADS) {
             if (t < kLoads) ld.issue(t, off);
         }
-        if (t < kUnits) read_unit<OpA, OpB, MI>(g, t, rd, j, m0, n0, lane);
+        if (t < kUnits) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (LOADS) {
@@ -183,7 +179,7 @@ __device__ __forceinline__ void substep(typename Mfma<MI>::Acc (&acc)[TM][TN], c
         for (int t = kMfma; t < kLoads; ++t) ld.issue(t, off);
     }
 #pragma unroll
-    for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB, MI>(g, t, rd, j, m0, n0, lane);
+    for (int t = kMfma; t < kUnits; ++t) read_unit<OpA, OpB>(g, t, rd, j, m0, n0, lane);
 }
 
 // Fragments of the 16x16x32 path.  A row block's fragment is replaced by
@@ -428,13 +424,16 @@ struct StageCursor {
     __device__ int klim() const { return (a.krem != 0 && ks == a.ktiles - 1) ? a.krem : BK; }
 };
 
-// Pipeline (S LDS buffers; a stage is BK deep in K, NS = BK/16 MFMA
-// substeps).  The stages of all the tiles a workgroup visits form one
-// stream; stream stage g lives in buffer g mod S.
+// Pipeline (S LDS buffers; a stage is BK deep in K, NS = BK / (the MFMA's
+// k) substeps: 4 of k16 for 32x32x16, 2 of k32 for 16x16x32).  The stages of
+// all the tiles a workgroup visits form one stream; stream stage g lives in
+// buffer g mod S.
 //   prologue  request stages 0..S-1; wait for stage 0; barrier; read the
 //             substep-0 fragments of stage 0.
 //   step g    substeps 0..NS-2: MFMAs on the current fragments while the
-//                        next substep's fragments of stage g are read;
+//                        next substep's fragments of stage g are read
+//                        (16x16x32: into the B set not in use and, row by
+//                        row, in place of the A fragments just consumed);
 //             sync:      this wave's loads of stage g+1 have landed
 //                        (vmcnt <= the loads of stages g+2..g+S-1), its
 //                        LDS reads are done, then a workgroup barrier: every
@@ -466,6 +465,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int TN = WTN / MI;         // ... along N
     constexpr int NS = BK / Mfma<MI>::kK;   // MFMA substeps per stage
     static_assert(NS % 2 == 0, "fragment sets alternate; NS must be even");
+    static_assert(MI == 32 || NS == 2, "the 16x16x32 path runs two k32 substeps per stage");
     using OpA = OperandTile<TILE, A_K, BK, NW>;
     using OpB = OperandTile<TILE, B_K, BK, NW>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
@@ -518,7 +518,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     Frags16<TM, TN> f16;
     if constexpr (MI == 32) {
 #pragma unroll
-        for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB, MI>(f[0], u, smem, 0, m0, n0, lane);
+        for (int u = 0; u < TM + TN; ++u) read_unit<OpA, OpB>(f[0], u, smem, 0, m0, n0, lane);
     } else {
 #pragma unroll
         for (int u = 0; u < TM; ++u) f16.a[u] = OpA::frag16(smem, m0 + 16 * u, 0, lane);
@@ -544,7 +544,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
                     substep<OpA, OpB, MI, TM, TN, false, RAGGED, NT_A>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0,
                                                                      lane, ld, off);
             } else {
-                static_assert(NS == 2, "the 16x16x32 path runs two k32 substeps per stage");
                 substep16<OpA, OpB, TM, TN, 0, false, RAGGED, NT_A>(acc, f16, st, 1, m0, n0, lane, ld, off);
             }
             // the next stage landed everywhere; nobody reads buffer `cur` any more
