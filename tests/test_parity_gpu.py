@@ -582,3 +582,30 @@ def test_rotated_k_random_data_within_tolerance_and_deterministic():
         assert nfail == 0, "flags 0x%x: %d sampled elements outside tolerance (max util %.3g)" % (flags, nfail, util)
         runs.append(C)
     assert torch.equal(runs[0].view(torch.int32), runs[1].view(torch.int32))
+
+
+# --------------------------------------------------- randomized shape sweep --
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M, N = int(rng.integers(1, 700)), int(rng.integers(1, 600))
+        K = 8 * int(rng.integers(1, 80))
+        batch = int(rng.integers(1, 3))
+        a_k, b_k = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        out = "bf16" if rng.integers(0, 2) else "f32"
+        flags = [asl.AS_FLAG_TILE_256, asl.AS_FLAG_TILE_128, 0][i % 3]
+        flags |= [0, asl.AS_FLAG_ROTATE_K, asl.AS_FLAG_NT_A, asl.AS_FLAG_ROTATE_K | asl.AS_FLAG_NT_A][(i // 3) % 4]
+        cases.append((M, N, K, batch, a_k, b_k, out, flags))
+    return cases
+
+
+@pytest.mark.parametrize("M,N,K,batch,a_k,b_k,out,flags", _random_cases(24, 2026))
+def test_random_shapes_bit_exact(M, N, K, batch, a_k, b_k, out, flags):
+    """Seeded random shapes, layouts, output types, tiles and streaming
+    options on integer data: bit-exact against the oracle, nothing written
+    outside C (both MFMA shapes, both wave grids of the 256 tile, edge tiles,
+    rotated K loops and split K where the plan chooses it)."""
+    _say("random M=%d N=%d K=%d batch=%d a_k=%s b_k=%s out=%s flags=0x%x" % (M, N, K, batch, a_k, b_k, out, flags))
+    _ragged(M, N, K, batch, a_k, b_k, out, flags, 7000 + M + N + K)
