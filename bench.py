@@ -11,9 +11,12 @@ events on the launch stream; algorithmic flops = 2*M*N*K per launch; peak =
 summary of the workload when it was taken on the current kernel source, and the CPU oracle
 timed on a bounded sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--per-launch N]
       (defaults: warm up for about 0.5 s of launches, then time at least 50
-      launches and 0.1 s; the JSON line reports the counts used)
+      launches and 0.1 s; the JSON line reports the counts used.  Then N = 50
+      single launches are timed warm and N cold -- each after a 1 GiB read
+      that evicts L2 and the MALL -- and their median and minimum reported
+      as per_launch_ms)
   python bench.py --workload NAME      other workloads (reported, not the headline);
                                        attn32x2048 is the fused attention forward
   python bench.py --tilecast           tile fan-out microbenchmark (JSON lines)
@@ -95,6 +98,9 @@ def _plan(asl, w, flags=0):
 
 WARMUP_S = 0.5      # default warm-up: launches for about this long, so the clocks settle
 TIMED_S = 0.1       # default timed region: at least this long (and at least 50 launches)
+PER_LAUNCH_N = 0    # after the timed region: this many single launches timed warm and cold (0: none)
+FLUSH_BYTES = 1 << 30   # cold launches: this many bytes read first (4x the 256 MB MALL)
+LAST_PER_LAUNCH = None  # per-launch statistics of the last _timed call, when PER_LAUNCH_N > 0
 
 
 def _timed(run, steps, warmup, stream):
@@ -127,7 +133,39 @@ def _timed(run, steps, warmup, stream):
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if PER_LAUNCH_N > 0:
+        _per_launch(run, PER_LAUNCH_N, stream)
     return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps, steps, warmup
+
+
+def _per_launch(run, n, stream):
+    """Median and minimum of n single launches (HIP events around each, on the
+    launch stream), warm and then cold: before each cold launch a FLUSH_BYTES
+    buffer is read on the same stream, which evicts L2 and the MALL.  It is
+    read, not written: a write leaves the caches full of dirty lines that the
+    measured kernel would then have to write back (the attention scores took
+    a third longer after a 1 GiB write than after a 1 GiB read)."""
+    import statistics
+    import torch
+    global LAST_PER_LAUNCH
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=stream.device)
+    sink = torch.empty((), dtype=torch.float32, device=stream.device)
+    torch.cuda.synchronize()
+    stats = {"launches": n, "flush_bytes_read": FLUSH_BYTES}
+    for kind in ("warm", "cold"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i, (e0, e1) in enumerate(evs):
+            if kind == "cold":
+                torch.amax(flush, dim=0, out=sink)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        stats[kind + "_median"] = round(statistics.median(ms), 4)
+        stats[kind + "_min"] = round(min(ms), 4)
+    del flush, sink
+    LAST_PER_LAUNCH = stats
 
 
 def time_attention(w, steps, warmup):
@@ -339,6 +377,8 @@ def attention_line(w, args):
         "hbm_bytes_per_s_compulsory": round((w.bytes_in + w.bytes_out) / (ev_ms * 1e-3) / 1e9, 1),
         "hbm_read_over_compulsory": (round(traffic["read_bytes"] / w.bytes_in, 3) if traffic else None),
     }
+    if LAST_PER_LAUNCH:
+        out["per_launch_ms"] = LAST_PER_LAUNCH
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_attn(w)
     return out
@@ -356,6 +396,8 @@ def main():
     ap.add_argument("--tilecast", action="store_true")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--per-launch", type=int, default=50,
+                    help="single launches timed warm and cold after the timed region (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -379,6 +421,8 @@ def main():
             print(json.dumps(line))
         return
 
+    global PER_LAUNCH_N
+    PER_LAUNCH_N = max(0, args.per_launch)
     from workloads import ATTN_WORKLOADS
     if args.workload in ATTN_WORKLOADS:
         print(json.dumps(attention_line(ATTN_WORKLOADS[args.workload], args)))
@@ -419,6 +463,8 @@ def main():
         "mfma_util": round(achieved / PEAK_BF16_TFLOPS, 4),
         "hbm_read_over_compulsory": (round(traffic["read_bytes"] / compulsory_read, 3) if traffic else None),
     }
+    if LAST_PER_LAUNCH:
+        out["per_launch_ms"] = LAST_PER_LAUNCH
     if not args.no_cpu_baseline and w.a_major == "row" and w.kind == "gemm":
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
