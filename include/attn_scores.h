@@ -22,9 +22,11 @@
  *     and streaming scenarios).
  *
  * Numerics: A and B (Q and K) are bf16; products are accumulated in fp32 by
- * v_mfma_f32_32x32x16_bf16; C is written as fp32, or rounded to bf16 with
- * round-to-nearest-even.  Results are deterministic run to run (no atomics,
- * no split-K).
+ * v_mfma_f32_16x16x32_bf16 (256x256 tiles) or v_mfma_f32_32x32x16_bf16
+ * (128x128 tiles); C is written as fp32, or rounded to bf16 with
+ * round-to-nearest-even.  Results are deterministic run to run: no atomics,
+ * and a split-K plan adds its chunks in a fixed order.  The order of the fp32
+ * sum depends on the plan (K split, rotated K loop), never on the run.
  *
  * Layout conventions.  All strides are ELEMENT strides (not bytes).  A matrix
  * X[b, r, c] lives at base + b*batch + r*row + c*col.  A batch stride of 0
