@@ -335,6 +335,17 @@ as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* 
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return fail(AS_ERR_HIP, "hipGetDevice failed");
         if (!plan->ws || plan->ws_dev != dev) {
+            // Allocating (or freeing) while the stream records a graph would
+            // invalidate the capture; say so instead.
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing((hipStream_t)hip_stream, &cs) != hipSuccess) {
+                (void)hipGetLastError();
+                cs = hipStreamCaptureStatusNone;
+            }
+            if (cs != hipStreamCaptureStatusNone)
+                return fail(AS_ERR_UNSUPPORTED,
+                            "split-K workspace not yet allocated on this device: run the plan once outside "
+                            "graph capture first");
             if (plan->ws) {
                 (void)hipSetDevice(plan->ws_dev);
                 (void)hipFree(plan->ws);

@@ -150,7 +150,13 @@ AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, in
 /* Launch the planned product on `hip_stream`.  A, B: device bf16; C: device
  * fp32 or bf16 as planned.  Pointers must be 16-byte aligned.  A split plan
  * launches two kernels and, on its first run on a device, allocates its
- * workspace (AS_ERR_NOMEM if that fails). */
+ * workspace (AS_ERR_NOMEM if that fails).
+ * Graph capture: the launches allocate, clear and synchronize nothing, so a
+ * run may be recorded into a HIP graph on a capturing stream and replayed.
+ * The one exception is a split plan's first run on a device: that run
+ * allocates, so it must happen outside capture (inside, gemm_run returns
+ * AS_ERR_UNSUPPORTED and records nothing).  A replay reuses the pointers
+ * and the workspace of the recorded run. */
 AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream);
 
 /* Whether a plan splits K: number of K chunks (1: no split) and the bytes
@@ -187,7 +193,8 @@ AS_API as_status gemm_plan_tile_of(as_gemm_t plan, int64_t slot, int64_t* batch,
  * GEMM with A = Q and B = K^T, planned and launched in one call (same
  * kernels, same errors).  The plans of the last 8 distinct size/stride/type
  * combinations are kept per calling thread (host memory only), so a loop of
- * calls plans once.  Asynchronous on `hip_stream`.
+ * calls plans once.  Asynchronous on `hip_stream`.  It never splits K, so
+ * every call may be recorded into a HIP graph (see gemm_run).
  */
 AS_API as_status sscore_run(const void* Q, const void* K, void* S,
                      int64_t batch, int64_t Lq, int64_t Lk, int64_t dim,
@@ -238,6 +245,9 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
  * bitwise the same O.  The queue counters live in the library (64 slots per
  * device, taken in turn by successive launches; each launch leaves its slot
  * at zero): at most 64 queue launches may run at once on one device.
+ * Graph capture: a launch allocates and clears nothing, so it may be
+ * recorded into a HIP graph and replayed; a recorded queue launch uses its
+ * slot again on every replay.
  */
 #define AS_ATTN_CAUSAL 0x1u   /* attn_fwd_run: query i sees keys j <= i + (Lk - Lq) only */
 #define AS_ATTN_QUERIES_256 0x2u  /* force work items of 256 queries (each wave sweeps all keys) */
