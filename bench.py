@@ -100,6 +100,7 @@ WARMUP_S = 0.5      # default warm-up: launches for about this long, so the cloc
 TIMED_S = 0.1       # default timed region: at least this long (and at least 50 launches)
 PER_LAUNCH_N = 0    # after the timed region: this many single launches timed warm and cold (0: none)
 FLUSH_BYTES = 1 << 30   # cold launches: this many bytes read first (4x the 256 MB MALL)
+GRAPH_LAUNCHES = 20     # graph timing: launches recorded into one HIP graph
 LAST_PER_LAUNCH = None  # per-launch statistics of the last _timed call, when PER_LAUNCH_N > 0
 
 
@@ -144,7 +145,10 @@ def _per_launch(run, n, stream):
     buffer is read on the same stream, which evicts L2 and the MALL.  It is
     read, not written: a write leaves the caches full of dirty lines that the
     measured kernel would then have to write back (the attention scores took
-    a third longer after a 1 GiB write than after a 1 GiB read)."""
+    a third longer after a 1 GiB write than after a 1 GiB read).  Then the
+    launch time without the host: GRAPH_LAUNCHES launches recorded into one
+    HIP graph (run(stream handle) launches on the capturing stream), each
+    replay timed with events; reported per launch."""
     import statistics
     import torch
     global LAST_PER_LAUNCH
@@ -165,6 +169,25 @@ def _per_launch(run, n, stream):
         stats[kind + "_median"] = round(statistics.median(ms), 4)
         stats[kind + "_min"] = round(min(ms), 4)
     del flush, sink
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(GRAPH_LAUNCHES):
+            run(cs)
+    g.replay()                                   # the first replay uploads the graph
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(5, n // 5))]
+    for e0, e1 in evs:
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) / GRAPH_LAUNCHES for e0, e1 in evs]
+    stats["graph_launches"] = GRAPH_LAUNCHES
+    stats["graph_median"] = round(statistics.median(ms), 4)
+    stats["graph_min"] = round(min(ms), 4)
+    del g
     LAST_PER_LAUNCH = stats
 
 
@@ -183,8 +206,8 @@ def time_attention(w, steps, warmup):
     args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), w.batch, w.kv_group, w.Lq, w.Lk, w.d, w.dv,
             sq, sk, sv, so, w.scale, asl.AS_BF16, o_t, asl.AS_ATTN_CAUSAL if w.causal else 0, stream.cuda_stream)
 
-    def run():
-        asl.attn_fwd_run_gqa(*args)
+    def run(s=None):
+        asl.attn_fwd_run_gqa(*args[:-1], stream.cuda_stream if s is None else s)
     out = _timed(run, steps, warmup, stream)
     del Q, K, V, O
     return out
@@ -213,14 +236,14 @@ def time_workload(w, steps, warmup, flags=0):
         info = asl.gemm_plan_info(plan) + (1,)
         asl.gemm_destroy(plan)
 
-        def run():
-            asl.sscore_run(a, b, c, w.batch, w.M, w.N, w.K, sq, sk, ss, asl.AS_BF16, s_t, sh)
+        def run(s=None):
+            asl.sscore_run(a, b, c, w.batch, w.M, w.N, w.K, sq, sk, ss, asl.AS_BF16, s_t, sh if s is None else s)
     else:
         plan = _plan(asl, w, flags)
         info = asl.gemm_plan_info(plan) + (asl.gemm_plan_split_k(plan)[0],)
 
-        def run():
-            asl.gemm_run(plan, a, b, c, sh)
+        def run(s=None):
+            asl.gemm_run(plan, a, b, c, sh if s is None else s)
     wall_ms, ev_ms, steps, warmup = _timed(run, steps, warmup, stream)
     if w.kind != "sscore":
         asl.gemm_destroy(plan)
