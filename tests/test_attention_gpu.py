@@ -292,6 +292,42 @@ def test_queue_counters_reset_between_launches():
     assert not bad, "launches %s differ" % bad[:10]
 
 
+def test_queue_launches_overlapping_on_concurrent_streams():
+    # Successive launches take successive counter slots, so queue launches
+    # that overlap on different streams never share counters.  Three streams
+    # each enqueue 12 causal queue launches on their own data, with no
+    # synchronization between the streams; every output must equal that
+    # data's lone launch bit for bit (the schedule is deterministic).
+    b, L, d, rounds = 8, 1024, 128, 12
+    _say("queue launches on 3 concurrent streams, b=%d L=%d d=%d, %d rounds" % (b, L, d, rounds))
+    scale = d ** -0.5
+    data = [tuple(draw((b, L, d), "normal", 0, 1, 4100 + 3 * i + j).to(DEV) for j in range(3)) for i in range(3)]
+
+    def launch(i, O, stream):
+        Q, K, V = data[i]
+        asl.attn_fwd_run(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), b, L, L, d, d,
+                         (d, 1, L * d), (d, 1, L * d), (d, 1, L * d), (d, 1, L * d), scale,
+                         asl.AS_BF16, asl.AS_F32, flags=asl.AS_ATTN_CAUSAL | asl.AS_ATTN_SCHED_QUEUE,
+                         stream=stream.cuda_stream)
+
+    refs = []
+    for i in range(3):
+        O = torch.empty((b, L, d), dtype=torch.float32, device=DEV)
+        launch(i, O, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        refs.append(O)
+    outs = [[torch.full((b, L, d), float("nan"), dtype=torch.float32, device=DEV) for _ in range(rounds)]
+            for _ in range(3)]
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in range(rounds):
+        for i, st in enumerate(streams):
+            launch(i, outs[i][r], st)
+    torch.cuda.synchronize()
+    bad = [(i, r) for i in range(3) for r in range(rounds) if not torch.equal(outs[i][r], refs[i])]
+    assert not bad, "stream/round %s differ from the lone launch" % bad[:10]
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("items", [256, 128])
 def test_negative_scale_exact_power_of_two_probabilities(items, causal):

@@ -156,6 +156,30 @@ def test_split_k_integer_data_bit_exact(M, N, K, a_k, b_k, out):
         assert np.array_equal(bits(C), oracle.f64_to_bf16_rne_array(Cref))
 
 
+def test_split_k_on_concurrent_streams():
+    # A split plan's runs share its workspace, so the binding keeps one plan
+    # per stream: split products enqueued on three streams with no
+    # synchronization between them must each equal a lone run bit for bit.
+    M, N, K, rounds = 1024, 1024, 8192, 6
+    _say("split-K %dx%dx%d on 3 concurrent streams, %d rounds" % (M, N, K, rounds))
+    data = [(draw((M, K), "uniform", -1.0, 1.0, 4200 + 2 * i).to(DEV),
+             draw((K, N), "uniform", -1.0, 1.0, 4201 + 2 * i).to(DEV)) for i in range(3)]
+    refs = [asl.gemm(A, B, out_dtype=torch.float32) for A, B in data]
+    torch.cuda.synchronize()
+    outs = [[torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV) for _ in range(rounds)]
+            for _ in range(3)]
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(3)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for r in range(rounds):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                asl.gemm(data[i][0], data[i][1], out=outs[i][r])
+    torch.cuda.synchronize()
+    bad = [(i, r) for i in range(3) for r in range(rounds) if not torch.equal(outs[i][r], refs[i])]
+    assert not bad, "stream/round %s differ from the lone run" % bad[:10]
+
+
 @pytest.mark.parametrize("M,N,K,a_k,b_k", SPLIT[:2])
 def test_split_k_random_data_within_tolerance_and_deterministic(M, N, K, a_k, b_k):
     _say("split-K random %dx%dx%d" % (M, N, K))
