@@ -243,13 +243,20 @@ def _require_cuda(*ts):
 _PLAN_CACHE_SIZE = 64
 _plan_cache = collections.OrderedDict()
 _plan_cache_lock = threading.Lock()
+# Split plans evicted from the cache.  A HIP graph that recorded a run of a
+# split plan replays into that plan's workspace, and nothing tells the cache
+# whether one did, so an evicted split plan is kept (never destroyed) until
+# the process ends.  Plans without a split hold no device memory and are
+# destroyed on eviction.
+_retired_split_plans = []
 
 
 def plan_for(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags=0, stream=0) -> int:
     """Cached gemm_create for a shape/stride/dtype/flags/stream key: the last
-    64 plans are kept, the least recently used is destroyed (with its split-K
-    workspace, if any).  The stream is part of the key because a split plan's
-    runs share its workspace: calls on different streams get their own plans."""
+    64 plans are kept; the least recently used is destroyed, or, if it splits
+    K, set aside for the life of the process (with its workspace).  The stream
+    is part of the key because a split plan's runs share its workspace: calls
+    on different streams get their own plans."""
     key = (M, N, K, batch, tuple(sa), tuple(sb), tuple(sc), a_t, b_t, c_t, flags, stream)
     with _plan_cache_lock:
         p = _plan_cache.get(key)
@@ -260,7 +267,10 @@ def plan_for(M, N, K, batch, sa, sb, sc, a_t, b_t, c_t, flags=0, stream=0) -> in
         _plan_cache[key] = p
         while len(_plan_cache) > _PLAN_CACHE_SIZE:
             _, old = _plan_cache.popitem(last=False)
-            gemm_destroy(old)
+            if gemm_plan_split_k(old)[0] > 1:
+                _retired_split_plans.append(old)
+            else:
+                gemm_destroy(old)
         return p
 
 

@@ -13,7 +13,8 @@
 #include <algorithm>
 #include <utility>
 #include <string>
-#include <unordered_set>
+#include <memory>
+#include <unordered_map>
 
 #include <hip/hip_runtime_api.h>
 
@@ -23,19 +24,31 @@
 struct as_gemm_plan {
     asl::GemmDesc d;
     // Split-K workspace (device memory of d.ws_bytes), allocated by the first
-    // run on a device and kept until the plan is destroyed.
+    // run on a device and kept until the plan is released.
     std::mutex ws_mu;
     void* ws = nullptr;
     int ws_dev = -1;
+    ~as_gemm_plan() {
+        if (!ws) return;
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(ws_dev);
+        (void)hipFree(ws);
+        (void)hipSetDevice(cur);
+    }
 };
 
 namespace {
 
 thread_local std::string g_last_error;
 
+// Live plans.  A run holds its own reference for as long as it reads the
+// plan, so a gemm_destroy racing with it on another thread only drops the
+// registry's reference; the plan (and its workspace) goes when the last
+// reference does.
 std::mutex g_plans_mu;
-std::unordered_set<const as_gemm_plan*>& plans() {
-    static std::unordered_set<const as_gemm_plan*> s;
+std::unordered_map<const as_gemm_plan*, std::shared_ptr<as_gemm_plan>>& plans() {
+    static std::unordered_map<const as_gemm_plan*, std::shared_ptr<as_gemm_plan>> s;
     return s;
 }
 
@@ -153,6 +166,11 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     const int64_t c_align = d.c_bf16 ? 8 : 4;
     if (c.row % c_align)
         return fail(AS_ERR_UNSUPPORTED, "C row stride must be a multiple of %" PRId64 " elements", c_align);
+    // Every batch origin must start a 16-byte chunk like row origins do:
+    // the kernels move operands and C in 16-byte pieces from there.
+    if (batch > 1 && (a.batch % 8 || b.batch % 8 || c.batch % c_align))
+        return fail(AS_ERR_UNSUPPORTED, "batch strides must be multiples of 8 elements (fp32 C: 4); got A %" PRId64
+                    ", B %" PRId64 ", C %" PRId64, a.batch, b.batch, c.batch);
     if (M > 1 && c.row < N) return fail(AS_ERR_INVALID, "C rows overlap (row stride %" PRId64 " < N)", c.row);
     if (batch > 1 && c.batch < M * c.row)
         return fail(AS_ERR_INVALID, "C batches overlap (batch stride %" PRId64 ")", c.batch);
@@ -285,9 +303,10 @@ asl::GemmDesc split_launch_desc(const asl::GemmDesc& d) {
     return e;
 }
 
-bool plan_live(const as_gemm_plan* p) {
+std::shared_ptr<as_gemm_plan> acquire(const as_gemm_plan* p) {
     std::lock_guard<std::mutex> lk(g_plans_mu);
-    return p && plans().count(p);
+    auto it = p ? plans().find(p) : plans().end();
+    return it == plans().end() ? nullptr : it->second;
 }
 
 as_status run_desc(const asl::GemmDesc& d, const void* A, const void* B, void* C, void* stream) {
@@ -311,55 +330,66 @@ as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, int64_t b
     asl::GemmDesc d;
     as_status s = plan_desc(&d, M, N, K, batch, a, b, c, a_t, b_t, c_t, flags);
     if (s != AS_OK) return s;
-    as_gemm_plan* p = new (std::nothrow) as_gemm_plan;
-    if (!p) return fail(AS_ERR_NOMEM, "out of host memory");
-    p->d = d;
-    {
+    std::shared_ptr<as_gemm_plan> p;
+    try {
+        p = std::make_shared<as_gemm_plan>();
+        p->d = d;
         std::lock_guard<std::mutex> lk(g_plans_mu);
-        plans().insert(p);
+        plans().emplace(p.get(), p);
+    } catch (const std::bad_alloc&) {
+        return fail(AS_ERR_NOMEM, "out of host memory");
     }
-    *out = p;
+    *out = p.get();
     return ok();
 }
 
 as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream) {
-    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
-    const asl::GemmDesc& d = plan->d;
+    const std::shared_ptr<as_gemm_plan> p = acquire(plan);
+    if (!p) return fail(AS_ERR_INVALID, "null or unknown plan");
+    const asl::GemmDesc& d = p->d;
     if (d.splits == 1) return run_desc(d, A, B, C, hip_stream);
     if (!A || !B || !C) return fail(AS_ERR_INVALID, "null device pointer");
     if (!aligned16(A) || !aligned16(B) || !aligned16(C))
         return fail(AS_ERR_UNSUPPORTED, "device pointers must be 16-byte aligned");
     void* ws;
     {
-        std::lock_guard<std::mutex> lk(plan->ws_mu);
+        std::lock_guard<std::mutex> lk(p->ws_mu);
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return fail(AS_ERR_HIP, "hipGetDevice failed");
-        if (!plan->ws || plan->ws_dev != dev) {
-            // Allocating (or freeing) while the stream records a graph would
-            // invalidate the capture; say so instead.
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            if (hipStreamIsCapturing((hipStream_t)hip_stream, &cs) != hipSuccess) {
-                (void)hipGetLastError();
-                cs = hipStreamCaptureStatusNone;
-            }
-            if (cs != hipStreamCaptureStatusNone)
-                return fail(AS_ERR_UNSUPPORTED,
-                            "split-K workspace not yet allocated on this device: run the plan once outside "
-                            "graph capture first");
-            if (plan->ws) {
-                (void)hipSetDevice(plan->ws_dev);
-                (void)hipFree(plan->ws);
+        if (!p->ws || p->ws_dev != dev) {
+            if (p->ws) {
+                // A run on another device: its workspace moves here.  Freeing
+                // waits for the device, which a capture cannot record.
+                hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+                if (hipStreamIsCapturing((hipStream_t)hip_stream, &cs) != hipSuccess) {
+                    (void)hipGetLastError();
+                    cs = hipStreamCaptureStatusNone;
+                }
+                if (cs != hipStreamCaptureStatusNone)
+                    return fail(AS_ERR_UNSUPPORTED, "split-K workspace lives on device %d: run the plan once on "
+                                "device %d outside graph capture first", p->ws_dev, dev);
+                (void)hipSetDevice(p->ws_dev);
+                (void)hipFree(p->ws);
                 (void)hipSetDevice(dev);
-                plan->ws = nullptr;
+                p->ws = nullptr;
             }
-            if (hipMalloc(&plan->ws, (size_t)d.ws_bytes) != hipSuccess) {
-                plan->ws = nullptr;
+            // The allocation is not a stream operation: with the calling
+            // thread's capture mode relaxed for it (as a caching allocator
+            // does), it is allowed while a stream records a graph, and the
+            // recorded launches use this workspace on every replay.
+            hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+            (void)hipThreadExchangeStreamCaptureMode(&mode);
+            const hipError_t e = hipMalloc(&p->ws, (size_t)d.ws_bytes);
+            (void)hipThreadExchangeStreamCaptureMode(&mode);
+            if (e != hipSuccess) {
+                p->ws = nullptr;
                 (void)hipGetLastError();
-                return fail(AS_ERR_NOMEM, "split-K workspace of %" PRId64 " bytes", d.ws_bytes);
+                return fail(AS_ERR_NOMEM, "split-K workspace of %" PRId64 " bytes: %s", d.ws_bytes,
+                            hipGetErrorString(e));
             }
-            plan->ws_dev = dev;
+            p->ws_dev = dev;
         }
-        ws = plan->ws;
+        ws = p->ws;
     }
     int e = asl::launch_gemm(split_launch_desc(d), A, B, ws, hip_stream);
     if (e == 0) e = asl::launch_splitk_reduce(d, ws, C, hip_stream);
@@ -368,36 +398,35 @@ as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* 
 }
 
 as_status gemm_destroy(as_gemm_t plan) {
+    std::shared_ptr<as_gemm_plan> p;
     {
         std::lock_guard<std::mutex> lk(g_plans_mu);
-        if (!plan || !plans().erase(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
+        auto it = plan ? plans().find(plan) : plans().end();
+        if (it == plans().end()) return fail(AS_ERR_INVALID, "null or unknown plan");
+        p = std::move(it->second);
+        plans().erase(it);
     }
-    if (plan->ws) {
-        int cur = 0;
-        (void)hipGetDevice(&cur);
-        (void)hipSetDevice(plan->ws_dev);
-        (void)hipFree(plan->ws);
-        (void)hipSetDevice(cur);
-    }
-    delete plan;
+    p.reset();   // frees the plan here, or at the end of a run still holding it
     return ok();
 }
 
 as_status gemm_plan_info(as_gemm_t plan, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k, int64_t* tiles,
                          int64_t* workgroups) {
-    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
-    if (tile_m) *tile_m = plan->d.tile;
-    if (tile_n) *tile_n = plan->d.tile;
+    const std::shared_ptr<as_gemm_plan> p = acquire(plan);
+    if (!p) return fail(AS_ERR_INVALID, "null or unknown plan");
+    if (tile_m) *tile_m = p->d.tile;
+    if (tile_n) *tile_n = p->d.tile;
     if (tile_k) *tile_k = (int32_t)kBK;
-    if (tiles) *tiles = plan->d.tiles;
-    if (workgroups) *workgroups = plan->d.grid;
+    if (tiles) *tiles = p->d.tiles;
+    if (workgroups) *workgroups = p->d.grid;
     return ok();
 }
 
 as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* batch, int64_t* tile_row,
                             int64_t* tile_col) {
-    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
-    const asl::GemmDesc L = plan->d.splits > 1 ? split_launch_desc(plan->d) : plan->d;
+    const std::shared_ptr<as_gemm_plan> p = acquire(plan);
+    if (!p) return fail(AS_ERR_INVALID, "null or unknown plan");
+    const asl::GemmDesc L = p->d.splits > 1 ? split_launch_desc(p->d) : p->d;
     if (workgroup < 0 || workgroup >= L.tiles || !batch || !tile_row || !tile_col)
         return fail(AS_ERR_INVALID, "execution slot out of range or null output");
     if (!asl::tile_of_slot(L, workgroup, batch, tile_row, tile_col))
@@ -406,9 +435,10 @@ as_status gemm_plan_tile_of(as_gemm_t plan, int64_t workgroup, int64_t* batch, i
 }
 
 as_status gemm_plan_split_k(as_gemm_t plan, int32_t* splits, int64_t* workspace_bytes) {
-    if (!plan_live(plan)) return fail(AS_ERR_INVALID, "null or unknown plan");
-    if (splits) *splits = plan->d.splits;
-    if (workspace_bytes) *workspace_bytes = plan->d.splits > 1 ? plan->d.ws_bytes : 0;
+    const std::shared_ptr<as_gemm_plan> p = acquire(plan);
+    if (!p) return fail(AS_ERR_INVALID, "null or unknown plan");
+    if (splits) *splits = p->d.splits;
+    if (workspace_bytes) *workspace_bytes = p->d.splits > 1 ? p->d.ws_bytes : 0;
     return ok();
 }
 
@@ -486,6 +516,10 @@ as_status attn_fwd_run_gqa(const void* Q, const void* K, const void* V, void* O,
         return fail(AS_ERR_UNSUPPORTED, "Q, K, V and O need a contiguous last dimension (column stride 1)");
     if (q.row % 8 || k.row % 8 || v.row % 8 || o.row % 4)
         return fail(AS_ERR_UNSUPPORTED, "row strides must be multiples of 8 elements (O: 4)");
+    // Batch origins of the slices that are used start 16-byte chunks too
+    // (Q is read 16 bytes at a time, K and V by 16-byte LDS-DMA loads).
+    if ((batch > 1 && (q.batch % 8 || o.batch % 4)) || (batch / kv_group > 1 && (k.batch % 8 || v.batch % 8)))
+        return fail(AS_ERR_UNSUPPORTED, "batch strides must be multiples of 8 elements (O: 4)");
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
         return fail(AS_ERR_UNSUPPORTED, "device pointers must be 16-byte aligned");
     if (Lq > INT32_MAX / 2 || Lk > INT32_MAX / 2) return fail(AS_ERR_UNSUPPORTED, "sequence too long");
@@ -509,6 +543,19 @@ as_status attn_fwd_run_gqa(const void* Q, const void* K, const void* V, void* O,
     ad.tiles = batch * ad.qtiles;
     ad.sched = attn_sched(flags);
     ad.grid = ad.sched == 0 ? ad.tiles : std::min<int64_t>(ad.tiles, kCus);
+    if (ad.sched == 2) {
+        // A queue launch takes its counters' slot when it is launched; a
+        // graph would replay the recorded slot, which an eager launch or
+        // another replay may hold at the same time.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing((hipStream_t)hip_stream, &cs) != hipSuccess) {
+            (void)hipGetLastError();
+            cs = hipStreamCaptureStatusNone;
+        }
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(AS_ERR_UNSUPPORTED, "AS_ATTN_SCHED_QUEUE cannot be recorded into a graph capture "
+                        "(use the default or the static schedule there)");
+    }
     int e = asl::launch_attn(ad, Q, K, V, O, hip_stream);
     if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
     return ok();

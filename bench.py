@@ -251,36 +251,73 @@ def time_workload(w, steps, warmup, flags=0):
     return wall_ms, ev_ms, info, steps, warmup
 
 
-def cpu_baseline(w, target_s=15.0):
-    """The oracle, as it stands, on a bounded row sample of workload w."""
-    import numpy as np
+# The oracle's threads: the GPU machine gives one GPU's job a 16-core share of its
+# host, whatever the machine reports in all (both counts are recorded).
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def host_cpu():
+    """What the CPU baseline ran on: the machine's CPU count, the cores this
+    process may use, and the CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def _oracle_rows(w, a, b, r0, nrows, threads):
+    """Seconds the oracle takes for output rows r0 .. r0+nrows-1 of workload
+    w (a GEMM: rows of C, whatever A's layout -- a row offset into A's storage
+    with the workload's strides; the attention scores: whole slices)."""
     import oracle
+    sa, sb = w.a_strides(), w.b_strides()
+    t = time.perf_counter()
+    if w.kind == "sscore":
+        s0, ns = r0 // w.M, nrows // w.M
+        oracle.sscore(a[s0 * sa[2]:], b[s0 * sb[2]:], ns, w.M, w.N, w.K, sa, sb, nthreads=threads)
+    else:
+        oracle.gemm(a[r0 * sa[0]:], b, 1, nrows, w.N, w.K, sa, sb, want_T=True, nthreads=threads)
+    return time.perf_counter() - t
+
+
+def cpu_baseline(w, target_s=15.0, single_thread_s=None):
+    """The oracle, as it stands, on a bounded sample of workload w's output
+    rows (the attention scores: whole slices), on ORACLE_THREADS threads;
+    with single_thread_s, also a single-thread run of about that long."""
     from workloads import bits, operands
     A, B = operands(w)
-    a, b = bits(A), bits(B)
-    threads = min(16, os.cpu_count() or 1)
-    sa, sb = w.a_strides(), w.b_strides()
+    a, b = bits(A).reshape(-1), bits(B).reshape(-1)
+    unit = w.M if w.kind == "sscore" else 1            # rows per sampling unit
+    total_rows = w.batch * w.M
+    flop_per_row = 2.0 * w.N * w.K
 
-    def rows_job(r0, nrows):
-        # rows r0 .. r0+nrows-1 of C: a row-major A slice is a contiguous block
-        if w.a_major != "row":
-            raise ValueError("row sampling needs a row-major A")
-        sub = a.reshape(w.M, w.K)[r0:r0 + nrows]
-        t = time.perf_counter()
-        oracle.gemm(sub, b, 1, nrows, w.N, w.K, sa, sb, want_T=True, nthreads=threads)
-        return time.perf_counter() - t
+    def sample(threads, seconds):
+        probe = max(unit, (threads + unit - 1) // unit * unit)
+        t_probe = _oracle_rows(w, a, b, 0, probe, threads)
+        n = int(probe * seconds / max(t_probe, 1e-3)) // probe * probe
+        n = max(0, min(n, total_rows - probe))
+        t_main = _oracle_rows(w, a, b, probe, n, threads) if n else 0.0
+        rows, secs = probe + n, t_probe + t_main
+        return rows, secs, rows * flop_per_row / secs / 1e12
 
-    probe_rows = threads
-    t_probe = rows_job(0, probe_rows)
-    nrows = max(threads, int(probe_rows * target_s / max(t_probe, 1e-3)) // threads * threads)
-    nrows = min(nrows, w.M - probe_rows)
-    t_main = rows_job(probe_rows, nrows)
-    total_rows = probe_rows + nrows
-    secs = t_probe + t_main
-    flop = 2.0 * total_rows * w.N * w.K
-    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d output rows of the %dx%dx%d product (fp64 oracle incl. the sum|a*b| pass), "
-                      "%.1f s" % (total_rows, w.M, w.M, w.N, w.K, secs)}
+    rows, secs, value = sample(ORACLE_THREADS, target_s)
+    what = ("%d of %d slices of the %d x %dx%dx%d scores" % (rows // w.M, w.batch, w.batch, w.M, w.N, w.K)
+            if w.kind == "sscore" else
+            "%d of %d output rows of the %dx%dx%d product" % (rows, w.M, w.M, w.N, w.K))
+    out = {"value": value, "unit": "TFLOP/s", "cores": ORACLE_THREADS, "kind": "oracle",
+           "sample": "%s (fp64 oracle incl. the sum|a*b| pass), %.1f s on %d threads"
+                     % (what, secs, ORACLE_THREADS)}
+    out.update(host_cpu())
+    if single_thread_s:
+        rows1, secs1, value1 = sample(1, single_thread_s)
+        out["single_thread"] = {"value": value1, "unit": "TFLOP/s", "rows": rows1, "seconds": round(secs1, 2)}
+    return out
 
 
 def cpu_baseline_attn(w, target_s=12.0):
@@ -289,7 +326,7 @@ def cpu_baseline_attn(w, target_s=12.0):
     import oracle
     from workloads import attn_operands, bits
     Q, K, V = (bits(t) for t in attn_operands(w))
-    threads = min(16, os.cpu_count() or 1)
+    threads = ORACLE_THREADS
     sq, sk, sv, _ = w.strides()
 
     order = np.random.default_rng(7).permutation(w.batch * w.Lq)  # rows of every cost, in any prefix
@@ -310,9 +347,11 @@ def cpu_baseline_attn(w, target_s=12.0):
     n = min(n, w.batch * w.Lq - probe)
     t_main, f_main = rows_job(probe, n)
     rows, secs, flop = probe + n, t_probe + t_main, f_probe + f_main
-    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d query rows (fp64 oracle incl. the sum p|v| pass), %.1f s"
-                      % (rows, w.batch * w.Lq, secs)}
+    out = {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": "%d of %d query rows (fp64 oracle incl. the sum p|v| pass), %.1f s on %d threads"
+                     % (rows, w.batch * w.Lq, secs, threads)}
+    out.update(host_cpu())
+    return out
 
 
 def tilecast_report(iters=5000):
@@ -488,8 +527,9 @@ def main():
     }
     if LAST_PER_LAUNCH:
         out["per_launch_ms"] = LAST_PER_LAUNCH
-    if not args.no_cpu_baseline and w.a_major == "row" and w.kind == "gemm":
-        out["cpu_baseline"] = cpu_baseline(w)
+    if not args.no_cpu_baseline:
+        # single-thread times too where they take seconds (512^3, the attention scores)
+        out["cpu_baseline"] = cpu_baseline(w, single_thread_s=(8.0 if w.flop < 1e11 else None))
     print(json.dumps(out))
 
 

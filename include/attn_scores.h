@@ -35,14 +35,21 @@
  * "M-major" (column-major A).  For B (K x N): row == 1 is "K-major" (B given
  * as its transpose, like K in Q.K^T), col == 1 is "N-major" (row-major B).
  * C must have col == 1.  The leading (non-unit) stride of every operand must
- * be a multiple of 8 elements and every base pointer 16-byte aligned.
+ * be a multiple of 8 elements, every base pointer 16-byte aligned, and every
+ * batch stride that is used (batch > 1) a multiple of 8 elements (fp32 C and
+ * O: 4), so that each batch origin starts a 16-byte chunk.
  *
  * Ownership.  The caller owns every device buffer; the library never
- * allocates, frees or keeps user memory.  A plan (as_gemm_t) is host memory
- * only; it may be destroyed as soon as gemm_run returns, because kernel
- * arguments are captured by value at launch.  `hip_stream` is the caller's
+ * allocates, frees or keeps user memory.  A plan (as_gemm_t) is host memory,
+ * plus a device workspace when it splits K (gemm_create below).  A plan
+ * without a split may be destroyed as soon as gemm_run returns, because
+ * kernel arguments are captured by value at launch; a split plan's launches
+ * use its workspace until they complete, so a split plan must outlive every
+ * HIP graph that recorded one of its runs.  `hip_stream` is the caller's
  * hipStream_t (NULL = the null stream); every run call is asynchronous on it
- * and never synchronizes.  Calls are thread-safe; as_last_error() is
+ * and never synchronizes.  Calls are thread-safe: a run holds the plan for
+ * as long as it reads it, so a gemm_destroy on another thread at the same
+ * time releases the plan only when that run returns.  as_last_error() is
  * per-thread.
  *
  * Errors.  Every entry point returns an as_status.  All argument checks
@@ -52,8 +59,8 @@
  *                       dtypes, a null or unknown plan
  *   AS_ERR_UNSUPPORTED  a well-formed request the kernels do not cover
  *                       (operand dtypes other than bf16, a contiguous stride
- *                       other than 1, unaligned pointers or leading strides,
- *                       K not a multiple of 8)
+ *                       other than 1, unaligned pointers, leading or batch
+ *                       strides, K not a multiple of 8)
  *   AS_ERR_HIP          a HIP launch error (the text is in as_last_error())
  *   AS_ERR_NOMEM        host allocation of a plan failed
  * Nothing is ever computed silently wrong: an unsupported case is refused.
@@ -150,13 +157,15 @@ AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, in
 /* Launch the planned product on `hip_stream`.  A, B: device bf16; C: device
  * fp32 or bf16 as planned.  Pointers must be 16-byte aligned.  A split plan
  * launches two kernels and, on its first run on a device, allocates its
- * workspace (AS_ERR_NOMEM if that fails).
- * Graph capture: the launches allocate, clear and synchronize nothing, so a
- * run may be recorded into a HIP graph on a capturing stream and replayed.
- * The one exception is a split plan's first run on a device: that run
- * allocates, so it must happen outside capture (inside, gemm_run returns
- * AS_ERR_UNSUPPORTED and records nothing).  A replay reuses the pointers
- * and the workspace of the recorded run. */
+ * workspace (hipMalloc; AS_ERR_NOMEM if that fails).
+ * Graph capture: the launches clear and synchronize nothing, so a run may be
+ * recorded into a HIP graph on a capturing stream and replayed.  A split
+ * plan's first run on a device allocates its workspace even while a stream
+ * records (with the calling thread's capture mode relaxed for the
+ * allocation, which is not a stream operation); a replay reuses the pointers
+ * and the workspace of the recorded run, so the plan must outlive the graph.
+ * A plan whose workspace lives on another device moves it only outside
+ * capture (inside, AS_ERR_UNSUPPORTED and nothing is recorded). */
 AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream);
 
 /* Whether a plan splits K: number of K chunks (1: no split) and the bytes
@@ -165,8 +174,12 @@ AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C,
 AS_API as_status gemm_plan_split_k(as_gemm_t plan, int32_t* splits, int64_t* workspace_bytes);
 
 /* Release a plan created by gemm_create (NULL or unknown -> AS_ERR_INVALID).
- * Frees a split plan's workspace (hipFree, which waits for the device).  The
- * handle is dead afterwards; a later gemm_create may return the same value. */
+ * Frees a split plan's workspace (hipFree, which waits for the device), so
+ * a graph that recorded a run of it must not be replayed afterwards, and a
+ * split plan must not be destroyed while a stream records a graph.  A run
+ * of the plan in progress on another thread keeps it until that run
+ * returns.  The handle is dead afterwards; a later gemm_create may return
+ * the same value. */
 AS_API as_status gemm_destroy(as_gemm_t plan);
 
 /* What a plan chose (for reporting): output tile shape and K stage depth,
@@ -217,7 +230,8 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
  * but do not write out.  One fused kernel: the scores stay in registers.
  *   Q [batch, Lq, d], K [batch, Lk, d], V [batch, Lk, dv], O [batch, Lq, dv],
  *   each addressed by (row, col, batch) element strides with col == 1;
- *   row strides multiples of 8 (O: 4), pointers 16-byte aligned.
+ *   row strides multiples of 8 (O: 4), pointers 16-byte aligned, batch
+ *   strides of the slices used multiples of 8 (O: 4).
  *   d == dv, 64 or 128.  Lq, Lk >= 1, any length.  qkv_t AS_BF16; o_t AS_BF16
  *   (round-to-nearest-even) or AS_F32.  scale finite.
  * Numerics: scores accumulate in fp32; probabilities are rounded to bf16
@@ -245,9 +259,12 @@ AS_API as_status sscore_run(const void* Q, const void* K, void* S,
  * bitwise the same O.  The queue counters live in the library (64 slots per
  * device, taken in turn by successive launches; each launch leaves its slot
  * at zero): at most 64 queue launches may run at once on one device.
- * Graph capture: a launch allocates and clears nothing, so it may be
- * recorded into a HIP graph and replayed; a recorded queue launch uses its
- * slot again on every replay.
+ * Graph capture: a launch allocates and clears nothing, so the default and
+ * the static schedules may be recorded into a HIP graph and replayed.  A
+ * queue launch takes its counters' slot at launch time, and a replay would
+ * reuse the recorded slot while an eager launch or another replay may hold
+ * it: AS_ATTN_SCHED_QUEUE on a capturing stream returns AS_ERR_UNSUPPORTED
+ * and records nothing.
  */
 #define AS_ATTN_CAUSAL 0x1u   /* attn_fwd_run: query i sees keys j <= i + (Lk - Lq) only */
 #define AS_ATTN_QUERIES_256 0x2u  /* force work items of 256 queries (each wave sweeps all keys) */

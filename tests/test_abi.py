@@ -364,8 +364,8 @@ def test_split_plan_slots_cover_every_chunk_and_tile():
 
 
 def test_python_plan_cache_is_bounded_and_keyed_by_stream():
-    # the cache keeps the last 64 plans and destroys the rest (their split-K
-    # workspaces with them); a different stream gets its own plan
+    # the cache keeps the last 64 plans and destroys the rest; a different
+    # stream gets its own plan
     asl._plan_cache.clear()
     first = asl.plan_for(256, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
     assert asl.plan_for(256, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1, stream=1) != first
@@ -389,3 +389,120 @@ def test_attn_gqa_argument_checks():
     assert st(kv_group=0) == asl.AS_ERR_INVALID
     assert st(kv_group=-2) == asl.AS_ERR_INVALID
     assert st(batch=6, kv_group=4) == asl.AS_ERR_INVALID     # must divide batch
+
+
+def test_python_plan_cache_keeps_evicted_split_plans():
+    # A graph may have recorded a run of an evicted split plan, and replays
+    # write into that plan's workspace: split plans are set aside, never
+    # destroyed, while plans without a split are destroyed.
+    asl._plan_cache.clear()
+    del asl._retired_split_plans[:]
+    split = asl.plan_for(1024, 1024, 8192, 1, (8192, 1, 0), (1024, 1, 0), (1024, 1, 0), 0, 0, 1)
+    assert asl.gemm_plan_split_k(split)[0] > 1
+    plain = asl.plan_for(256, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
+    destroyed = []
+    real_destroy = asl.gemm_destroy
+    asl.gemm_destroy = lambda p: (destroyed.append(p), real_destroy(p))
+    try:
+        for i in range(1, asl._PLAN_CACHE_SIZE + 1):
+            asl.plan_for(256 + 8 * i, 256, 64, 1, (64, 1, 0), (256, 1, 0), (256, 1, 0), 0, 0, 1)
+    finally:
+        asl.gemm_destroy = real_destroy
+    assert destroyed == [plain]
+    assert asl._retired_split_plans == [split]
+    assert asl.gemm_plan_split_k(split)[0] > 1          # still a live plan
+
+
+def test_batch_strides_must_start_16_byte_chunks():
+    # Each batch origin is read (and C written) in 16-byte pieces, so a batch
+    # stride that is used must be a multiple of 8 elements (fp32 C: 4).
+    mk = lambda a, b, c, batch=2, c_t=asl.AS_F32: _status(asl.gemm_create, 64, 64, 64, batch, a, b, c,
+                                                          asl.AS_BF16, asl.AS_BF16, c_t)
+    good_a, good_b, good_c = (64, 1, 64 * 64), (64, 1, 64 * 64), (64, 1, 64 * 64)
+    assert mk(good_a, good_b, good_c) == asl.AS_OK
+    assert mk((64, 1, 64 * 64 + 4), good_b, good_c) == asl.AS_ERR_UNSUPPORTED
+    assert "batch strides" in asl.as_last_error()
+    assert mk(good_a, (64, 1, 64 * 64 + 1), good_c) == asl.AS_ERR_UNSUPPORTED
+    assert mk(good_a, good_b, (64, 1, 64 * 64 + 4)) == asl.AS_OK                       # fp32 C: 4 suffices
+    assert mk(good_a, good_b, (64, 1, 64 * 64 + 2)) == asl.AS_ERR_UNSUPPORTED
+    assert mk(good_a, good_b, (64, 1, 64 * 64 + 4), c_t=asl.AS_BF16) == asl.AS_ERR_UNSUPPORTED
+    assert mk((64, 1, 4), good_b, good_c, batch=1) == asl.AS_OK                        # unused with one batch
+    assert mk((64, 1, 0), (64, 1, 0), good_c) == asl.AS_OK                             # broadcast
+    # attention scores: the same rule through sscore_run
+    d = 128
+    st = lambda q, k, s: _status(asl.sscore_run, 16, 32, 48, 2, 64, 64, d, q, k, s)
+    assert st((d, 1, 64 * d + 4), (d, 1, 64 * d), (64, 1, 64 * 64)) == asl.AS_ERR_UNSUPPORTED
+    assert st((d, 1, 64 * d), (d, 1, 64 * d + 2), (64, 1, 64 * 64)) == asl.AS_ERR_UNSUPPORTED
+    assert st((d, 1, 64 * d), (d, 1, 64 * d), (64, 1, 64 * 64 + 2)) == asl.AS_ERR_UNSUPPORTED
+    # fused attention: Q, K, V by 8 elements, O by 4, K and V only when several K/V slices are used
+    q = (d, 1, 256 * d)
+
+    def at(batch=4, kv_group=1, qs=q, ks=q, vs=q, os_=q, Q=16):
+        return _status(asl.attn_fwd_run_gqa, Q, 32, 48, 64, batch, kv_group, 256, 256, d, d, qs, ks, vs, os_, 0.1,
+                       asl.AS_BF16, asl.AS_BF16, 0)
+    odd = (d, 1, 256 * d + 4)
+    assert at(qs=odd) == asl.AS_ERR_UNSUPPORTED
+    assert at(ks=odd) == asl.AS_ERR_UNSUPPORTED
+    assert at(vs=(d, 1, 256 * d + 2)) == asl.AS_ERR_UNSUPPORTED
+    assert at(os_=(d, 1, 256 * d + 2)) == asl.AS_ERR_UNSUPPORTED
+    assert "batch strides" in asl.as_last_error()
+    # one shared K/V slice (kv_group == batch): its batch stride is never used,
+    # so the call passes that check and stops at the next one (a misaligned
+    # Q pointer; no call here may pass every check with these fake pointers)
+    assert at(kv_group=4, ks=odd, vs=odd, Q=24) == asl.AS_ERR_UNSUPPORTED
+    assert "16-byte aligned" in asl.as_last_error()
+
+
+def test_plans_survive_concurrent_destroy():
+    # Threads create plans, run them (null device pointers: the run reads
+    # the plan, then rejects the pointers before any HIP call) and destroy
+    # them, while other threads run and destroy the same handles.  Every call
+    # must return a status -- a run sees either a live plan (null-pointer
+    # error) or an unknown one -- and nothing may crash.
+    import threading
+    L = asl.lib()
+    shared, lock, errors = [], threading.Lock(), []
+    S = asl.Strides
+
+    def creator(n):
+        for i in range(n):
+            h = ctypes.c_void_p()
+            K = 8192 if i % 3 == 0 else 512                  # every third plan splits K
+            rc = L.gemm_create(ctypes.byref(h), 1024, 1024, K, 1, S(K, 1, 0), S(1024, 1, 0), S(1024, 1, 0),
+                               0, 0, 1, 0)
+            if rc != asl.AS_OK:
+                errors.append(("create", rc))
+                continue
+            with lock:
+                shared.append(h.value)
+            if L.gemm_run(h.value, None, None, None, None) != asl.AS_ERR_INVALID:
+                errors.append(("run own", rc))
+
+    def runner(n):
+        for _ in range(n):
+            with lock:
+                h = shared[-1] if shared else None
+            if h is not None and L.gemm_run(h, None, None, None, None) != asl.AS_ERR_INVALID:
+                errors.append(("run shared",))
+
+    def destroyer(n):
+        done = 0
+        while done < n:
+            with lock:
+                h = shared.pop(0) if shared else None
+            if h is None:
+                continue
+            if L.gemm_destroy(h) != asl.AS_OK:
+                errors.append(("destroy",))
+            done += 1
+
+    n = 400
+    threads = [threading.Thread(target=creator, args=(n,)) for _ in range(2)] + \
+              [threading.Thread(target=runner, args=(2 * n,)) for _ in range(3)] + \
+              [threading.Thread(target=destroyer, args=(n,)) for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
+    assert not shared

@@ -315,6 +315,64 @@ def test_check_accepts_and_rejects():
     assert oracle.check(inf, ref, T)[0] == 1
 
 
+def test_rne_array_equals_the_pinned_scalar():
+    # The vector rounding used by every bf16 bit-exact comparison is the
+    # scalar rule pinned above (hand-worked fixtures and torch's cast),
+    # element by element: the golden values, torch's tie set, specials.
+    golden = [float(eval(e, {"__builtins__": {}})) for e, _ in _read_pairs("bf16_rne.txt")]
+    want_golden = [int(h, 16) for _, h in _read_pairs("bf16_rne.txt")]
+    g = torch.Generator().manual_seed(11)
+    ties = torch.randn(3000, generator=g).to(torch.bfloat16).double()
+    ties = torch.cat([ties + ties.abs() * 2.0 ** -8, ties - ties.abs() * 2.0 ** -9,
+                      torch.randn(3000, generator=g, dtype=torch.float64) * 1e3])
+    x = np.concatenate([np.array(golden), ties.numpy(), [0.0, -0.0, np.inf, -np.inf, np.nan, 1e300, -1e-300]])
+    arr = oracle.f64_to_bf16_rne_array(x)
+    sca = np.array([oracle.f64_to_bf16_rne(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(arr, sca)
+    assert list(arr[:len(golden)]) == want_golden
+    # shape is kept and torch agrees on the float32-representable part
+    x2 = ties.numpy()[:3000].reshape(30, 100)
+    a2 = oracle.f64_to_bf16_rne_array(x2)
+    assert a2.shape == (30, 100)
+    assert np.array_equal(a2, bits(torch.from_numpy(x2).float().to(torch.bfloat16)))
+
+
+def test_check_attention_accepts_rounded_probabilities_and_rejects_beyond():
+    # What the attention tolerance is for: a result whose probabilities were
+    # rounded to bf16 before the P.V product (simulated here with torch's
+    # independent bf16 cast, normalised by the unrounded sum) must pass, with
+    # room to spare; results moved past the bound must fail; NaN and Inf fail;
+    # a bf16 output gets its own rounding (2^-8 |O|) on top.
+    rng = np.random.default_rng(5)
+    n, Lk, dv = 64, 300, 16
+    t = rng.normal(0, 3, (n, Lk))
+    p = np.exp(t - t.max(axis=1, keepdims=True))
+    V = rng.normal(0, 1, (Lk, dv))
+    O_ref = p @ V / p.sum(axis=1, keepdims=True)
+    TO = p @ np.abs(V) / p.sum(axis=1, keepdims=True)
+    p_bf = torch.from_numpy(p).to(torch.bfloat16).double().numpy()
+    O_fused = p_bf @ V / p.sum(axis=1, keepdims=True)
+    nfail, util = oracle.check_attention(O_fused, O_ref, TO)
+    assert nfail == 0 and util <= 0.5                     # rounding p costs at most 2^-8 TO: half the bound
+    bound = 2.0 ** -7 * TO + 1e-6
+    assert oracle.check_attention(O_ref + 0.99 * bound, O_ref, TO)[0] == 0
+    assert oracle.check_attention(O_ref - 1.01 * bound, O_ref, TO)[0] == O_ref.size
+    moved = O_ref.copy()
+    moved[3, 5] += 1.01 * bound[3, 5]
+    assert oracle.check_attention(moved, O_ref, TO)[0] == 1
+    for special in (np.nan, np.inf, -np.inf):
+        bad = O_fused.copy()
+        bad[7, 2] = special
+        assert oracle.check_attention(bad, O_ref, TO)[0] == 1
+    # bf16 output: the stored value is RNE(O), which may sit 2^-9 |O| away
+    O_out = torch.from_numpy(O_fused).to(torch.bfloat16).double().numpy()
+    assert oracle.check_attention(O_out, O_ref, TO, out_bf16=True)[0] == 0
+    extra = 2.0 ** -8 * np.abs(O_ref)
+    edge = O_ref + bound + 0.5 * extra
+    assert oracle.check_attention(edge, O_ref, TO, out_bf16=True)[0] == 0
+    assert oracle.check_attention(edge, O_ref, TO, out_bf16=False)[0] == np.count_nonzero(extra > 0)
+
+
 # ----------------------------------------------------- tile fan-out bench --
 
 def test_tilecast_accounting_matches_printed_run():

@@ -2,10 +2,14 @@
 
 Bars: bit-exact where the arithmetic is exact (integer-valued data, identity
 operands, checksums); otherwise |C_gpu - C_ref| <= 1e-3 * sum_k|a*b| + 1e-5
-per element.  Full checks at sizes the oracle finishes in seconds (several
-tiles, odd tile counts); at the full workload sizes, seeded samples of output
-elements that the oracle computes one by one, plus the tile corners.
+per element.  Every element is compared: at sizes the oracle finishes in
+seconds (several tiles, odd tile counts, the 256 x 256 kernel at full K
+depth), and at the five workloads' full sizes, where the oracle computes the
+whole product in row blocks on the host's cores.  Only the 8 GiB-output and
+one-workgroup-per-tile ablation cases compare seeded samples.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -28,6 +32,11 @@ def _need_gpu():
 
 def _say(msg):
     print("[case] " + msg, flush=True)
+
+
+# Oracle threads: the GPU machine's share of its host is 16 cores, whatever the
+# machine reports in all.
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def _decode(out: torch.Tensor) -> np.ndarray:
@@ -204,12 +213,6 @@ def test_split_k_random_data_within_tolerance_and_deterministic(M, N, K, a_k, b_
     _check_full(unsplit, Cref, T)
 
 
-def test_split_k_shard_workload_sampled():
-    w = WORKLOADS["gemm4096x2048x8192"]
-    _say("%s full size, sampled" % w.name)
-    _sampled_gemm(w)
-
-
 # -------------------------------------------------- workloads, full checks --
 
 def _check_full(C, Cref, T):
@@ -227,22 +230,41 @@ def test_gemm512_full():
     _check_full(C, Cref, T)
 
 
-@pytest.mark.parametrize("name,M,N,K,batch", [
-    ("gemm8192", 1024, 1024, 1024, 1),
-    ("gemm65536x256x4096", 4096, 256, 1024, 1),
-    ("gemm16384x8192x2048_colA", 1024, 512, 512, 1),
+@pytest.mark.parametrize("name,M,N,K", [
+    ("gemm8192", 1024, 1024, 8192),             # 16 tiles, 128 K stages each
+    ("gemm65536x256x4096", 8192, 256, 4096),    # one tile column: rotated K loop, non-temporal A
+    ("gemm16384x8192x2048_colA", 2048, 1024, 2048),
 ])
-def test_workload_distribution_reduced_full(name, M, N, K, batch):
-    """Same layouts, value distribution and output type as the full workload, at an oracle-sized shape."""
+def test_workload_kernel_reduced_full(name, M, N, K):
+    """The full workload's kernel -- 256 x 256 tiles, 8 waves of 16x16x32
+    MFMAs, its operand layouts, value distribution and output type, the
+    workload's full K depth -- on fewer tiles, every element against the
+    oracle.  K is not split, so the tile's whole K loop runs as it does at
+    full size."""
     w = WORKLOADS[name]
-    _say("%s reduced %dx%dx%d" % (name, M, N, K))
+    _say("%s kernel at %dx%dx%d" % (name, M, N, K))
     a_k = w.a_major == "row"
-    a_shape, sa, b_shape, sb = _layout(M, N, K, batch, a_k, False)
+    a_shape, sa, b_shape, sb = _layout(M, N, K, 1, a_k, False)
     A = draw(a_shape, w.dist, w.lo, w.hi, w.seeds[0] + 1000)
     B = draw(b_shape, w.dist, w.lo, w.hi, w.seeds[1] + 1000)
+    flags = asl.AS_FLAG_TILE_256 | asl.AS_FLAG_NO_SPLIT_K
+    plan = asl.gemm_create(M, N, K, 1, sa, sb, (N, 1, M * N), asl.AS_BF16, asl.AS_BF16,
+                           asl.AS_BF16 if w.out == "bf16" else asl.AS_F32, flags)
+    try:
+        assert asl.gemm_plan_info(plan)[:3] == (256, 256, 64)
+        assert asl.gemm_plan_split_k(plan)[0] == 1
+    finally:
+        asl.gemm_destroy(plan)
+    # the full workload plans the same tile
+    full = asl.gemm_create(w.M, w.N, w.K, 1, w.a_strides(), w.b_strides(), (w.N, 1, w.M * w.N), asl.AS_BF16,
+                           asl.AS_BF16, asl.AS_BF16 if w.out == "bf16" else asl.AS_F32)
+    try:
+        assert asl.gemm_plan_info(full)[:3] == (256, 256, 64) and asl.gemm_plan_split_k(full)[0] == 1
+    finally:
+        asl.gemm_destroy(full)
     od = torch.bfloat16 if w.out == "bf16" else torch.float32
-    C = _run_gemm(A, B, M, N, K, batch, sa, sb, od)
-    Cref, T = oracle.gemm(bits(A), bits(B), batch, M, N, K, sa, sb)
+    C = _run_gemm(A, B, M, N, K, 1, sa, sb, od, flags)
+    Cref, T = oracle.gemm(bits(A), bits(B), 1, M, N, K, sa, sb, nthreads=ORACLE_THREADS)
     _check_full(C, Cref, T)
 
 
@@ -269,13 +291,13 @@ def test_sscore_symmetric_when_Q_is_K():
     assert np.all(np.abs(s - np.transpose(s, (0, 2, 1))) <= 2 * (1e-3 * T + 1e-5))
 
 
-# ------------------------------------------------ full sizes, sampled checks --
+# ---------------------------------------------- full sizes, every element --
 
 N_SAMPLES = 4000
+ROW_BLOCK = 1024      # output rows per oracle call (bounds host memory)
 
 
-def _sampled_gemm(w, flags=0, out=None):
-    A, B = operands(w)
+def _gemm_on_gpu(w, A, B, flags=0):
     od = torch.bfloat16 if w.out == "bf16" else torch.float32
     Ad, Bd = A.to(DEV), B.to(DEV)
     C = torch.empty((w.batch, w.M, w.N), dtype=od, device=DEV)
@@ -286,38 +308,78 @@ def _sampled_gemm(w, flags=0, out=None):
         torch.cuda.synchronize()
     finally:
         asl.gemm_destroy(plan)
+    del Ad, Bd
+    return C
+
+
+def _full_compare(w, C, A, B):
+    """Every element of C against the oracle, ROW_BLOCK output rows at a
+    time (a row block of A is a view into its storage: a row offset with the
+    workload's own strides)."""
+    a = bits(A).reshape(-1)
+    b = bits(B)
+    sa, sb = w.a_strides(), w.b_strides()
+    row_step = sa[0]                     # elements from one row of A to the next
+    worst, checked = 0.0, 0
+    for bi in range(w.batch):
+        for r0 in range(0, w.M, ROW_BLOCK):
+            r1 = min(w.M, r0 + ROW_BLOCK)
+            sub = a[bi * sa[2] + r0 * row_step:]
+            Cref, T = oracle.gemm(sub, b[bi * sb[2]:] if sb[2] else b, 1, r1 - r0, w.N, w.K, sa, sb,
+                                  nthreads=ORACLE_THREADS)
+            got = _decode(C[bi, r0:r1])
+            nfail, util = oracle.check(got, Cref[0], T[0])
+            assert nfail == 0, "batch %d rows %d..%d: %d elements outside tolerance (max util %.3g)" % (
+                bi, r0, r1, nfail, util)
+            worst = max(worst, util)
+            checked += got.size
+    assert checked == w.batch * w.M * w.N
+    return worst
+
+
+@pytest.mark.timeout(900)     # the oracle takes tens of seconds for 8192^3 on 16 cores
+@pytest.mark.parametrize("name", ["gemm8192", "gemm65536x256x4096", "gemm16384x8192x2048_colA",
+                                  "gemm4096x2048x8192"])
+def test_full_size_every_element(name):
+    """The workload as the benchmark runs it (default plan, inputs of the
+    benchmark's seeds), every output element against the oracle."""
+    w = WORKLOADS[name]
+    _say("%s full size, every element (oracle on %d threads)" % (name, ORACLE_THREADS))
+    A, B = operands(w)
+    C = _gemm_on_gpu(w, A, B)
+    util = _full_compare(w, C, A, B)
+    _say("%s max tolerance use %.3g" % (name, util))
+
+
+def _sampled_gemm(w, flags=0):
+    A, B = operands(w)
+    C = _gemm_on_gpu(w, A, B, flags)
     pts = sample_points(w.batch, w.M, w.N, N_SAMPLES, seed=w.seeds[0] * 7)
     idx = torch.from_numpy(pts).to(DEV)
     got = _decode(C[idx[:, 0], idx[:, 1], idx[:, 2]])
     Cref, T = oracle.gemm_points(bits(A), bits(B), pts, w.K, w.a_strides(), w.b_strides(),
-                                 dims=(w.batch, w.M, w.N))
+                                 dims=(w.batch, w.M, w.N), nthreads=ORACLE_THREADS)
     nfail, util = oracle.check(got, Cref, T)
     assert nfail == 0, "%d sampled elements outside tolerance (max util %.3g)" % (nfail, util)
     return C
 
 
-@pytest.mark.parametrize("name", ["gemm8192", "gemm65536x256x4096", "gemm16384x8192x2048_colA"])
-def test_full_size_sampled(name):
-    w = WORKLOADS[name]
-    _say("%s full size, sampled" % name)
-    _sampled_gemm(w)
-
-
-def test_sscore_full_size_sampled_and_deterministic():
+@pytest.mark.timeout(600)
+def test_sscore_full_size_every_element_and_deterministic():
     w = WORKLOADS["sscore32x2048"]
-    _say("sscore full size")
+    _say("sscore full size, every element")
     Q, K = operands(w)
     Qd, Kd = Q.to(DEV), K.to(DEV)
     S1 = asl.sscore(Qd, Kd)
     S2 = asl.sscore(Qd, Kd)
     torch.cuda.synchronize()
     assert torch.equal(S1, S2)
-    pts = sample_points(w.batch, w.M, w.N, N_SAMPLES, seed=w.seeds[0] * 7)
-    idx = torch.from_numpy(pts).to(DEV)
-    got = _decode(S1[idx[:, 0], idx[:, 1], idx[:, 2]])
-    Sref, T = oracle.sscore_points(bits(Q), bits(K), pts, w.K, w.a_strides(), w.b_strides())
-    nfail, util = oracle.check(got, Sref, T)
-    assert nfail == 0, "%d sampled elements outside tolerance (max util %.3g)" % (nfail, util)
+    q, k = bits(Q).reshape(w.batch, -1), bits(K).reshape(w.batch, -1)
+    sq, sk = w.a_strides(), w.b_strides()
+    for b in range(w.batch):
+        Sref, T = oracle.sscore(q[b], k[b], 1, w.M, w.N, w.K, sq, sk, nthreads=ORACLE_THREADS)
+        nfail, util = oracle.check(_decode(S1[b]), Sref[0], T[0])
+        assert nfail == 0, "slice %d: %d elements outside tolerance (max util %.3g)" % (b, nfail, util)
 
 
 def test_grouping_ablation_is_bitwise_identical():
@@ -588,24 +650,27 @@ def test_rotated_k_bit_exact(M, N, K, batch, flags, a_k, b_k, out):
 
 
 def test_rotated_k_random_data_within_tolerance_and_deterministic():
-    """The tall-skinny shape at reduced height with N(0,1) data: the default
-    plan (rotated, non-temporal A) and the unrotated ablation are both within
-    tolerance of the oracle, and the default plan repeats bit for bit."""
-    M, N, K = 4096, 256, 4096
+    """The tall-skinny workload's kernel at reduced height with N(0,1) data:
+    one 256-wide tile column, so the default plan streams A (rotated K loop,
+    non-temporal loads).  Default and forced rotation give the same bits, the
+    unrotated ablation sums in another order (different bits), and both are
+    within tolerance of the oracle at every element."""
+    M, N, K = 8192, 256, 4096
     A = draw((1, M, K), "normal", 0, 1, 411)
     B = draw((1, K, N), "normal", 0, 1, 412)
     sa, sb = (K, 1, M * K), (N, 1, K * N)
-    pts = sample_points(1, M, N, 768, 78)
-    Cref, T = oracle.gemm_points(bits(A), bits(B), pts, K, sa, sb, dims=(1, M, N))
-    runs = []
-    for flags in (0, 0, asl.AS_FLAG_NO_ROTATE_K):
-        _say("rotate tolerance flags=0x%x" % flags)
+    Cref, T = oracle.gemm(bits(A), bits(B), 1, M, N, K, sa, sb, nthreads=ORACLE_THREADS)
+    base = asl.AS_FLAG_TILE_256 | asl.AS_FLAG_NO_SPLIT_K
+    runs = {}
+    for name, flags in (("default", base), ("again", base), ("rotate", base | asl.AS_FLAG_ROTATE_K),
+                        ("unrotated", base | asl.AS_FLAG_NO_ROTATE_K)):
+        _say("rotate tolerance %s flags=0x%x" % (name, flags))
         C = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, flags)
-        got = C.double().cpu().numpy()[0][pts[:, 1], pts[:, 2]]
-        nfail, util = oracle.check(got, Cref, T)
-        assert nfail == 0, "flags 0x%x: %d sampled elements outside tolerance (max util %.3g)" % (flags, nfail, util)
-        runs.append(C)
-    assert torch.equal(runs[0].view(torch.int32), runs[1].view(torch.int32))
+        _check_full(C, Cref, T)
+        runs[name] = C.view(torch.int32)
+    assert torch.equal(runs["default"], runs["again"])
+    assert torch.equal(runs["default"], runs["rotate"])
+    assert not torch.equal(runs["default"], runs["unrotated"])
 
 
 # --------------------------------------------------- randomized shape sweep --
