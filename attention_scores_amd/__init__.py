@@ -5,7 +5,7 @@ kernels behind the C ABI.  torch supplies device memory and the current
 stream; nothing here computes on the CPU, and there is no fallback path --
 if the library has not been built, every call raises.
 
-Low-level names mirror the C ABI (``gemm_create``, ``gemm_run``,
+Low-level names mirror the C ABI (``gemm_create``, ``gemm_run``, ``gemm_run_no_alloc``,
 ``gemm_destroy``, ``gemm_plan_info``, ``gemm_plan_tile_of``, ``sscore_run``,
 ``tilecast_run``, ``as_status_str``, ``as_last_error``) and take raw device
 pointers.  ``gemm``, ``sscore`` and ``tilecast`` are tensor conveniences that
@@ -39,7 +39,7 @@ AS_ATTN_QUERIES_128 = 0x4
 AS_ATTN_SCHED_STATIC = 0x8
 AS_ATTN_SCHED_QUEUE = 0x10
 
-EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of", "gemm_plan_split_k",
+EXPORTED = ("gemm_create", "gemm_run", "gemm_run_no_alloc", "gemm_destroy", "gemm_plan_info", "gemm_plan_tile_of", "gemm_plan_split_k",
             "sscore_run", "attn_fwd_run", "attn_fwd_run_gqa", "attn_fwd_plan_info", "tilecast_run", "as_status_str",
             "as_last_error")
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_create.restype = ctypes.c_int
         L.gemm_run.argtypes = [vp, vp, vp, vp, vp]
         L.gemm_run.restype = ctypes.c_int
+        L.gemm_run_no_alloc.argtypes = [vp, vp, vp, vp, vp]
+        L.gemm_run_no_alloc.restype = ctypes.c_int
         L.gemm_destroy.argtypes = [vp]
         L.gemm_destroy.restype = ctypes.c_int
         L.gemm_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -138,6 +140,12 @@ def gemm_create(M: int, N: int, K: int, batch: int, a: Tuple[int, int, int], b: 
 
 def gemm_run(plan: int, A: int, B: int, C: int, stream: int = 0) -> None:
     _check(lib().gemm_run(plan, A, B, C, stream))
+
+
+def gemm_run_no_alloc(plan: int, A: int, B: int, C: int, stream: int = 0) -> None:
+    """gemm_run that allocates nothing: a split plan uses the library's static
+    per-GPU scratch array (calls overlapping on one GPU race; see the header)."""
+    _check(lib().gemm_run_no_alloc(plan, A, B, C, stream))
 
 
 def gemm_destroy(plan: int) -> None:

@@ -397,6 +397,26 @@ as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* 
     return ok();
 }
 
+as_status gemm_run_no_alloc(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream) {
+    const std::shared_ptr<as_gemm_plan> p = acquire(plan);
+    if (!p) return fail(AS_ERR_INVALID, "null or unknown plan");
+    const asl::GemmDesc& d = p->d;
+    if (d.splits == 1) return run_desc(d, A, B, C, hip_stream);   // no workspace: gemm_run itself
+    if (!A || !B || !C) return fail(AS_ERR_INVALID, "null device pointer");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C))
+        return fail(AS_ERR_UNSUPPORTED, "device pointers must be 16-byte aligned");
+    if (d.ws_bytes > asl::kScratchBytes)
+        return fail(AS_ERR_UNSUPPORTED, "split-K workspace of %" PRId64 " bytes exceeds the %" PRId64
+                    "-byte static scratch array", d.ws_bytes, asl::kScratchBytes);
+    void* ws = nullptr;
+    if (int e = asl::scratch_address(&ws); e != 0)
+        return fail(AS_ERR_HIP, "scratch array address: HIP error %d", e);
+    int e = asl::launch_gemm(split_launch_desc(d), A, B, ws, hip_stream);
+    if (e == 0) e = asl::launch_splitk_reduce(d, ws, C, hip_stream);
+    if (e != 0) return fail(AS_ERR_HIP, "kernel launch failed: HIP error %d", e);
+    return ok();
+}
+
 as_status gemm_destroy(as_gemm_t plan) {
     std::shared_ptr<as_gemm_plan> p;
     {

@@ -40,6 +40,17 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
 // rounded to C's type.  Returns 0 or a hipError_t value.
 int launch_splitk_reduce(const GemmDesc& d, const void* ws, void* C, void* stream);
 
+// Bytes of the static split-K scratch array (per GPU) that gemm_run_no_alloc
+// uses instead of a plan's own workspace.  It holds every workspace the
+// planner makes: K is split only when tiles x chunks fit the 256-workgroup
+// resident grid (256 x 256 x 256 x 4 bytes) or the 512-workgroup one of
+// 128 x 128 tiles (half that).
+constexpr int64_t kScratchBytes = INT64_C(64) << 20;
+
+// Device address of the scratch array on the current device (looked up once
+// per device).  Returns 0 or a hipError_t value.
+int scratch_address(void** out);
+
 // Tile computed in execution slot i (round i div grid of workgroup i mod
 // grid; the device schedule, shared with the kernels).  False if empty.
 bool tile_of_slot(const GemmDesc& d, int64_t i, int64_t* b, int64_t* tm, int64_t* tn);

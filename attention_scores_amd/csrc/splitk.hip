@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.hpp"
 #include "tile.hpp"
@@ -52,7 +53,39 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     }
 }
 
+// Split-K workspace for callers that cannot allocate device memory
+// (gemm_run_no_alloc): one array per GPU, which the GPU holds from the
+// loading of the code object until the process ends.  Host code must never
+// pass the name itself to a kernel (on the host it is only a stand-in, not
+// the device address): scratch_address() looks up each device's address.
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 }  // namespace kern
+
+int scratch_address(void** out) {
+    // Device addresses of the array, looked up once per device with that
+    // device current (each GPU has its own copy at its own address).
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        // Not a stream operation: allowed while a stream of this thread records.
+        hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+        (void)hipThreadExchangeStreamCaptureMode(&mode);
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(kern::scratch));
+        (void)hipThreadExchangeStreamCaptureMode(&mode);
+        if (e != hipSuccess) return (int)e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return 0;
+}
 
 int launch_splitk_reduce(const GemmDesc& d, const void* ws, void* C, void* stream) {
     const int64_t groups = d.ws_ld / 4, total = d.M * groups;   // < 2^31: split plans are small grids

@@ -168,6 +168,23 @@ AS_API as_status gemm_create(as_gemm_t* out, int64_t M, int64_t N, int64_t K, in
  * capture (inside, AS_ERR_UNSUPPORTED and nothing is recorded). */
 AS_API as_status gemm_run(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): gemm_run
+ * without any allocation.  A plan that does not split K runs exactly as in
+ * gemm_run.  A split plan's partial sums go to the library's static scratch
+ * array instead of the plan's own workspace: 64 MiB of device memory per
+ * GPU, held from the loading of the library's kernels until the process
+ * ends, which covers every workspace the planner makes (gemm_plan_split_k
+ * reports the bytes; a larger one would be refused with
+ * AS_ERR_UNSUPPORTED).  The first call on a device looks up that device's
+ * array address (hipGetSymbolAddress; no allocation).  Every call on a GPU
+ * shares its one array, which keeps the last call's contents (nothing in it
+ * needs to start at zero): calls that overlap on one GPU -- on different
+ * streams, or from threads whose calls are not otherwise ordered -- race and
+ * give wrong results; calls on one stream are ordered and safe.  Results
+ * are bitwise those of gemm_run.  Errors as for gemm_run. */
+AS_API as_status gemm_run_no_alloc(as_gemm_t plan, const void* A, const void* B, void* C, void* hip_stream);
+
 /* Whether a plan splits K: number of K chunks (1: no split) and the bytes
  * of device workspace its runs use (0 without a split).  Any output pointer
  * may be NULL.  AS_ERR_INVALID on a bad plan. */
