@@ -33,6 +33,7 @@ AS_FLAG_NT_A = 0x20
 AS_FLAG_NO_NT_A = 0x40
 AS_FLAG_ROTATE_K = 0x80
 AS_FLAG_NO_ROTATE_K = 0x100
+AS_FLAG_NO_XCD_SPLIT = 0x200
 AS_ATTN_CAUSAL = 0x1
 AS_ATTN_QUERIES_256 = 0x2
 AS_ATTN_QUERIES_128 = 0x4

@@ -72,7 +72,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 |
                                  AS_FLAG_ONE_TILE_PER_WORKGROUP | AS_FLAG_NO_SPLIT_K | AS_FLAG_NT_A |
-                                 AS_FLAG_NO_NT_A | AS_FLAG_ROTATE_K | AS_FLAG_NO_ROTATE_K;
+                                 AS_FLAG_NO_NT_A | AS_FLAG_ROTATE_K | AS_FLAG_NO_ROTATE_K | AS_FLAG_NO_XCD_SPLIT;
 constexpr int64_t kBK = asl::kTileK;
 constexpr int64_t kCus = 256;   // MI355X compute units
 constexpr int64_t kMinSplitK = 1024;   // shallowest K chunk of a split product
@@ -206,6 +206,7 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         return fail(AS_ERR_UNSUPPORTED, "too many output tiles");
     d.tiles = batch * d.tiles_m * d.tiles_n;
     d.grouped = !(flags & AS_FLAG_NO_GROUPING);
+    d.xcd_split = d.grouped && !(flags & AS_FLAG_NO_XCD_SPLIT);
     // With one tile column every A row panel has a single consumer: A
     // streams from HBM once while every tile re-reads all of B.  A's loads
     // then carry the non-temporal hint (its lines leave L2 before B's), and

@@ -59,7 +59,7 @@ struct KArgs {
     int64_t M, N, K;      // problem sizes (edge tiles are partial)
     int32_t ktiles;       // ceil(K / BK) stages per tile
     int32_t krem;         // K mod BK: valid k of the last stage (0: the last stage is full)
-    int32_t tiles, tiles_m, tiles_n, group_m, grouped;
+    int32_t tiles, tiles_m, tiles_n, group_m, grouped, xcd_split;
     int32_t rotate;       // tile row tm starts its K loop at stage tm mod ktiles
 };
 
@@ -489,7 +489,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
 
     // The logical tiles this workgroup visits: first, first + stride, ... < end.
     int first, stride, end;
-    tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, a.grouped != 0, first, stride, end);
+    tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, a.xcd_split != 0, first, stride, end);
     if (first >= end) return;
 
     StageCursor<TILE, BK, A_K, B_K, RAGGED> cur_ld(a, first, stride, end);
@@ -668,7 +668,8 @@ int launch_tile(const GemmDesc& d, const KArgs& k, hipStream_t s) {
 
 bool tile_of_slot(const GemmDesc& d, int64_t i, int64_t* b, int64_t* tm, int64_t* tn) {
     int64_t bb, m, n;
-    if (!asl::tile_of_slot<int64_t>(i, d.grid, d.tiles, d.tiles_m, d.tiles_n, d.group_m, d.grouped, bb, m, n))
+    if (!asl::tile_of_slot<int64_t>(i, d.grid, d.tiles, d.tiles_m, d.tiles_n, d.group_m, d.grouped, d.xcd_split, bb,
+                                    m, n))
         return false;
     *b = bb;
     *tm = m;
@@ -697,6 +698,7 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
     k.tiles_n = (int32_t)d.tiles_n;
     k.group_m = d.group_m;
     k.grouped = d.grouped ? 1 : 0;
+    k.xcd_split = d.xcd_split ? 1 : 0;
     k.rotate = d.rotate_k ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
     if (d.tile == 256) return launch_tile<256>(d, k, s);

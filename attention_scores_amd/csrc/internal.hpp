@@ -20,7 +20,8 @@ struct GemmDesc {
     bool c_bf16;                     // output rounded to bf16 (else fp32)
     int tile;                        // 256 or 128 (square output tile)
     int group_m;                     // rows of tiles per group in the grouped order
-    bool grouped;                    // XCD-aware grouped order (false: identity)
+    bool grouped;                    // band order of group_m tile rows (false: row-major, the identity)
+    bool xcd_split;                  // each XCD walks a contiguous range of that order
     bool nt_a;                       // A's loads carry the non-temporal hint (A streams)
     bool rotate_k;                   // tile row tm starts its K loop at stage tm mod (K stages)
     int64_t tiles_m, tiles_n, tiles; // output tiles

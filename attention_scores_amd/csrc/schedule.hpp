@@ -28,8 +28,12 @@
 //   2. Grouped order inside a batch: logical tiles walk a band of group_m
 //      tile rows column by column, so the ~32 tiles an XCD runs at once span
 //      group_m A row-panels and 32/group_m B column-panels.
-// With grouping off (the ablation) workgroup h takes tiles h, h + P, ... in
-// row-major tile order.  Every tile is visited exactly once.
+// Two ablations: with grouping off, workgroup h takes tiles h, h + P, ... in
+// row-major tile order; without the XCD split (step 1 skipped), workgroup h
+// takes logical tiles h, h + P, ... of the grouped order of step 2, so
+// consecutive tiles of a band run on different XCDs (the band order of a
+// GPU whose workgroups all share one L2).  Every tile is visited exactly
+// once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,10 +72,10 @@ __host__ __device__ inline void logical_tile(I L, I tiles_m, I tiles_n, I group_
 }
 
 // Logical tiles workgroup h of a P-workgroup grid visits: first, first +
-// stride, ... while < end.
+// stride, ... while < end.  xcd_split: each XCD walks its own range (step 1).
 template <typename I>
-__host__ __device__ inline void tile_walk(I h, I P, I tiles, bool grouped, I& first, I& stride, I& end) {
-    if (!grouped) {
+__host__ __device__ inline void tile_walk(I h, I P, I tiles, bool xcd_split, I& first, I& stride, I& end) {
+    if (!xcd_split) {
         first = h;
         stride = P;
         end = tiles;
@@ -89,11 +93,11 @@ __host__ __device__ inline void tile_walk(I h, I P, I tiles, bool grouped, I& fi
 // i < tiles; returns false if that slot is empty.  Slot i runs on XCD i mod 8
 // when P is a multiple of 8 or P == tiles.
 template <typename I>
-__host__ __device__ inline bool tile_of_slot(I i, I P, I tiles, I tiles_m, I tiles_n, I group_m, bool grouped, I& b,
-                                             I& tm, I& tn) {
+__host__ __device__ inline bool tile_of_slot(I i, I P, I tiles, I tiles_m, I tiles_n, I group_m, bool grouped,
+                                             bool xcd_split, I& b, I& tm, I& tn) {
     const I h = i % P, j = i / P;
     I first, stride, end;
-    tile_walk<I>(h, P, tiles, grouped, first, stride, end);
+    tile_walk<I>(h, P, tiles, xcd_split, first, stride, end);
     const I L = first + j * stride;
     if (L >= end) return false;
     logical_tile<I>(L, tiles_m, tiles_n, group_m, grouped, b, tm, tn);

@@ -92,7 +92,10 @@ def _gpu_inputs(w, dev):
 
 def _plan(asl, w, flags=0):
     c_t = asl.AS_BF16 if w.out == "bf16" else asl.AS_F32
-    return asl.gemm_create(w.M, w.N, w.K, w.batch, w.a_strides(), w.b_strides(), (w.N, 1, w.M * w.N),
+    sb = w.b_strides()
+    if w.kind == "sscore":                       # B = K^T: B[d, j] = K[j, d]
+        sb = (1, sb[0], sb[2])
+    return asl.gemm_create(w.M, w.N, w.K, w.batch, w.a_strides(), sb, (w.N, 1, w.M * w.N),
                            asl.AS_BF16, asl.AS_BF16, c_t, flags)
 
 
@@ -228,7 +231,7 @@ def time_workload(w, steps, warmup, flags=0):
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     a, b, c = A.data_ptr(), B.data_ptr(), C.data_ptr()
-    if w.kind == "sscore":
+    if w.kind == "sscore" and flags == 0:
         s_t = asl.AS_BF16 if w.out == "bf16" else asl.AS_F32
         sq, sk, ss = w.a_strides(), w.b_strides(), (w.N, 1, w.M * w.N)
         # the plan sscore_run makes internally, for reporting only
@@ -239,13 +242,15 @@ def time_workload(w, steps, warmup, flags=0):
         def run(s=None):
             asl.sscore_run(a, b, c, w.batch, w.M, w.N, w.K, sq, sk, ss, asl.AS_BF16, s_t, sh if s is None else s)
     else:
-        plan = _plan(asl, w, flags)
+        # (the attention scores with flags, e.g. the grouping ablation: the
+        # plan sscore_run makes -- A = Q, B = K^T, no split -- with the flags)
+        plan = _plan(asl, w, flags | (asl.AS_FLAG_NO_SPLIT_K if w.kind == "sscore" else 0))
         info = asl.gemm_plan_info(plan) + (asl.gemm_plan_split_k(plan)[0],)
 
         def run(s=None):
             asl.gemm_run(plan, a, b, c, sh if s is None else s)
     wall_ms, ev_ms, steps, warmup = _timed(run, steps, warmup, stream)
-    if w.kind != "sscore":
+    if w.kind != "sscore" or flags:
         asl.gemm_destroy(plan)
     del A, B, C
     return wall_ms, ev_ms, info, steps, warmup
@@ -386,14 +391,14 @@ def tilecast_report(iters=5000):
     return lines
 
 
-def profile_run(steps, name=HEADLINE):
+def profile_run(steps, name=HEADLINE, flags=0):
     """Short run for counter collection: one workload, then a copy kernel of known size."""
     import torch
     from workloads import ATTN_WORKLOADS, WORKLOADS
     if name in ATTN_WORKLOADS:
         time_attention(ATTN_WORKLOADS[name], steps, 1)
     else:
-        time_workload(WORKLOADS[name], steps, 1)
+        time_workload(WORKLOADS[name], steps, 1, flags)
     n = 1 << 29                                  # 1 GiB of bf16 read, 1 GiB written
     src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
@@ -476,7 +481,7 @@ def main():
     asl.lib()
 
     if args.profile:
-        profile_run(args.steps if args.steps else 3, args.workload)
+        profile_run(args.steps if args.steps else 3, args.workload, args.flags)
         return
     if args.tilecast:
         for line in tilecast_report():

@@ -110,6 +110,10 @@ typedef struct {
 #define AS_FLAG_ROTATE_K    0x80u /* tile row tm starts its K loop at K stage tm mod (K / 64): concurrent tiles read
                                    * different K columns (the default when every A row panel feeds a single tile) */
 #define AS_FLAG_NO_ROTATE_K 0x100u /* ablation: every tile walks K from 0 */
+#define AS_FLAG_NO_XCD_SPLIT 0x200u /* ablation: the grouped band order of tiles, but workgroup h takes its tiles
+                                     * h, h + grid, ... of that order instead of a range owned by its XCD, so
+                                     * tiles that share panels run on different XCDs (no effect with
+                                     * AS_FLAG_NO_GROUPING) */
 
 typedef struct as_gemm_plan* as_gemm_t;
 

@@ -166,6 +166,8 @@ SHAPES = [  # (M, N, K, batch, flags)
     (2048, 2048, 128, 7, 0),                              # 1792 tiles of 128 over 512 workgroups
     (2048, 2048, 128, 7, asl.AS_FLAG_ONE_TILE_PER_WORKGROUP),
     (8192, 8192, 8192, 1, asl.AS_FLAG_NO_GROUPING),
+    (8192, 8192, 8192, 1, asl.AS_FLAG_NO_XCD_SPLIT),
+    (2048, 2048, 128, 7, asl.AS_FLAG_NO_XCD_SPLIT),
     (1000, 3000, 96, 3, 0),                               # ragged: partial edge tiles
     (4100, 4104, 520, 2, asl.AS_FLAG_TILE_256),
 ]
@@ -212,6 +214,23 @@ def test_concurrent_tiles_touch_few_panels(M, N, K, sa):
     assert asl.gemm_plan_info(p)[0] == 256
     assert _wave_panels(p, asl.gemm_plan_info(p)[3]) <= 12
     asl.gemm_destroy(p)
+
+
+def test_xcd_split_is_what_keeps_a_wave_of_tiles_on_few_panels():
+    # 8192^3: 32 tiles running together on an XCD touch 12 panels under the
+    # default order and under the identity (whose row-major walk happens to
+    # give each XCD four whole tile columns, 32 being a multiple of 8), but
+    # 18 under the band order without the XCD split: a 4-row band's
+    # consecutive tiles run on 8 different XCDs, so XCD 0 takes row 0 and row
+    # 4 of two bands at every other column (2 A + 16 B panels).
+    got = {}
+    for flags in (0, asl.AS_FLAG_NO_GROUPING, asl.AS_FLAG_NO_XCD_SPLIT):
+        p = asl.gemm_create(8192, 8192, 8192, 1, (8192, 1, 0), (8192, 1, 0), (8192, 1, 0), c_t=asl.AS_BF16,
+                            flags=flags)
+        got[flags] = _wave_panels(p, asl.gemm_plan_info(p)[3])
+        asl.gemm_destroy(p)
+    assert got[0] == 12 and got[asl.AS_FLAG_NO_GROUPING] == 12
+    assert got[asl.AS_FLAG_NO_XCD_SPLIT] == 18
 
 
 def test_grouping_keeps_slices_on_one_xcd_identity_spreads_them():

@@ -392,7 +392,9 @@ def test_grouping_ablation_is_bitwise_identical():
     sa, sb = (K, 1, 0), (N, 1, 0)
     C1 = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.bfloat16, 0)
     C2 = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.bfloat16, asl.AS_FLAG_NO_GROUPING)
+    C3 = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.bfloat16, asl.AS_FLAG_NO_XCD_SPLIT)
     assert torch.equal(C1, C2)
+    assert torch.equal(C1, C3)
 
 
 # ------------------------------------------------------ tile fan-out bench --
