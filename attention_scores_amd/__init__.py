@@ -27,6 +27,7 @@ AS_BF16, AS_F32 = 0, 1
 AS_FLAG_NO_GROUPING = 0x1
 AS_FLAG_TILE_128 = 0x2
 AS_FLAG_TILE_256 = 0x4
+AS_FLAG_TILE_64 = 0x400
 AS_FLAG_ONE_TILE_PER_WORKGROUP = 0x8
 AS_FLAG_NO_SPLIT_K = 0x10
 AS_FLAG_NT_A = 0x20

@@ -70,12 +70,33 @@ as_status ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 |
+constexpr uint32_t kKnownFlags = AS_FLAG_NO_GROUPING | AS_FLAG_TILE_128 | AS_FLAG_TILE_256 | AS_FLAG_TILE_64 |
                                  AS_FLAG_ONE_TILE_PER_WORKGROUP | AS_FLAG_NO_SPLIT_K | AS_FLAG_NT_A |
                                  AS_FLAG_NO_NT_A | AS_FLAG_ROTATE_K | AS_FLAG_NO_ROTATE_K | AS_FLAG_NO_XCD_SPLIT;
 constexpr int64_t kBK = asl::kTileK;
 constexpr int64_t kCus = 256;   // MI355X compute units
 constexpr int64_t kMinSplitK = 1024;   // shallowest K chunk of a split product
+
+// Workgroups that stay resident at once: one per CU for the 256 tile's
+// 146 KiB and the 64 tile's 133 KiB of LDS (its 8-stage ring), two for the
+// 128 tile's 73 KiB.
+int64_t resident_of(int tile) { return (tile == 128 ? 2 : 1) * kCus; }
+
+// K chunks of a split product (1: no split).  K is split when the output
+// tiles leave CUs idle (fewer tiles than CUs): into 2, 4, 8 or 16 chunks,
+// each a multiple of the K stage and at least kMinSplitK deep, as many as
+// keep tiles x chunks within the resident grid.  The fp32 partial sums then
+// cost 8 bytes per output element and chunk (written, then read back by the
+// reduction), against 2*kc flop per element and chunk.  (With a tile per CU
+// already, a second workgroup per CU gained nothing: 2048^2 x 4096 ran
+// 43.3 us unsplit, 44.4 us in two chunks.)
+int64_t split_count(int64_t tiles, int tile, int64_t K, int64_t batch, uint32_t flags) {
+    int64_t s = 1;
+    if (!(flags & AS_FLAG_NO_SPLIT_K) && batch == 1 && tiles < kCus)
+        while (s < 16 && tiles * s * 2 <= resident_of(tile) && K % (kBK * s * 2) == 0 && K / (s * 2) >= kMinSplitK)
+            s *= 2;
+    return s;
+}
 
 // Rows of tiles per group.  The cost of a candidate is the operand-panel
 // traffic one XCD's L2 would take from memory, estimated on XCD 0's share
@@ -128,8 +149,8 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
         return fail(AS_ERR_INVALID, "sizes must be positive (M=%" PRId64 " N=%" PRId64 " K=%" PRId64
                     " batch=%" PRId64 ")", M, N, K, batch);
     if (flags & ~kKnownFlags) return fail(AS_ERR_INVALID, "unknown flag bits 0x%x", flags & ~kKnownFlags);
-    if ((flags & AS_FLAG_TILE_128) && (flags & AS_FLAG_TILE_256))
-        return fail(AS_ERR_INVALID, "AS_FLAG_TILE_128 and AS_FLAG_TILE_256 are exclusive");
+    if (__builtin_popcount(flags & (AS_FLAG_TILE_64 | AS_FLAG_TILE_128 | AS_FLAG_TILE_256)) > 1)
+        return fail(AS_ERR_INVALID, "AS_FLAG_TILE_64, AS_FLAG_TILE_128 and AS_FLAG_TILE_256 are exclusive");
     if ((flags & AS_FLAG_NT_A) && (flags & AS_FLAG_NO_NT_A))
         return fail(AS_ERR_INVALID, "AS_FLAG_NT_A and AS_FLAG_NO_NT_A are exclusive");
     if ((flags & AS_FLAG_ROTATE_K) && (flags & AS_FLAG_NO_ROTATE_K))
@@ -184,13 +205,21 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     // a CU so one's stores overlap the other's loads (store-bound shapes such
     // as attention scores with a short K).
     auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
+    // A grid of 128 tiles that would fill at most a quarter of the CUs and
+    // cannot split K (too shallow, or batched) is latency-bound: its few
+    // workgroups wait on one stage load after another.  64 tiles give it 4x
+    // the workgroups, each with every stage of a K up to 512 in flight.
     int tile;
     if (flags & AS_FLAG_TILE_256) tile = 256;
     else if (flags & AS_FLAG_TILE_128) tile = 128;
+    else if (flags & AS_FLAG_TILE_64) tile = 64;
     else {
         const int64_t area256 = cdiv(M, 256) * cdiv(N, 256) * 4, area128 = cdiv(M, 128) * cdiv(N, 128);
         const bool deep = K >= 512, many = batch * cdiv(M, 256) * cdiv(N, 256) >= 128;
         tile = (deep && many && area256 * 100 <= area128 * 106) ? 256 : 128;
+        if (tile == 128 && batch * cdiv(M, 64) * cdiv(N, 64) <= kCus &&
+            split_count(batch * area128, 128, K, batch, flags) == 1)
+            tile = 64;
     }
     // Per-lane 32-bit byte offsets inside one staged tile.
     const int64_t a_span = (d.a_kmajor ? tile : kBK) * a_ld * 2;
@@ -217,33 +246,19 @@ as_status plan_desc(asl::GemmDesc* out, int64_t M, int64_t N, int64_t K, int64_t
     const bool streams_a = d.tiles_n == 1;
     d.nt_a = (flags & AS_FLAG_NT_A) ? true : (flags & AS_FLAG_NO_NT_A) ? false : streams_a;
     d.rotate_k = (flags & AS_FLAG_ROTATE_K) ? true : (flags & AS_FLAG_NO_ROTATE_K) ? false : streams_a;
-    // Split K when the output tiles leave CUs idle (fewer tiles than CUs):
-    // into 2, 4, 8 or 16 chunks, each a multiple of the K stage and at least
-    // kMinSplitK deep, as many as keep tiles x chunks within the resident
-    // grid.  The fp32 partial sums then cost 8 bytes per output element and
-    // chunk (written, then read back by the reduction), against 2*kc flop
-    // per element and chunk.  (With a tile per CU already, a second
-    // workgroup per CU gained nothing: 2048^2 x 4096 ran 43.3 us unsplit,
-    // 44.4 us in two chunks.)
     d.splits = 1;
     d.kc = K;
-    if (!(flags & AS_FLAG_NO_SPLIT_K) && batch == 1 && d.tiles < kCus) {
-        const int64_t resident = (tile == 256 ? 1 : 2) * kCus;
-        int64_t s = 1;
-        while (s < 16 && d.tiles * s * 2 <= resident && K % (kBK * s * 2) == 0 && K / (s * 2) >= kMinSplitK) s *= 2;
-        if (s > 1) {
-            d.splits = (int32_t)s;
-            d.kc = K / s;
-            d.ws_ld = (N + 3) & ~INT64_C(3);
-            d.ws_bytes = s * M * d.ws_ld * 4;
-        }
+    if (const int64_t sk = split_count(d.tiles, tile, K, batch, flags); sk > 1) {
+        d.splits = (int32_t)sk;
+        d.kc = K / sk;
+        d.ws_ld = (N + 3) & ~INT64_C(3);
+        d.ws_bytes = sk * M * d.ws_ld * 4;
     }
-    // As many workgroups as stay resident (one per CU for the 256 tile's
-    // 146 KiB of LDS, two for the 128 tile's 73 KiB), each walking its XCD's tiles
+    // As many workgroups as stay resident, each walking its XCD's tiles
     // with the LDS ring streaming across tile boundaries, so one tile's
     // stores drain while the next tile computes; or, for the ablation, one
     // workgroup per tile.
-    const int64_t resident = (tile == 256 ? 1 : 2) * kCus;
+    const int64_t resident = resident_of(tile);
     const int64_t launched = d.tiles * d.splits;   // split: every (chunk, tile) pair
     d.grid = !(flags & AS_FLAG_ONE_TILE_PER_WORKGROUP) && launched > resident ? resident : launched;
     d.group_m = choose_group_m(launched, d.tiles_m, d.tiles_n, tile, d.kc);

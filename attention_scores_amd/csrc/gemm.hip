@@ -474,9 +474,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
     constexpr int kWaitStage = L * (S - 2);                       // loads issued after the awaited stage's
-    constexpr int kEpiStores = epilogue_stores<WTM, WTN, 8, OUT_BF16>();
+    // Rows per chunk of a tile followed by another: 8, or 16 where 8 rows
+    // of a narrow bf16 block are fewer than one 16-byte piece per lane.
+    constexpr int ER = 8 * WTN / (OUT_BF16 ? 8 : 4) >= 64 ? 8 : 16;
+    constexpr int kEpiStores = epilogue_stores<WTM, WTN, ER, OUT_BF16>();
     constexpr int kWaitAfterEpi = kWaitStage + kEpiStores < 63 ? kWaitStage + kEpiStores : 63;
-    using Epi8 = EpiRegion<WTN, 8>;
+    using Epi8 = EpiRegion<WTN, ER>;
     using Epi32 = EpiRegion<WTN, 32>;
     static_assert(NW * Epi32::kBytes <= S * kStage, "last-tile epilogue must fit in the ring");
     __shared__ __attribute__((aligned(1024))) char smem[S * kStage + NW * Epi8::kBytes];
@@ -593,19 +596,24 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
         int el = lane;
         if constexpr (RAGGED) asm volatile("" : "+v"(el));
         if (RAGGED && !full)
-            epilogue<MI, WTM, WTN, 8, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
+            epilogue<MI, WTM, WTN, ER, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
         else if (last)
             epilogue<MI, WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
         else
-            epilogue<MI, WTM, WTN, 8, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+            epilogue<MI, WTM, WTN, ER, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
         prev_full = full;
     }
 }
 
 // Stage depth and ring length: 2 x 64 KiB of LDS for the 256 tile.  A
-// 64-deep stage reads whole 128-byte lines of K-contiguous operands.
+// 64-deep stage reads whole 128-byte lines of K-contiguous operands.  The
+// 64 tile is for grids too small to fill the CUs, whose time is the latency
+// of the dependent stage loads rather than bandwidth: its 16 KiB stages sit
+// in a ring of 8, so a K of up to 512 is requested at once and deeper K
+// keeps 7 stages in flight.
 constexpr int kBK = 64;
-constexpr int kStages = 2;
+template <int TILE>
+constexpr int stages_of() { return TILE == 64 ? 8 : 2; }
 
 // Wave grid and MFMA of a workgroup.
 //   256 tile: 16x16x32 MFMAs; 2 x 4 waves of 128 x 64, two waves per SIMD,
@@ -616,6 +624,7 @@ constexpr int kStages = 2;
 //     element accumulates the same MFMA chain either way, so the bits agree.
 //   128 tile: 32x32x16 MFMAs; 2 x 2 waves of 64 x 64 (8 waves would leave
 //     2 MFMAs per substep).
+//   64 tile: 32x32x16 MFMAs; 2 x 2 waves of 32 x 32.
 // Against 32x32x16, the 16x16x32 MFMA reads and writes half the accumulator
 // bytes per multiply-add; on this power-limited part the clock it keeps
 // makes 8192^3 7 % faster (measured, interleaved: 0.800 -> 0.744 ms).
@@ -632,11 +641,12 @@ void launch_nt(const GemmDesc& d, const KArgs& k, hipStream_t s) {
     using WF = WaveGrid<TILE, false, OUT_BF16>;
     const bool ragged = d.M % TILE || d.N % TILE || d.K % kBK;
     const dim3 grid((unsigned)d.grid);
+    constexpr int S = stages_of<TILE>();
     if (ragged)
-        gemm_kernel<TILE, kBK, kStages, WR::M, WR::N, WR::MI, A_K, B_K, OUT_BF16, true, NT_A>
+        gemm_kernel<TILE, kBK, S, WR::M, WR::N, WR::MI, A_K, B_K, OUT_BF16, true, NT_A>
             <<<grid, dim3(64 * WR::M * WR::N), 0, s>>>(k);
     else
-        gemm_kernel<TILE, kBK, kStages, WF::M, WF::N, WF::MI, A_K, B_K, OUT_BF16, false, NT_A>
+        gemm_kernel<TILE, kBK, S, WF::M, WF::N, WF::MI, A_K, B_K, OUT_BF16, false, NT_A>
             <<<grid, dim3(64 * WF::M * WF::N), 0, s>>>(k);
 }
 
@@ -702,6 +712,7 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
     k.rotate = d.rotate_k ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
     if (d.tile == 256) return launch_tile<256>(d, k, s);
+    if (d.tile == 64) return launch_tile<64>(d, k, s);
     return launch_tile<128>(d, k, s);
 }
 

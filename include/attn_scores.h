@@ -101,6 +101,7 @@ typedef struct {
 #define AS_FLAG_NO_GROUPING 0x1u  /* ablation: workgroup id -> tile is the identity (row-major tile order) */
 #define AS_FLAG_TILE_128    0x2u  /* force 128x128 output tiles */
 #define AS_FLAG_TILE_256    0x4u  /* force 256x256 output tiles */
+#define AS_FLAG_TILE_64     0x400u /* force 64x64 output tiles (8 K stages in flight) */
 #define AS_FLAG_ONE_TILE_PER_WORKGROUP 0x8u  /* ablation: one workgroup per output tile instead of a resident
                                                * (persistent) grid whose workgroups walk several tiles */
 #define AS_FLAG_NO_SPLIT_K  0x10u /* never split K over workgroups (no workspace) */
@@ -129,10 +130,12 @@ typedef struct as_gemm_plan* as_gemm_t;
  *   a_t, b_t     must be AS_BF16
  *   c_t          AS_F32, or AS_BF16 (round-to-nearest-even)
  *   flags        AS_FLAG_* bits
- * Chooses the output tile (256x256 with 8 waves or 128x128 with 4), the workgroup
- * grouping and the grid: by default as many workgroups as stay resident
- * (256 for the 256x256 tile, 512 for 128x128; fewer if there are fewer
- * tiles), each walking several tiles.  Makes no HIP call.
+ * Chooses the output tile (256x256 with 8 waves, 128x128 with 4, or 64x64
+ * with 4 for a grid of 128x128 tiles that would fill at most a quarter of
+ * the CUs without splitting K), the workgroup grouping and the grid: by
+ * default as many workgroups as stay resident (256 for the 256x256 and
+ * 64x64 tiles, 512 for 128x128; fewer if there are fewer tiles), each
+ * walking several tiles.  Makes no HIP call.
  * Split K: when batch == 1 and there are fewer output tiles than the 256
  * CUs, the plan splits K into 2, 4, 8 or 16 equal chunks
  * (each a multiple of 64 and at least 1024 deep), as many as keep tiles x

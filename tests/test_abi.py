@@ -93,9 +93,9 @@ def test_create_refuses_k_not_a_multiple_of_8(M, N, K):
     assert "multiple of 8" in asl.as_last_error()
 
 
-@pytest.mark.parametrize("M,N,K,tile", [(500, 512, 512, 128), (512, 520, 512, 128), (512, 512, 80, 128),
-                                        (1, 1, 8, 128), (8000, 8000, 8000, 256), (8100, 8000, 4096, 256),
-                                        (4224, 4224, 4096, 128)])
+@pytest.mark.parametrize("M,N,K,tile", [(500, 512, 512, 64), (512, 520, 512, 64), (512, 512, 80, 64),
+                                        (1, 1, 8, 64), (8000, 8000, 8000, 256), (8100, 8000, 4096, 256),
+                                        (4224, 4224, 4096, 128), (2048, 1024, 512, 128)])
 def test_ragged_shapes_plan_partial_tiles(M, N, K, tile):
     # M and N need not be multiples of the tile nor K of the 64-deep stage:
     # edge tiles are partial, the tile count rounds up.
@@ -114,7 +114,7 @@ def test_create_refuses_huge_leading_stride():
 
 def test_plan_registry_and_run_argument_checks():
     p = asl.gemm_create(512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512))
-    assert asl.gemm_plan_info(p) == (128, 128, 64, 16, 16)
+    assert asl.gemm_plan_info(p) == (64, 64, 64, 64, 64)
     assert _status(asl.gemm_run, p, 0, 0, 0) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_run, p, 16, 32, 0) == asl.AS_ERR_INVALID
     assert _status(asl.gemm_run, p, 8, 16, 32) == asl.AS_ERR_UNSUPPORTED          # misaligned
@@ -151,6 +151,17 @@ def test_tile_choice():
     p = asl.gemm_create(65536, 256, 4096, 1, RM(65536, 4096), RM(4096, 256), RM(65536, 256))
     assert asl.gemm_plan_info(p) == (256, 256, 64, 256, 256)
     asl.gemm_destroy(p)
+    # small grids that cannot split K: 64 tiles, as many as the CUs at most
+    for (M, N, K, batch), want in (((512, 512, 512, 1), (64, 64, 64, 64, 64)),
+                                   ((512, 512, 512, 3), (64, 64, 64, 192, 192)),
+                                   ((1024, 1024, 1024, 1), (64, 64, 64, 256, 256)),
+                                   ((1024, 1152, 1024, 1), (128, 128, 64, 72, 72)),     # 288 tiles of 64
+                                   ((1024, 1024, 4096, 1), (128, 128, 64, 64, 256))):   # splits K in 4
+        p = asl.gemm_create(M, N, K, batch, (K, 1, M * K), (N, 1, K * N), (N, 1, M * N))
+        assert asl.gemm_plan_info(p) == want, (M, N, K, batch)
+        asl.gemm_destroy(p)
+    assert _status(asl.gemm_create, 512, 512, 512, 1, RM(512, 512), RM(512, 512), RM(512, 512), asl.AS_BF16,
+                   asl.AS_BF16, asl.AS_F32, asl.AS_FLAG_TILE_64 | asl.AS_FLAG_TILE_128) == asl.AS_ERR_INVALID
 
 
 SHAPES = [  # (M, N, K, batch, flags)
@@ -365,7 +376,10 @@ def test_split_k_plans():
     assert plan(2048, 2048, 4096)[1] == (1, 0)                        # 256 tiles of 128: one per CU
     assert plan(1024, 1024, 8192, batch=2)[1] == (1, 0)               # batched: no split
     assert plan(1024, 1024, 8200)[1] == (1, 0)                        # K not a multiple of 128
-    assert plan(1024, 1024, 8192, flags=asl.AS_FLAG_NO_SPLIT_K) == ((128, 128, 64, 64, 64), (1, 0))
+    # without a split, 64 tiles of 128 would fill a quarter of the CUs: 256 tiles of 64 instead
+    assert plan(1024, 1024, 8192, flags=asl.AS_FLAG_NO_SPLIT_K) == ((64, 64, 64, 256, 256), (1, 0))
+    assert plan(1024, 1024, 8192, flags=asl.AS_FLAG_NO_SPLIT_K | asl.AS_FLAG_TILE_128) == \
+        ((128, 128, 64, 64, 64), (1, 0))
 
 
 def test_split_plan_slots_cover_every_chunk_and_tile():

@@ -77,7 +77,10 @@ def _layout(M, N, K, batch, a_k, b_k):
 LAYOUTS = [(ak, bk) for ak in (True, False) for bk in (True, False)]
 
 
-@pytest.mark.parametrize("tile", [128, 256])
+TILE_FLAG = {64: asl.AS_FLAG_TILE_64, 128: asl.AS_FLAG_TILE_128, 256: asl.AS_FLAG_TILE_256}
+
+
+@pytest.mark.parametrize("tile", [64, 128, 256])
 @pytest.mark.parametrize("a_k,b_k", LAYOUTS, ids=lambda v: str(v))
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_integer_data_bit_exact(tile, a_k, b_k, out):
@@ -90,8 +93,7 @@ def test_integer_data_bit_exact(tile, a_k, b_k, out):
     A = draw(a_shape, "int", -4, 4, 11 + tile)
     B = draw(b_shape, "int", -4, 4, 12 + tile)
     od = torch.bfloat16 if out == "bf16" else torch.float32
-    flags = asl.AS_FLAG_TILE_256 if tile == 256 else asl.AS_FLAG_TILE_128
-    C = _run_gemm(A, B, M, N, K, batch, sa, sb, od, flags)
+    C = _run_gemm(A, B, M, N, K, batch, sa, sb, od, TILE_FLAG[tile])
     Cref, _ = oracle.gemm(bits(A), bits(B), batch, M, N, K, sa, sb, want_T=False)
     if out == "f32":
         assert np.array_equal(_decode(C), Cref)
@@ -488,6 +490,18 @@ def test_resident_grid_256_tiles_bit_exact(K, out, a_k, b_k):
         assert np.array_equal(bits(C), oracle.f64_to_bf16_rne_array(Cref))
 
 
+@pytest.mark.parametrize("K,out,a_k,b_k", [(64, "f32", True, False), (576, "bf16", True, False),
+                                           (200, "f32", False, True), (192, "bf16", False, False)])
+def test_resident_grid_64_tiles_bit_exact(K, out, a_k, b_k):
+    # 40 x 36 = 1440 tiles of 64 x 64 over 256 resident workgroups: every
+    # workgroup walks several tiles through the 8-stage ring (K = 576: the
+    # ring wraps within a tile; K = 200: a partial last stage), with the
+    # 8-row (fp32) or 16-row (bf16) epilogue chunks between tiles.
+    M, N, batch = 2560, 2300, 1
+    _say("resident grid 64 tiles K=%d out=%s a_k=%s b_k=%s" % (K, out, a_k, b_k))
+    _ragged(M, N, K, batch, a_k, b_k, out, asl.AS_FLAG_TILE_64, 3300 + K)
+
+
 def test_one_tile_per_workgroup_full_size_sampled():
     w = WORKLOADS["gemm8192"]
     _say("gemm8192 one tile per workgroup, sampled")
@@ -567,6 +581,8 @@ RAGGED = [  # (M, N, K, batch, tile flag)
     (257, 300, 136, 1, asl.AS_FLAG_TILE_256),
     (513, 260, 8, 1, asl.AS_FLAG_TILE_256),
     (256, 256, 520, 1, asl.AS_FLAG_TILE_256),     # full tiles, partial last stage only
+    (65, 200, 1032, 2, asl.AS_FLAG_TILE_64),      # 17 stages through the 8-stage ring, partial last
+    (100, 37, 40, 1, asl.AS_FLAG_TILE_64),
 ]
 
 
@@ -686,13 +702,13 @@ def _random_cases(n, seed):
         batch = int(rng.integers(1, 3))
         a_k, b_k = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
         out = "bf16" if rng.integers(0, 2) else "f32"
-        flags = [asl.AS_FLAG_TILE_256, asl.AS_FLAG_TILE_128, 0][i % 3]
+        flags = [asl.AS_FLAG_TILE_256, asl.AS_FLAG_TILE_128, 0, asl.AS_FLAG_TILE_64][i % 4]
         flags |= [0, asl.AS_FLAG_ROTATE_K, asl.AS_FLAG_NT_A, asl.AS_FLAG_ROTATE_K | asl.AS_FLAG_NT_A][(i // 3) % 4]
         cases.append((M, N, K, batch, a_k, b_k, out, flags))
     return cases
 
 
-@pytest.mark.parametrize("M,N,K,batch,a_k,b_k,out,flags", _random_cases(24, 2026))
+@pytest.mark.parametrize("M,N,K,batch,a_k,b_k,out,flags", _random_cases(32, 2026))
 def test_random_shapes_bit_exact(M, N, K, batch, a_k, b_k, out, flags):
     """Seeded random shapes, layouts, output types, tiles and streaming
     options on integer data: bit-exact against the oracle, nothing written
