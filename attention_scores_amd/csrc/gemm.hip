@@ -67,8 +67,9 @@ struct KArgs {
 // stage of a K-contiguous operand, a chunk at k >= K would read the next
 // row, so its offset is moved out of range there.  A load of such an operand
 // covers 8 rows of 8 chunks and the chunk order depends only on the lane and
-// on the parity of the load's row group (the swizzle in swz_k<8>); kc[p] is
-// the lane's k offset in loads of parity p.  An MN-contiguous operand needs
+// on one bit of the load's row-group index (OperandTile::kGroupBit, from
+// the swizzle in swz_k<8>); kc[p] is the lane's k offset in loads where that
+// bit is p.  An MN-contiguous operand needs
 // no mask: its k rows past K lie past the resource's range.
 template <class OpA, class OpB>
 struct LaneOffsets {
@@ -85,8 +86,8 @@ struct LaneOffsets {
 template <class OpA, class OpB, bool RAGGED, bool NT_A>
 struct StageLoads {
     static constexpr int kCount = OpA::kLoadsPerWave + OpB::kLoadsPerWave;
-    static_assert(OpA::kLoadsPerWave % 2 == 0 && OpB::kLoadsPerWave % 2 == 0,
-                  "a wave's loads must start on an even row group");
+    static_assert(OpA::kLoadsPerWave % (2 << OpA::kGroupBit) == 0 && OpB::kLoadsPerWave % (2 << OpB::kGroupBit) == 0,
+                  "a wave's loads must start on a row group whose swizzle bit is 0");
     static_assert(OpA::kCHR == 8 && OpB::kCHR == 8, "the two-parity chunk order holds for 8-chunk rows");
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t sa, sb;   // LDS byte addresses of this wave's first A / B row in the stage
@@ -103,13 +104,13 @@ struct StageLoads {
     __device__ void issue(int i, const LaneOffsets<OpA, OpB>& o) const {
         if (i < OpA::kLoadsPerWave) {
             uint32_t v = o.a[i];
-            if constexpr (RAGGED && OpA::kKMaj) v = o.akc[i & 1] < klim ? v : kOob;
+            if constexpr (RAGGED && OpA::kKMaj) v = o.akc[(i >> OpA::kGroupBit) & 1] < klim ? v : kOob;
             if constexpr (NT_A) lds_dma16_nt(ra, v, sa + i * 1024);
             else lds_dma16(ra, v, sa + i * 1024);
         } else {
             const int j = i - OpA::kLoadsPerWave;
             uint32_t v = o.b[j];
-            if constexpr (RAGGED && OpB::kKMaj) v = o.bkc[j & 1] < klim ? v : kOob;
+            if constexpr (RAGGED && OpB::kKMaj) v = o.bkc[(j >> OpB::kGroupBit) & 1] < klim ? v : kOob;
             lds_dma16(rb, v, sb + j * 1024);
         }
     }
@@ -468,8 +469,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int NS = BK / Mfma<MI>::kK;   // MFMA substeps per stage
     static_assert(NS % 2 == 0, "fragment sets alternate; NS must be even");
     static_assert(MI == 32 || NS == 2, "the 16x16x32 path runs two k32 substeps per stage");
-    using OpA = OperandTile<TILE, A_K, BK, NW>;
-    using OpB = OperandTile<TILE, B_K, BK, NW>;
+    using OpA = OperandTile<TILE, A_K, BK, NW, MI == 16>;
+    using OpB = OperandTile<TILE, B_K, BK, NW, MI == 16>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
@@ -503,8 +504,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     for (int i = 0; i < OpB::kLoadsPerWave; ++i) off.b[i] = OpB::src_offset(w, i, lane, a.b_ld);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        off.akc[p] = (uint32_t)OpA::inner_of(w, p, lane);
-        off.bkc[p] = (uint32_t)OpB::inner_of(w, p, lane);
+        off.akc[p] = (uint32_t)OpA::inner_of(w, p << OpA::kGroupBit, lane);
+        off.bkc[p] = (uint32_t)OpB::inner_of(w, p << OpB::kGroupBit, lane);
     }
 
     const int KT = a.ktiles;
