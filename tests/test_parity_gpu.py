@@ -229,7 +229,8 @@ def test_gemm512_full():
     A, B = operands(w)
     C = _run_gemm(A, B, w.M, w.N, w.K, 1, w.a_strides(), w.b_strides(), torch.float32)
     Cref, T = oracle.gemm(bits(A), bits(B), 1, w.M, w.N, w.K, w.a_strides(), w.b_strides())
-    _check_full(C, Cref, T)
+    util = _check_full(C, Cref, T)
+    _say("%s max tolerance use %.3g" % (w.name, util))
 
 
 @pytest.mark.parametrize("name,M,N,K", [
@@ -378,10 +379,13 @@ def test_sscore_full_size_every_element_and_deterministic():
     assert torch.equal(S1, S2)
     q, k = bits(Q).reshape(w.batch, -1), bits(K).reshape(w.batch, -1)
     sq, sk = w.a_strides(), w.b_strides()
+    worst = 0.0
     for b in range(w.batch):
         Sref, T = oracle.sscore(q[b], k[b], 1, w.M, w.N, w.K, sq, sk, nthreads=ORACLE_THREADS)
         nfail, util = oracle.check(_decode(S1[b]), Sref[0], T[0])
         assert nfail == 0, "slice %d: %d elements outside tolerance (max util %.3g)" % (b, nfail, util)
+        worst = max(worst, util)
+    _say("%s max tolerance use %.3g" % (w.name, worst))
 
 
 def test_grouping_ablation_is_bitwise_identical():
