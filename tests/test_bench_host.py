@@ -84,8 +84,9 @@ def test_traffic_summary_agrees_with_compulsory_bytes(name):
         w = ATTN_WORKLOADS[name]
         comp_in, comp_out = w.bytes_in, w.bytes_out
     if name == "gemm4096x2048x8192":
-        # split K: the product kernel's fp32 partial sums (two chunks) are its output
-        comp_out = 2 * 4 * w.M * w.N
+        # split K, one step = the product kernel, which writes fp32 partial sums
+        # (two chunks), and the reduction, which writes C
+        comp_out = 2 * 4 * w.M * w.N + w.bytes_c
     # every output byte goes to memory exactly once
     assert wr == pytest.approx(comp_out, rel=0.02)
     # inputs larger than all the L2s together cannot come from L2 across launches
