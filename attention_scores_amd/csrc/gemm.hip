@@ -2,8 +2,9 @@
 //
 // C[b] = A[b].B[b] with fp32 accumulation, one square output tile per
 // workgroup: 256x256 with 8 waves laid out 2x4 (each wave a 128x64 block of
-// 16x16 MFMA tiles, two waves per SIMD), or 128x128 with 4 waves laid out
-// 2x2 (64x64 blocks of 32x32 MFMA tiles); WaveGrid below.  The pages compute the same
+// 16x16 MFMA tiles, two waves per SIMD), 128x128 with 4 waves laid out 2x2
+// (64x64 blocks of 32x32 MFMA tiles), or 64x64 with 4 waves of 32x32 for
+// small grids; WaveGrid below.  The pages compute the same
 // contraction with shared operand tiles fanned out to several consumers
 // (lesson 07 "Clusters, distributed shared memory & cluster launch control",
 // sections "Two CTAs, one MMA" and "TMA multicast"; "Hopper TMA Multicast"
@@ -18,7 +19,8 @@
 //                   double-buffered; the next step's tile is requested while
 //                   the current one is multiplied.  LDS keeps each operand in
 //                   its global orientation, 16-byte chunks XOR-swizzled so
-//                   that the fragment reads below are bank-conflict free.
+//                   that the fragment reads below are bank-conflict free
+//                   (one swizzle per MFMA shape, tile.hpp).
 //   LDS -> VGPR     K-contiguous operands: ds_read_b128 (8 k values of one
 //                   row per lane); MN-contiguous operands: two
 //                   ds_read_b64_tr_b16, which transpose 4x16 blocks on the way
@@ -234,9 +236,12 @@ __device__ __forceinline__ void substep16(f32x4 (&acc)[TM][TN], Frags16<TM, TN>&
 }
 
 // Epilogue staging region of one wave: ROWS rows of the wave's block as
-// fp32 with a padded row stride (rows r and r+4 -- the two halves of one wave
-// write -- start 128 bytes apart modulo 256, so the writes are conflict
-// free).  A tile followed by another tile of the same workgroup stages 8 rows
+// fp32 with a padded row stride (rows r and r+4, the two halves of one wave
+// write, start 128 bytes apart modulo 256).  4-byte LDS stores are served
+// 32 lanes at a time over a 128-byte bank window, so those halves still
+// collide, and so do some passes of the 16-byte read-back: about 0.1
+// conflict cycles per LDS instruction of the whole kernel.  A layout free of
+// both was measured no faster.  A tile followed by another tile of the same workgroup stages 8 rows
 // at a time in a region past the LDS ring, so the next tile's stages can
 // stream in meanwhile; a workgroup's last tile stages 32 rows at a time in
 // the then idle ring (fewer LDS round trips per tile).
