@@ -236,20 +236,56 @@ __device__ __forceinline__ void substep16(f32x4 (&acc)[TM][TN], Frags16<TM, TN>&
 }
 
 // Epilogue staging region of one wave: ROWS rows of the wave's block as
-// fp32 with a padded row stride (rows r and r+4, the two halves of one wave
-// write, start 128 bytes apart modulo 256).  4-byte LDS stores are served
-// 32 lanes at a time over a 128-byte bank window, so those halves still
-// collide, and so do some passes of the 16-byte read-back: about 0.1
-// conflict cycles per LDS instruction of the whole kernel.  A layout free of
-// both was measured no faster.  A tile followed by another tile of the same workgroup stages 8 rows
-// at a time in a region past the LDS ring, so the next tile's stages can
-// stream in meanwhile; a workgroup's last tile stages 32 rows at a time in
-// the then idle ring (fewer LDS round trips per tile).
+// fp32, WTN*4 bytes per row and 64 more bytes after every 4 rows.  LDS
+// serves 4-byte stores 32 lanes at a time over a 128-byte bank window, and
+// 16-byte loads in passes of 16 lanes (see swz_k in tile.hpp).  The 64-byte
+// step puts the two 16-lane halves of a 16x16 staging write (rows r and r+4)
+// in different halves of the bank window, and the read-back below picks, per
+// lane, which row piece it reads (ReadBack), so that every pass of it hits
+// 16 distinct 16-byte groups: no bank conflicts on either side.  A tile
+// followed by another tile of the same workgroup stages 8 rows at a time in
+// a region past the LDS ring, so the next tile's stages can stream in
+// meanwhile; a workgroup's last tile stages 32 rows at a time in the then
+// idle ring (fewer LDS round trips per tile).
 template <int WTN, int ROWS>
 struct EpiRegion {
-    static constexpr int kStride = WTN * 4 + 32;
-    static constexpr int kBytes = ROWS * kStride;
+    static constexpr int kStride = WTN * 4;
+    static constexpr int kBytes = ROWS * kStride + 64 * (ROWS / 4);
+    // Byte offset of the fp32 element in row `row`, column `col`.
+    __device__ static int offset(int row, int col) { return row * kStride + 64 * (row >> 2) + 4 * col; }
+    // Row R + e of a lane whose own rows start at lr (R and lr multiples of
+    // 4, e < 4): offset(lr, c) plus this constant.
+    static constexpr int step(int R, int e) { return (R + e) * kStride + 16 * R; }
 };
+
+// Read-back order: lane l reads piece cp of row rl of each group of rows one
+// read-back instruction covers (16-byte pieces for fp32, 32-byte pieces for
+// bf16, read as two 16-byte halves, the upper one first where s = 1).  The
+// maps were found by exhaustive search over the lane-bit assignments against
+// the bank model: with them no pass of a read-back instruction meets a
+// bank twice.
+__device__ __forceinline__ int lane_bit(int l, int b) { return (l >> b) & 1; }
+template <int WTN, bool OUT_BF16>
+__device__ __forceinline__ void read_back_map(int l, int& rl, int& cp, int& s) {
+    if constexpr (!OUT_BF16) {
+        rl = l / (WTN / 4);
+        cp = l % (WTN / 4);
+        s = 0;
+    } else if constexpr (WTN == 64) {
+        rl = lane_bit(l, 0) | lane_bit(l, 2) << 1 | lane_bit(l, 1) << 2;
+        cp = lane_bit(l, 3) | lane_bit(l, 5) << 1 | lane_bit(l, 4) << 2;
+        s = lane_bit(l, 0);
+    } else if constexpr (WTN == 128) {
+        rl = lane_bit(l, 0) | lane_bit(l, 2) << 1;
+        cp = lane_bit(l, 1) | lane_bit(l, 3) << 1 | lane_bit(l, 4) << 2 | lane_bit(l, 5) << 3;
+        s = lane_bit(l, 0);
+    } else {
+        static_assert(WTN == 32, "read-back maps exist for 32-, 64- and 128-column wave blocks");
+        rl = l & 15;
+        cp = l >> 4;
+        s = lane_bit(l, 1);
+    }
+}
 
 // Write a wave's (WTM x WTN) accumulator block to C (row r0.., column c0..)
 // through its LDS region, ROWS rows at a time.  With 32x32 MFMAs element e
@@ -270,36 +306,41 @@ template <int MI, int WTM, int WTN, int ROWS>
 __device__ __forceinline__ void epilogue_stage(const typename Mfma<MI>::Acc (&acc)[WTM / MI][WTN / MI], int qc,
                                                char* region, int lane) {
     constexpr int TN = WTN / MI;
-    constexpr int STRIDE = EpiRegion<WTN, ROWS>::kStride;
-    auto put = [&](int row, int col, float x) {
-        *(__attribute__((address_space(3))) float*)(lds_void_t*)(region + row * STRIDE + col * 4) = x;
+    using Region = EpiRegion<WTN, ROWS>;
+    // Element at row R + lr + e, column C + lc of the chunk: the lane's base
+    // plus a constant.
+    auto put = [&](int base, int R, int e, int C, float x) {
+        *(__attribute__((address_space(3))) float*)(lds_void_t*)(region + base + Region::step(R, e) + 4 * C) = x;
     };
     if constexpr (MI == 32) {
         constexpr int H = 32 / ROWS;                 // chunks per MFMA row block
         const int mi = qc / H, h = qc % H;           // rows ROWS*h .. +ROWS-1 of row block mi
         const int lr = 4 * (lane >> 5), lc = lane & 31;
+        const int base = Region::offset(lr, lc);
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
             for (int e = (ROWS / 8) * 4 * h; e < (ROWS / 8) * 4 * (h + 1); ++e)
-                put(8 * (e >> 2) - ROWS * h + lr + (e & 3), 32 * ni + lc, acc[mi][ni][e]);
+                put(base, 8 * (e >> 2) - ROWS * h, e & 3, 32 * ni, acc[mi][ni][e]);
     } else if constexpr (ROWS >= 16) {
         const int lr = 4 * (lane >> 4), lc = lane & 15;   // whole 16-row blocks per chunk
+        const int base = Region::offset(lr, lc);
 #pragma unroll
         for (int b = 0; b < ROWS / 16; ++b)
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) put(16 * b + lr + e, 16 * ni + lc, acc[qc * (ROWS / 16) + b][ni][e]);
+                for (int e = 0; e < 4; ++e) put(base, 16 * b, e, 16 * ni, acc[qc * (ROWS / 16) + b][ni][e]);
     } else {
         // 8-row chunks: half h of row block mi is held by lanes 32h .. 32h+31
         const int mi = qc / 2, h = qc % 2;
+        const int lr = 4 * ((lane >> 4) & 1), lc = lane & 15;
+        const int base = Region::offset(lr, lc);
         if ((lane >> 5) == h) {
-            const int lr = 4 * ((lane >> 4) & 1), lc = lane & 15;
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) put(lr + e, 16 * ni + lc, acc[mi][ni][e]);
+                for (int e = 0; e < 4; ++e) put(base, 0, e, 16 * ni, acc[mi][ni][e]);
         }
     }
 }
@@ -308,31 +349,40 @@ template <int MI, int WTM, int WTN, int ROWS, bool OUT_BF16, bool EDGE = false>
 __device__ __forceinline__ void epilogue(const typename Mfma<MI>::Acc (&acc)[WTM / MI][WTN / MI], char* region,
                                          void* Cv, int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane,
                                          int64_t m_lim = 0, int64_t n_lim = 0) {
-    constexpr int STRIDE = EpiRegion<WTN, ROWS>::kStride;
+    using Region = EpiRegion<WTN, ROWS>;
     constexpr int ELEMS = OUT_BF16 ? 8 : 4;          // elements per lane per store (16 bytes out)
     constexpr int PPR = WTN / ELEMS;                 // pieces per row
     constexpr int PIECES = ROWS * PPR;
     static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "chunks are whole 8-row groups of a row block");
     static_assert(MI == 16 || ROWS <= 32, "a 32x32 row block splits into whole chunks");
     static_assert(PIECES % 64 == 0, "epilogue pieces must fill whole wave stores");
+    // Read-back q covers rows RQ*q .. RQ*q + RQ-1; the lane's addresses are
+    // its q = 0 ones plus a constant (RQ*q moves whole groups of 4 rows, or,
+    // for RQ = 2, keeps the lane's row inside its group of 4).
+    constexpr int RQ = 64 / PPR;
+    static_assert(RQ % 4 == 0 || RQ == 2, "read-back steps keep the lane's offset within its 4-row group");
+    int rl, cp, sw;
+    read_back_map<WTN, OUT_BF16>(lane, rl, cp, sw);
+    const int rd_a = Region::offset(rl, cp * ELEMS + 4 * sw);        // read first
+    const int rd_b = Region::offset(rl, cp * ELEMS + 4 * (1 - sw));  // bf16: read second
 #pragma unroll
     for (int qc = 0; qc < WTM / ROWS; ++qc) {        // rows ROWS*qc .. ROWS*qc+ROWS-1 of the block
         epilogue_stage<MI, WTM, WTN, ROWS>(acc, qc, region, lane);
         wave_lds_order();                            // other lanes' staged values are read below
 #pragma unroll
         for (int q = 0; q < PIECES / 64; ++q) {
-            const int piece = q * 64 + lane;
-            const int row = piece / PPR, cp = piece % PPR;
-            const char* src = region + row * STRIDE + cp * ELEMS * 4;
+            const int row = RQ * q + rl;
+            const int qoff = RQ * q * Region::kStride + 64 * ((RQ * q) >> 2);
             const int64_t gi = c_off + (r0 + ROWS * qc + row) * ldc + c0 + cp * ELEMS;
             if constexpr (EDGE) {
-                const int rl = ROWS * qc + row, cl = cp * ELEMS;
-                if (rl >= m_lim || cl >= n_lim) continue;
+                const int rg = ROWS * qc + row, cl = cp * ELEMS;
+                if (rg >= m_lim || cl >= n_lim) continue;
                 if (cl + ELEMS > n_lim) {
 #pragma unroll
                     for (int e = 0; e < ELEMS; ++e) {
                         if (cl + e < n_lim) {
-                            const float x = *(const __attribute__((address_space(3))) float*)(lds_void_t*)(src + 4 * e);
+                            const float x = *(const __attribute__((address_space(3))) float*)(lds_void_t*)(
+                                region + Region::offset(row, cl + e));
                             if constexpr (OUT_BF16) ((__bf16*)Cv)[gi + e] = (__bf16)x;
                             else ((float*)Cv)[gi + e] = x;
                         }
@@ -341,17 +391,17 @@ __device__ __forceinline__ void epilogue(const typename Mfma<MI>::Acc (&acc)[WTM
                 }
             }
             if constexpr (OUT_BF16) {
-                const f32x4 lo = *(const lds_f32x4_t*)(lds_void_t*)src;
-                const f32x4 hi = *(const lds_f32x4_t*)(lds_void_t*)(src + 16);
+                const f32x4 fa = *(const lds_f32x4_t*)(lds_void_t*)(region + rd_a + qoff);
+                const f32x4 fb = *(const lds_f32x4_t*)(lds_void_t*)(region + rd_b + qoff);
                 bf16x8 o;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    o[k] = (__bf16)lo[k];
-                    o[k + 4] = (__bf16)hi[k];
+                    o[k] = (__bf16)(sw ? fb[k] : fa[k]);
+                    o[k + 4] = (__bf16)(sw ? fa[k] : fb[k]);
                 }
                 __builtin_nontemporal_store(__builtin_bit_cast(i16x8, o), (i16x8*)((__bf16*)Cv + gi));
             } else {
-                const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)src;
+                const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)(region + rd_a + qoff);
                 __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
             }
         }

@@ -79,11 +79,15 @@ __device__ __forceinline__ int swz_k(int r) {
 // transposing reads of one pass touch 2 (16x16) or 4 (32x32) consecutive
 // chunks of 4 consecutive rows, plus, for 16x16, the same chunks of the 4
 // rows 8 further on; the XOR spreads them over 16 distinct groups (bit 3
-// of k moves the second set of rows to the other chunk pairs).
+// of k moves the second set of rows to the other chunk pairs).  With
+// 128-byte rows (CH = 8) two rows share a 256-byte line, so rows k and
+// k + 2 must take the other half of the line's chunks: bit 1 of k.
 template <int CH, bool L16 = false>
 __device__ __forceinline__ int swz_mn(int k) {
+    static_assert(CH >= 8, "rows of at least 128 bytes");
     if constexpr (L16) return (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) & (CH - 1);
-    else return ((k & 3) << 2) & (CH - 1);
+    else if constexpr (CH == 8) return ((k >> 1) & 1) << 2;
+    else return (k & 3) << 2;
 }
 
 // Buffer resource over `bytes` bytes at `base`.  The operands are wave
