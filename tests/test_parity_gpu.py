@@ -712,7 +712,7 @@ def _random_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("M,N,K,batch,a_k,b_k,out,flags", _random_cases(32, 2026))
+@pytest.mark.parametrize("M,N,K,batch,a_k,b_k,out,flags", _random_cases(128, 2026))
 def test_random_shapes_bit_exact(M, N, K, batch, a_k, b_k, out, flags):
     """Seeded random shapes, layouts, output types, tiles and streaming
     options on integer data: bit-exact against the oracle, nothing written
