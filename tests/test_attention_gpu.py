@@ -129,6 +129,33 @@ def test_random_data_within_tolerance(b, Lq, Lk, d, out, items):
     assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
 
 
+def _random_attention_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        causal = bool(rng.integers(0, 2))
+        Lq = int(rng.integers(1, 520))
+        Lk = Lq + int(rng.integers(0, 300)) if causal else int(rng.integers(1, 700))
+        cases.append((int(rng.integers(1, 4)), Lq, Lk, [64, 128][i % 2], causal, [256, 128][(i // 2) % 2],
+                      "bf16" if rng.integers(0, 2) else "f32"))
+    return cases
+
+
+@pytest.mark.parametrize("b,Lq,Lk,d,causal,items,out", _random_attention_cases(24, 4242))
+def test_random_attention_shapes_within_tolerance(b, Lq, Lk, d, causal, items, out):
+    """Seeded random sizes (ragged queries and keys, both head sizes, with and
+    without the causal mask, both item shapes, both output types)."""
+    _say("attn random shape b=%d Lq=%d Lk=%d d=%d causal=%s items=%d out=%s" % (b, Lq, Lk, d, causal, items, out))
+    Q = draw((b, Lq, d), "normal", 0, 1, 930 + Lq)
+    K = draw((b, Lk, d), "normal", 0, 1, 931 + Lk)
+    V = draw((b, Lk, d), "normal", 0, 1, 932 + d)
+    scale = d ** -0.5
+    got, _ = _run(Q, K, V, scale, out=out, causal=causal, items=items)
+    ref, TO = _ref(Q, K, V, scale, causal=causal)
+    nfail, util = oracle.check_attention(got, ref, TO, out_bf16=(out == "bf16"))
+    assert nfail == 0, "%d outside tolerance, max util %.3g" % (nfail, util)
+
+
 def test_padded_output_leaves_the_rest_untouched():
     # O rows of stride 136 with 2 spare rows per slice: only [0, Lq) x [0, dv) is written
     b, Lq, Lk, d = 2, 300, 200, 128
