@@ -94,16 +94,19 @@ struct StageLoads {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t sa, sb;   // LDS byte addresses of this wave's first A / B row in the stage
     uint32_t klim;
+    bool live;         // the stage exists (false past the workgroup's last tile: nothing is requested)
 
     __device__ void setup(const char* dst, int w, const uint16_t* a_src, const uint16_t* b_src, int a_bytes,
-                          int b_bytes, int klim_) {
+                          int b_bytes, int klim_, bool live_) {
         ra = make_rsrc(a_src, a_bytes);
         rb = make_rsrc(b_src, b_bytes);
         sa = lds_u32(dst + w * OpA::kLoadsPerWave * 1024);
         sb = lds_u32(dst + OpA::kBytes + w * OpB::kLoadsPerWave * 1024);
         if constexpr (RAGGED) klim = (uint32_t)__builtin_amdgcn_readfirstlane(klim_);
+        live = live_;
     }
     __device__ void issue(int i, const LaneOffsets<OpA, OpB>& o) const {
+        if (!live) return;
         if (i < OpA::kLoadsPerWave) {
             uint32_t v = o.a[i];
             if constexpr (RAGGED && OpA::kKMaj) v = o.akc[(i >> OpA::kGroupBit) & 1] < klim ? v : kOob;
@@ -502,9 +505,12 @@ struct StageCursor {
 //                        last fragments of stage g.
 // After a tile's last step its accumulators go out through the wave's own
 // epilogue region while the next tile's first stages are already landing.
-// A stage is requested S-1 steps before it is consumed.  Every step issues
-// the same number of loads (stages past the end fetch nothing), so the wait
-// count is a constant.
+// A stage is requested S-1 steps before it is consumed.  While stages
+// remain, every step issues the same number of loads, so the wait count is a
+// constant.  With a ring deeper than two stages, nothing is requested past
+// the workgroup's last stage (each wave-wide load holds the issuing wave for
+// tens of cycles even when it fetches nothing), and from the first skipped
+// stage on the waits are for everything outstanding.
 //
 // NT_A (an A that streams from HBM, e.g. one tile column): A's loads carry
 // the non-temporal hint, so its lines leave L2 first and B stays resident.
@@ -565,14 +571,95 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
 
     const int KT = a.ktiles;
     StageLoads<OpA, OpB, RAGGED, NT_A> ld;
+    if constexpr (S > 2 && MI == 32) {
+        // One tile whose K stages all fit the ring (short products on the 64
+        // tile): every stage is requested at once and waited for once, and
+        // the tile's k16 substeps then run without barriers, their fragments
+        // read kAhead-1 substeps ahead.  Nothing refills the ring, so reads
+        // may run across stage boundaries.  The general loop below pays a
+        // barrier and a fragment read latency per stage of only 4 MFMAs
+        // (512^3: 6.6 us per launch there, 6.2 us here).  The MFMA order is
+        // the general loop's, so the results are bitwise the same.
+        if (KT <= S && first + stride >= end) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                if (s < KT) {
+                    ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(),
+                             cur_ld.klim(), true);
+#pragma unroll
+                    for (int i = 0; i < L; ++i) ld.issue(i, off);
+                    cur_ld.advance();
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            asm volatile("s_barrier" ::: "memory");
+
+            constexpr int kAhead = 4;
+            const int nsub = KT * NS;
+            typename Mfma<MI>::Acc acc[TM][TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = typename Mfma<MI>::Acc{};
+            Frags<TM, TN> f[kAhead];
+#pragma unroll
+            for (int u = 0; u < kAhead - 1; ++u) {
+                if (u < nsub) {
+#pragma unroll
+                    for (int q = 0; q < TM + TN; ++q)
+                        read_unit<OpA, OpB>(f[u], q, smem + (u / NS) * kStage, u % NS, m0, n0, lane);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < S * NS; ++u) {
+                if (u < nsub) {
+                    const int v = u + kAhead - 1;
+                    if (v < nsub) {
+#pragma unroll
+                        for (int q = 0; q < TM + TN; ++q)
+                            read_unit<OpA, OpB>(f[v % kAhead], q, smem + (v / NS) * kStage, v % NS, m0, n0, lane);
+                    }
+#pragma unroll
+                    for (int t = 0; t < TM * TN; ++t)
+                        acc[t / TN][t % TN] =
+                            Mfma<MI>::run(f[u % kAhead].a[t / TN], f[u % kAhead].b[t % TN], acc[t / TN][t % TN]);
+                }
+            }
+
+            int bb, tm, tn;
+            logical_tile<int>(first, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
+            const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
+            const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
+            const int64_t m_lim = a.M - r0, n_lim = a.N - c0;
+            // Every wave is done reading the ring before it holds 32-row staging.
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            asm volatile("s_barrier" ::: "memory");
+            int el = lane;
+            if constexpr (RAGGED) asm volatile("" : "+v"(el));
+            if (RAGGED && !full)
+                epilogue<MI, WTM, WTN, ER, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim,
+                                                             n_lim);
+            else
+                epilogue<MI, WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld,
+                                                     el);
+            return;
+        }
+    }
+    // Stages past the end are skipped only with a ring deeper than two (the
+    // 64 tile, whose short products end with S-1 such steps); the two-stage
+    // kernels keep one constant wait and a branch-free main loop.
+    bool tail = false;                            // a stage past the last one was skipped
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim());
+        const bool lv = S == 2 || cur_ld.live();
+        tail |= !lv;
+        ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim(), lv);
 #pragma unroll
         for (int i = 0; i < L; ++i) ld.issue(i, off);
         cur_ld.advance();
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
+    if (tail) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
     asm volatile("s_barrier" ::: "memory");
 
     Frags<TM, TN> f[2];
@@ -609,7 +696,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
             }
             // the next stage landed everywhere; nobody reads buffer `cur` any more
             __builtin_amdgcn_sched_barrier(0);
-            if (kt == 0 && t != first && (!RAGGED || prev_full)) {
+            if (tail) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            } else if (kt == 0 && t != first && (!RAGGED || prev_full)) {
                 // The previous tile's epilogue stores (all kEpiStores of
                 // them: it was not an edge tile) were issued after the
                 // awaited loads; vector memory operations retire in issue
@@ -620,7 +709,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
             }
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim());
+            const bool lv = S == 2 || cur_ld.live();
+            tail |= !lv;
+            ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim(), lv);
             if constexpr (MI == 32)
                 substep<OpA, OpB, MI, TM, TN, true, RAGGED, NT_A>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0,
                                                                 n0, lane, ld, off);
@@ -639,10 +730,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
         const int64_t m_lim = a.M - r0, n_lim = a.N - c0;   // rows / columns of the wave's block inside C
         const bool last = t + stride >= end;
         if (last) {
-            // Last tile: only loads past the end (which fetch nothing but
-            // still complete into LDS) are outstanding.  Once they have
-            // landed and every wave is done reading the last stage, the ring
-            // is free for 32-row staging.
+            // Last tile: only loads past the end (two-stage ring: they fetch
+            // nothing but still complete into LDS) can be outstanding.  Once
+            // they have landed and every wave is done reading the last stage,
+            // the ring is free for 32-row staging.
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
             asm volatile("s_barrier" ::: "memory");
         }

@@ -506,6 +506,34 @@ def test_resident_grid_64_tiles_bit_exact(K, out, a_k, b_k):
     _ragged(M, N, K, batch, a_k, b_k, out, asl.AS_FLAG_TILE_64, 3300 + K)
 
 
+@pytest.mark.parametrize("K,out,rotate", [(512, "f32", False), (200, "bf16", False), (448, "f32", True)])
+def test_64_tile_short_product_paths_agree(K, out, rotate):
+    # On 64 x 64 tiles a workgroup with one tile whose K stages all fit the
+    # 8-stage ring runs them without per-stage barriers; a workgroup with
+    # several tiles runs the general ring loop.  Both issue the same MFMAs in
+    # the same order: slice 0 of an 8-slice product (512 tiles over 256
+    # workgroups: the general loop) must equal the 1-slice product (64 tiles:
+    # one each) bit for bit, on random data, and lie within tolerance.
+    M = N = 512
+    _say("64 tile short product paths K=%d out=%s rotate=%s" % (K, out, rotate))
+    flags = asl.AS_FLAG_TILE_64 | (asl.AS_FLAG_ROTATE_K if rotate else asl.AS_FLAG_NO_ROTATE_K)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    A1 = draw((1, M, K), "normal", 0, 1, 4101 + K)
+    B1 = draw((1, K, N), "normal", 0, 1, 4102 + K)
+    A8, B8 = A1.repeat(8, 1, 1), B1.repeat(8, 1, 1)
+    sa, sb = (K, 1, M * K), (N, 1, K * N)
+    one = _run_gemm(A1, B1, M, N, K, 1, sa, sb, od, flags)
+    many = _run_gemm(A8, B8, M, N, K, 8, sa, sb, od, flags)
+    assert torch.equal(one[0], many[0]) and torch.equal(many[0], many[7])
+    Cref, T = oracle.gemm(bits(A1), bits(B1), 1, M, N, K, sa, sb)
+    # With K = 200, |C| reaches 1/4 of T on this data, where rounding a
+    # correct result to bf16 (up to 2^-8 |C|) exceeds 1e-3 T by itself: the
+    # bf16-output allowance adds exactly that rounding.
+    extra = 2.0 ** -8 * np.abs(Cref[0]) if out == "bf16" else None
+    nfail, util = oracle.check(one[0].double().cpu().numpy(), Cref[0], T[0], extra=extra)
+    assert nfail == 0, util
+
+
 def test_one_tile_per_workgroup_full_size_sampled():
     w = WORKLOADS["gemm8192"]
     _say("gemm8192 one tile per workgroup, sampled")
