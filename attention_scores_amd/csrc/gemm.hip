@@ -105,6 +105,23 @@ struct StageLoads {
         if constexpr (RAGGED) klim = (uint32_t)__builtin_amdgcn_readfirstlane(klim_);
         live = live_;
     }
+    // Load i of a stage that lies a_add / b_add bytes past the resources'
+    // origins and lds_add bytes past this wave's first LDS row (resources
+    // set up once for a whole tile).
+    __device__ void issue_at(int i, const LaneOffsets<OpA, OpB>& o, uint32_t a_add, uint32_t b_add,
+                             uint32_t lds_add) const {
+        if (i < OpA::kLoadsPerWave) {
+            uint32_t v = o.a[i] + a_add;
+            if constexpr (RAGGED && OpA::kKMaj) v = o.akc[(i >> OpA::kGroupBit) & 1] < klim ? v : kOob;
+            if constexpr (NT_A) lds_dma16_nt(ra, v, sa + lds_add + i * 1024);
+            else lds_dma16(ra, v, sa + lds_add + i * 1024);
+        } else {
+            const int j = i - OpA::kLoadsPerWave;
+            uint32_t v = o.b[j] + b_add;
+            if constexpr (RAGGED && OpB::kKMaj) v = o.bkc[(j >> OpB::kGroupBit) & 1] < klim ? v : kOob;
+            lds_dma16(rb, v, sb + lds_add + j * 1024);
+        }
+    }
     __device__ void issue(int i, const LaneOffsets<OpA, OpB>& o) const {
         if (!live) return;
         if (i < OpA::kLoadsPerWave) {
@@ -483,6 +500,20 @@ struct StageCursor {
     }
     // Valid k of the stage: BK, or K mod BK in a partial last stage.
     __device__ int klim() const { return (a.krem != 0 && ks == a.ktiles - 1) ? a.krem : BK; }
+    // The current tile's operand origins (K stage 0) and the bytes from
+    // there to the end of each operand's last valid chunk.
+    __device__ const uint16_t* tile_a() const { return pa - ks * a_step; }
+    __device__ const uint16_t* tile_b() const { return pb - ks * b_step; }
+    __device__ int tile_a_bytes() const {
+        if constexpr (!RAGGED) return 0x7fffffff;
+        const int64_t mr = a.M - (int64_t)tm * TILE;
+        return A_K ? extent(mr, a.K, a.a_ld) : extent(a.K, mr, a.a_ld);
+    }
+    __device__ int tile_b_bytes() const {
+        if constexpr (!RAGGED) return 0x7fffffff;
+        const int64_t nr = a.N - (int64_t)tn * TILE;
+        return B_K ? extent(nr, a.K, a.b_ld) : extent(a.K, nr, a.b_ld);
+    }
 };
 
 // Pipeline (S LDS buffers; a stage is BK deep in K, NS = BK / (the MFMA's
@@ -571,80 +602,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
 
     const int KT = a.ktiles;
     StageLoads<OpA, OpB, RAGGED, NT_A> ld;
-    if constexpr (S > 2 && MI == 32) {
-        // One tile whose K stages all fit the ring (short products on the 64
-        // tile): every stage is requested at once and waited for once, and
-        // the tile's k16 substeps then run without barriers, their fragments
-        // read kAhead-1 substeps ahead.  Nothing refills the ring, so reads
-        // may run across stage boundaries.  The general loop below pays a
-        // barrier and a fragment read latency per stage of only 4 MFMAs
-        // (512^3: 6.6 us per launch there, 6.2 us here).  The MFMA order is
-        // the general loop's, so the results are bitwise the same.
-        if (KT <= S && first + stride >= end) {
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-                if (s < KT) {
-                    ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(),
-                             cur_ld.klim(), true);
-#pragma unroll
-                    for (int i = 0; i < L; ++i) ld.issue(i, off);
-                    cur_ld.advance();
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-            asm volatile("s_barrier" ::: "memory");
-
-            constexpr int kAhead = 4;
-            const int nsub = KT * NS;
-            typename Mfma<MI>::Acc acc[TM][TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = typename Mfma<MI>::Acc{};
-            Frags<TM, TN> f[kAhead];
-#pragma unroll
-            for (int u = 0; u < kAhead - 1; ++u) {
-                if (u < nsub) {
-#pragma unroll
-                    for (int q = 0; q < TM + TN; ++q)
-                        read_unit<OpA, OpB>(f[u], q, smem + (u / NS) * kStage, u % NS, m0, n0, lane);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < S * NS; ++u) {
-                if (u < nsub) {
-                    const int v = u + kAhead - 1;
-                    if (v < nsub) {
-#pragma unroll
-                        for (int q = 0; q < TM + TN; ++q)
-                            read_unit<OpA, OpB>(f[v % kAhead], q, smem + (v / NS) * kStage, v % NS, m0, n0, lane);
-                    }
-#pragma unroll
-                    for (int t = 0; t < TM * TN; ++t)
-                        acc[t / TN][t % TN] =
-                            Mfma<MI>::run(f[u % kAhead].a[t / TN], f[u % kAhead].b[t % TN], acc[t / TN][t % TN]);
-                }
-            }
-
-            int bb, tm, tn;
-            logical_tile<int>(first, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
-            const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
-            const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
-            const int64_t m_lim = a.M - r0, n_lim = a.N - c0;
-            // Every wave is done reading the ring before it holds 32-row staging.
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-            asm volatile("s_barrier" ::: "memory");
-            int el = lane;
-            if constexpr (RAGGED) asm volatile("" : "+v"(el));
-            if (RAGGED && !full)
-                epilogue<MI, WTM, WTN, ER, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim,
-                                                             n_lim);
-            else
-                epilogue<MI, WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld,
-                                                     el);
-            return;
-        }
-    }
     // Stages past the end are skipped only with a ring deeper than two (the
     // 64 tile, whose short products end with S-1 such steps); the two-stage
     // kernels keep one constant wait and a branch-free main loop.
@@ -762,6 +719,154 @@ constexpr int kBK = 64;
 template <int TILE>
 constexpr int stages_of() { return TILE == 64 ? 8 : 2; }
 
+// k16 substeps U0 .. U1-1 of a tile whose stages sit in the ring (substep u:
+// stage u / NS, k16 step u % NS), fragments read three substeps ahead; the
+// fixed order keeps every wait to the reads it needs.
+template <class OpA, class OpB, int MI, int TM, int TN, int NS, int U0, int U1, int kStage>
+__device__ __forceinline__ void ring_substeps(typename Mfma<MI>::Acc (&acc)[TM][TN], const char* smem, int m0, int n0,
+                                              int lane) {
+    constexpr int kAhead = 4;
+    Frags<TM, TN> f[kAhead];
+#pragma unroll
+    for (int u = U0; u < U0 + kAhead - 1; ++u) {
+        if (u < U1) {
+#pragma unroll
+            for (int q = 0; q < TM + TN; ++q)
+                read_unit<OpA, OpB>(f[u % kAhead], q, smem + (u / NS) * kStage, u % NS, m0, n0, lane);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = U0; u < U1; ++u) {
+        const int v = u + kAhead - 1;
+        if (v < U1) {
+#pragma unroll
+            for (int q = 0; q < TM + TN; ++q)
+                read_unit<OpA, OpB>(f[v % kAhead], q, smem + (v / NS) * kStage, v % NS, m0, n0, lane);
+        }
+#pragma unroll
+        for (int t = 0; t < TM * TN; ++t)
+            acc[t / TN][t % TN] = Mfma<MI>::run(f[u % kAhead].a[t / TN], f[u % kAhead].b[t % TN], acc[t / TN][t % TN]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Short products on the 64 tile: every workgroup has one tile, and all of
+// the tile's K stages (KT <= 8) fit the 8-stage ring.  The general loop
+// spends most of such a product's time on each wave's own stage loads (a
+// wave-wide LDS-DMA load holds the wave that issues it for tens of cycles,
+// and 512^3 asks 32 of each of 4 waves; the per-stage resources add
+// dependent scalar work) and on a barrier and a fragment read latency per
+// stage of only 4 MFMAs.  Here the roles are split: waves 4..7 request the
+// first half of the stages, release it with a barrier once it has landed,
+// then do the same for the second half; waves 0..3 (2 x 2 of 32 x 32, as in
+// the general kernel) run the MFMAs of the first half while the second is
+// still loading, reading fragments three k16 steps ahead across stage
+// boundaries.  The loads use one buffer resource per operand at the tile
+// origin and add each stage's offset to the lane offsets (the caller checks
+// that those stay below 2^31).  Stage s of the ring holds K stage
+// (ks + s) mod KT, and each output element accumulates the same MFMA chain
+// as in the general kernel, so the results are bitwise the same.  512^3:
+// 6.6 us per launch in the general loop, 4.3 us here.
+template <int KT, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED, bool NT_A>
+__device__ __forceinline__ void short64_tile(const KArgs& a, char* smem, int w, int lane, int first) {
+    constexpr int TILE = 64, BK = kBK, MI = 32, NW = 4;
+    constexpr int WTM = 32, WTN = 32, TM = 1, TN = 1;
+    constexpr int NS = BK / Mfma<MI>::kK;
+    using OpA = OperandTile<TILE, A_K, BK, NW>;
+    using OpB = OperandTile<TILE, B_K, BK, NW>;
+    constexpr int kStage = OpA::kBytes + OpB::kBytes;
+    constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;
+    constexpr int KH = (KT + 1) / 2;                 // stages of the first release
+    constexpr int ER = 8 * WTN / (OUT_BF16 ? 8 : 4) >= 64 ? 8 : 16;
+    using Epi8 = EpiRegion<WTN, ER>;
+    using Epi32 = EpiRegion<WTN, 32>;
+    StageCursor<TILE, BK, A_K, B_K, RAGGED> cur(a, first, 1, first + 1);
+
+    if (w >= NW) {
+        // Loader: the pieces compute wave w - 4 loads in the general kernel.
+        const int lw = w - NW;
+        LaneOffsets<OpA, OpB> off;
+#pragma unroll
+        for (int i = 0; i < OpA::kLoadsPerWave; ++i) off.a[i] = OpA::src_offset(lw, i, lane, a.a_ld);
+#pragma unroll
+        for (int i = 0; i < OpB::kLoadsPerWave; ++i) off.b[i] = OpB::src_offset(lw, i, lane, a.b_ld);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            off.akc[p] = (uint32_t)OpA::inner_of(lw, p << OpA::kGroupBit, lane);
+            off.bkc[p] = (uint32_t)OpB::inner_of(lw, p << OpB::kGroupBit, lane);
+        }
+        StageLoads<OpA, OpB, RAGGED, NT_A> ld;
+        ld.setup(smem, lw, cur.tile_a(), cur.tile_b(), cur.tile_a_bytes(), cur.tile_b_bytes(), BK, true);
+        const uint32_t astep = (uint32_t)(cur.a_step * 2), bstep = (uint32_t)(cur.b_step * 2);
+        const int ks0 = cur.ks;
+        auto issue_stage = [&](int s) __attribute__((always_inline)) {
+            const int kk = ks0 + s < KT ? ks0 + s : ks0 + s - KT;
+            if constexpr (RAGGED) ld.klim = (a.krem != 0 && kk == KT - 1) ? a.krem : BK;
+#pragma unroll
+            for (int i = 0; i < L; ++i) ld.issue_at(i, off, kk * astep, kk * bstep, s * kStage);
+        };
+#pragma unroll
+        for (int s = 0; s < KH; ++s) issue_stage(s);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        asm volatile("s_barrier" ::: "memory");     // release the first half
+#pragma unroll
+        for (int s = KH; s < KT; ++s) issue_stage(s);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        asm volatile("s_barrier" ::: "memory");     // release the second half
+        asm volatile("s_barrier" ::: "memory");     // the compute waves' last reads of the ring
+        return;
+    }
+
+    const int wm = w / 2, wn = w % 2;
+    const int m0 = wm * WTM, n0 = wn * WTN;
+    typename Mfma<MI>::Acc acc[TM][TN];
+    acc[0][0] = typename Mfma<MI>::Acc{};
+    asm volatile("s_barrier" ::: "memory");         // stages 0 .. KH-1 are in the ring
+    ring_substeps<OpA, OpB, MI, TM, TN, NS, 0, KH * NS, kStage>(acc, smem, m0, n0, lane);
+    asm volatile("s_barrier" ::: "memory");         // stages KH .. KT-1 too
+    ring_substeps<OpA, OpB, MI, TM, TN, NS, KH * NS, KT * NS, kStage>(acc, smem, m0, n0, lane);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    asm volatile("s_barrier" ::: "memory");         // every wave is done reading the ring
+
+    int bb, tm, tn;
+    logical_tile<int>(first, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
+    const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
+    const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
+    int el = lane;
+    if constexpr (RAGGED) asm volatile("" : "+v"(el));
+    if (RAGGED && !full)
+        epilogue<MI, WTM, WTN, ER, OUT_BF16, RAGGED>(acc, smem + KT * kStage + w * Epi8::kBytes, a.C, bb * a.c_bs, r0,
+                                                     c0, a.c_ld, el, a.M - r0, a.N - c0);
+    else if constexpr (KT * kStage >= NW * Epi32::kBytes)
+        epilogue<MI, WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+    else
+        epilogue<MI, WTM, WTN, ER, OUT_BF16>(acc, smem + KT * kStage + w * Epi8::kBytes, a.C, bb * a.c_bs, r0, c0,
+                                             a.c_ld, el);
+}
+
+template <bool A_K, bool B_K, bool OUT_BF16, bool RAGGED, bool NT_A>
+__global__ void __launch_bounds__(512, 1) gemm_short64_kernel(KArgs a) {
+    constexpr int kStage = 2 * 64 * kBK * 2;
+    constexpr int ER = 8 * 32 / (OUT_BF16 ? 8 : 4) >= 64 ? 8 : 16;
+    __shared__ __attribute__((aligned(1024))) char smem[8 * kStage + 4 * EpiRegion<32, ER>::kBytes];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int first, stride, end;
+    tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, a.xcd_split != 0, first, stride, end);
+    if (first >= end) return;
+    switch (a.ktiles) {
+        case 1: short64_tile<1, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+        case 2: short64_tile<2, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+        case 3: short64_tile<3, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+        case 4: short64_tile<4, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+        case 5: short64_tile<5, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+        case 6: short64_tile<6, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+        case 7: short64_tile<7, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+        default: short64_tile<8, A_K, B_K, OUT_BF16, RAGGED, NT_A>(a, smem, w, lane, first); break;
+    }
+}
+
 // Wave grid and MFMA of a workgroup.
 //   256 tile: 16x16x32 MFMAs; 2 x 4 waves of 128 x 64, two waves per SIMD,
 //     so that while one waits on its fragment reads or the stage barrier
@@ -782,6 +887,18 @@ struct WaveGrid {
     static constexpr int MI = TILE == 256 ? 16 : 32;
 };
 
+// A 64-tile product whose workgroups each get one tile with all K stages in
+// the ring, and whose stage offsets fit the 32-bit lane offsets, runs
+// gemm_short64_kernel.
+inline bool short64_fits(const GemmDesc& d, const KArgs& k) {
+    if (k.ktiles > 8 || d.grid < d.tiles) return false;
+    const int64_t a_step = d.a_kmajor ? kBK : (int64_t)kBK * k.a_ld;
+    const int64_t b_step = d.b_kmajor ? kBK : (int64_t)kBK * k.b_ld;
+    const int64_t a_span = (int64_t)(k.ktiles - 1) * a_step * 2 + (int64_t)(d.a_kmajor ? 64 : kBK) * k.a_ld * 2;
+    const int64_t b_span = (int64_t)(k.ktiles - 1) * b_step * 2 + (int64_t)(d.b_kmajor ? 64 : kBK) * k.b_ld * 2;
+    return a_span < 0x7fffffff && b_span < 0x7fffffff;
+}
+
 template <int TILE, bool A_K, bool B_K, bool OUT_BF16, bool NT_A>
 void launch_nt(const GemmDesc& d, const KArgs& k, hipStream_t s) {
     using WR = WaveGrid<TILE, true, OUT_BF16>;
@@ -789,6 +906,13 @@ void launch_nt(const GemmDesc& d, const KArgs& k, hipStream_t s) {
     const bool ragged = d.M % TILE || d.N % TILE || d.K % kBK;
     const dim3 grid((unsigned)d.grid);
     constexpr int S = stages_of<TILE>();
+    if constexpr (TILE == 64) {
+        if (short64_fits(d, k)) {
+            if (ragged) gemm_short64_kernel<A_K, B_K, OUT_BF16, true, NT_A><<<grid, dim3(512), 0, s>>>(k);
+            else gemm_short64_kernel<A_K, B_K, OUT_BF16, false, NT_A><<<grid, dim3(512), 0, s>>>(k);
+            return;
+        }
+    }
     if (ragged)
         gemm_kernel<TILE, kBK, S, WR::M, WR::N, WR::MI, A_K, B_K, OUT_BF16, true, NT_A>
             <<<grid, dim3(64 * WR::M * WR::N), 0, s>>>(k);

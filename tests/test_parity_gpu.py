@@ -508,9 +508,10 @@ def test_resident_grid_64_tiles_bit_exact(K, out, a_k, b_k):
 
 @pytest.mark.parametrize("K,out,rotate", [(512, "f32", False), (200, "bf16", False), (448, "f32", True)])
 def test_64_tile_short_product_paths_agree(K, out, rotate):
-    # On 64 x 64 tiles a workgroup with one tile whose K stages all fit the
-    # 8-stage ring runs them without per-stage barriers; a workgroup with
-    # several tiles runs the general ring loop.  Both issue the same MFMAs in
+    # On 64 x 64 tiles, a product whose workgroups each get one tile with all
+    # its K stages in the 8-stage ring runs the short-product kernel (stage
+    # loads by separate waves, released in two halves); with several tiles
+    # per workgroup the general ring loop runs.  Both issue the same MFMAs in
     # the same order: slice 0 of an 8-slice product (512 tiles over 256
     # workgroups: the general loop) must equal the 1-slice product (64 tiles:
     # one each) bit for bit, on random data, and lie within tolerance.
