@@ -535,6 +535,36 @@ def test_64_tile_short_product_paths_agree(K, out, rotate):
     assert nfail == 0, util
 
 
+@pytest.mark.parametrize("M,N,K,batch,a_k,b_k,out,extra", [
+    (200, 136, 320, 3, True, False, "f32", 0),                                         # ragged M, N; 5 stages
+    (130, 250, 456, 2, False, True, "bf16", 0),                                        # partial last K stage
+    (256, 192, 512, 1, True, False, "bf16", "rotate_nt"),                             # rotated, non-temporal A
+    (64, 64, 8, 1, True, True, "f32", 0),                                              # one partial stage
+])
+def test_short_product_kernel_bit_exact(M, N, K, batch, a_k, b_k, out, extra):
+    # 64 x 64 tiles with every workgroup holding one tile and K <= 512: the
+    # short-product kernel (separate loader waves, stage offsets in the lane
+    # offsets).  Integer data, NaN-padded operands, sentinel-filled C:
+    # bit-exact against the oracle and nothing stored outside C.
+    flags = asl.AS_FLAG_TILE_64
+    if extra == "rotate_nt":
+        flags |= asl.AS_FLAG_ROTATE_K | asl.AS_FLAG_NT_A
+    _say("short product %dx%dx%d batch=%d a_k=%s b_k=%s out=%s %s" % (M, N, K, batch, a_k, b_k, out, extra))
+    _ragged(M, N, K, batch, a_k, b_k, out, flags, 5100 + K)
+
+
+def test_short_product_kernel_broadcast_B_bit_exact():
+    # the same kernel with B shared by all slices (batch stride 0)
+    M, N, K, batch = 192, 128, 384, 3
+    _say("short product, broadcast B")
+    A = draw((batch, M, K), "int", -4, 4, 5201)
+    B = draw((K, N), "int", -4, 4, 5202)
+    sa, sb = (K, 1, M * K), (N, 1, 0)
+    C = _run_gemm(A, B, M, N, K, batch, sa, sb, torch.float32, asl.AS_FLAG_TILE_64)
+    Cref, _ = oracle.gemm(bits(A), bits(B), batch, M, N, K, sa, sb, want_T=False)
+    assert np.array_equal(_decode(C), Cref)
+
+
 def test_one_tile_per_workgroup_full_size_sampled():
     w = WORKLOADS["gemm8192"]
     _say("gemm8192 one tile per workgroup, sampled")
