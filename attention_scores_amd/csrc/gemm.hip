@@ -61,8 +61,10 @@ struct KArgs {
     int64_t M, N, K;      // problem sizes (edge tiles are partial)
     int32_t ktiles;       // ceil(K / BK) stages per tile
     int32_t krem;         // K mod BK: valid k of the last stage (0: the last stage is full)
-    int32_t tiles, tiles_m, tiles_n, group_m, grouped, xcd_split;
+    int32_t tiles, xcd_split;
     int32_t rotate;       // tile row tm starts its K loop at stage tm mod ktiles
+    TileMap map;          // logical tile -> (batch, tile row, tile column)
+    DivU31 kdiv;          // division by ktiles
 };
 
 // Per-lane source offsets of a wave's stage loads.  For the last, partial K
@@ -454,8 +456,8 @@ struct StageCursor {
     __device__ bool live() const { return t < end; }
     __device__ void origins() {
         int bb;
-        logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
-        ks = a.rotate ? tm % a.ktiles : 0;
+        a.map.coords((uint32_t)t, bb, tm, tn);
+        ks = a.rotate ? tm - (int)a.kdiv.div((uint32_t)tm) * a.ktiles : 0;
         pa = a.A + bb * a.a_bs + (A_K ? (int64_t)tm * TILE * a.a_ld : (int64_t)tm * TILE) + ks * a_step;
         pb = a.B + bb * a.b_bs + (B_K ? (int64_t)tn * TILE * a.b_ld : (int64_t)tn * TILE) + ks * b_step;
     }
@@ -681,7 +683,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
         }
 
         int bb, tm, tn;
-        logical_tile<int>(t, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
+        a.map.coords((uint32_t)t, bb, tm, tn);
         const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
         const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
         const int64_t m_lim = a.M - r0, n_lim = a.N - c0;   // rows / columns of the wave's block inside C
@@ -830,7 +832,7 @@ __device__ __forceinline__ void short64_tile(const KArgs& a, char* smem, int w, 
     asm volatile("s_barrier" ::: "memory");         // every wave is done reading the ring
 
     int bb, tm, tn;
-    logical_tile<int>(first, a.tiles_m, a.tiles_n, a.group_m, a.grouped != 0, bb, tm, tn);
+    a.map.coords((uint32_t)first, bb, tm, tn);
     const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
     const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
     int el = lane;
@@ -947,11 +949,16 @@ int launch_tile(const GemmDesc& d, const KArgs& k, hipStream_t s) {
 
 }  // namespace kern
 
+// Slot i is round i div P of hardware workgroup i mod P (P = d.grid); the
+// tile comes from the kernels' own walk and map.
 bool tile_of_slot(const GemmDesc& d, int64_t i, int64_t* b, int64_t* tm, int64_t* tn) {
-    int64_t bb, m, n;
-    if (!asl::tile_of_slot<int64_t>(i, d.grid, d.tiles, d.tiles_m, d.tiles_n, d.group_m, d.grouped, d.xcd_split, bb,
-                                    m, n))
-        return false;
+    const int64_t h = i % d.grid, j = i / d.grid;
+    int64_t first, stride, end;
+    tile_walk<int64_t>(h, d.grid, d.tiles, d.xcd_split, first, stride, end);
+    const int64_t L = first + j * stride;
+    if (L >= end) return false;
+    int bb, m, n;
+    TileMap::of(d.tiles_m, d.tiles_n, d.group_m, d.grouped).coords((uint32_t)L, bb, m, n);
     *b = bb;
     *tm = m;
     *tn = n;
@@ -975,12 +982,10 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
     k.N = d.N;
     k.K = d.K;
     k.tiles = (int32_t)d.tiles;
-    k.tiles_m = (int32_t)d.tiles_m;
-    k.tiles_n = (int32_t)d.tiles_n;
-    k.group_m = d.group_m;
-    k.grouped = d.grouped ? 1 : 0;
     k.xcd_split = d.xcd_split ? 1 : 0;
     k.rotate = d.rotate_k ? 1 : 0;
+    k.map = TileMap::of(d.tiles_m, d.tiles_n, d.group_m, d.grouped);
+    k.kdiv = DivU31::of((uint32_t)((d.K + kBK - 1) / kBK));
     hipStream_t s = (hipStream_t)stream;
     if (d.tile == 256) return launch_tile<256>(d, k, s);
     if (d.tile == 64) return launch_tile<64>(d, k, s);

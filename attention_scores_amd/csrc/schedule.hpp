@@ -38,6 +38,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+
 namespace asl {
 
 constexpr int kXcds = 8;
@@ -71,6 +73,68 @@ __host__ __device__ inline void logical_tile(I L, I tiles_m, I tiles_n, I group_
     }
 }
 
+// Unsigned division by a divisor fixed for a whole launch, for dividends
+// below 2^31.  With l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n div d = (n + mulhi(m, n)) >> l (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994, section 4, the
+// unsigned case); mulhi(m, n) < n, so the sum stays below 2^32.  On the
+// device a division by a run-time value is a loop of about forty scalar
+// instructions; this is three.
+struct DivU31 {
+    uint32_t m, l;
+    // 1 <= d < 2^31 (host).
+    static DivU31 of(uint32_t d) {
+        uint32_t l = 0;
+        while ((uint64_t(1) << l) < d) ++l;
+        return DivU31{(uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1), l};
+    }
+    __host__ __device__ uint32_t div(uint32_t n) const {
+        return ((uint32_t)(((uint64_t)n * m) >> 32) + n) >> l;
+    }
+};
+
+// logical_tile of one launch with its divisors prepared on the host: the
+// form the kernels evaluate at every tile they visit (and gemm_plan_tile_of
+// on the host).  Needs tiles_m * tiles_n * batch < 2^31 and
+// group_m <= tiles_m, which the planner guarantees.
+struct TileMap {
+    int32_t tiles_m, tiles_n, group_m, grouped;
+    DivU31 per_b, width, group, group_tail, cols;   // divisors tiles_m*tiles_n, group_m*tiles_n, group_m,
+                                                    // tiles_m mod group_m (the last band, if partial), tiles_n
+    static TileMap of(int64_t tiles_m, int64_t tiles_n, int64_t group_m, bool grouped) {
+        TileMap t;
+        t.tiles_m = (int32_t)tiles_m;
+        t.tiles_n = (int32_t)tiles_n;
+        t.group_m = (int32_t)group_m;
+        t.grouped = grouped ? 1 : 0;
+        t.per_b = DivU31::of((uint32_t)(tiles_m * tiles_n));
+        t.width = DivU31::of((uint32_t)(group_m * tiles_n));
+        t.group = DivU31::of((uint32_t)group_m);
+        t.group_tail = DivU31::of(tiles_m % group_m ? (uint32_t)(tiles_m % group_m) : 1u);
+        t.cols = DivU31::of((uint32_t)tiles_n);
+        return t;
+    }
+    __host__ __device__ void coords(uint32_t L, int& b, int& tm, int& tn) const {
+        const uint32_t bq = per_b.div(L);
+        const uint32_t t = L - bq * (uint32_t)(tiles_m * tiles_n);
+        b = (int)bq;
+        if (grouped) {
+            const uint32_t gid = width.div(t);
+            const uint32_t first = gid * (uint32_t)group_m;
+            const uint32_t in = t - gid * (uint32_t)(group_m * tiles_n);
+            const bool tail = (uint32_t)tiles_m - first < (uint32_t)group_m;
+            const uint32_t gsz = tail ? (uint32_t)tiles_m - first : (uint32_t)group_m;
+            const uint32_t q = (tail ? group_tail : group).div(in);
+            tm = (int)(first + (in - q * gsz));
+            tn = (int)q;
+        } else {
+            const uint32_t q = cols.div(t);
+            tm = (int)q;
+            tn = (int)(t - q * (uint32_t)tiles_n);
+        }
+    }
+};
+
 // Logical tiles workgroup h of a P-workgroup grid visits: first, first +
 // stride, ... while < end.  xcd_split: each XCD walks its own range (step 1).
 template <typename I>
@@ -87,21 +151,6 @@ __host__ __device__ inline void tile_walk(I h, I P, I tiles, bool xcd_split, I& 
     first = start + s;
     stride = P / kXcds + (x < P % kXcds ? 1 : 0);
     end = start + count;
-}
-
-// Tile computed in execution slot i = j*P + h (round j of workgroup h), for
-// i < tiles; returns false if that slot is empty.  Slot i runs on XCD i mod 8
-// when P is a multiple of 8 or P == tiles.
-template <typename I>
-__host__ __device__ inline bool tile_of_slot(I i, I P, I tiles, I tiles_m, I tiles_n, I group_m, bool grouped,
-                                             bool xcd_split, I& b, I& tm, I& tn) {
-    const I h = i % P, j = i / P;
-    I first, stride, end;
-    tile_walk<I>(h, P, tiles, xcd_split, first, stride, end);
-    const I L = first + j * stride;
-    if (L >= end) return false;
-    logical_tile<I>(L, tiles_m, tiles_n, group_m, grouped, b, tm, tn);
-    return true;
 }
 
 }  // namespace asl

@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: exports, status codes, argument validation,
-plan registry and the workgroup -> tile schedule (host replica of the device map)."""
+plan registry and the workgroup -> tile schedule (the kernels' own map, evaluated on the host)."""
 import ctypes
 import os
 import re
@@ -199,6 +199,64 @@ def test_schedule_is_a_bijection(M, N, K, batch, flags):
     assert len(seen) == wg
     assert _status(asl.gemm_plan_tile_of, p, wg) == asl.AS_ERR_INVALID
     asl.gemm_destroy(p)
+
+
+def _slot_model(slot, P, tiles, tiles_m, tiles_n, gm, grouped, xcd_split):
+    """Execution slot -> (batch, tile row, tile column) written out with plain
+    integer division: XCD x owns the contiguous range [x*q + min(x, r), ...)
+    of q or q+1 logical tiles and its workgroups stride through it; logical
+    tiles walk bands of gm tile rows column by column (a partial last band
+    keeps its own height)."""
+    h, j = slot % P, slot // P
+    if xcd_split:
+        x, s = h % 8, h // 8
+        q, r = divmod(tiles, 8)
+        start, count = x * q + min(x, r), q + (1 if x < r else 0)
+        first, stride, end = start + s, P // 8 + (1 if x < P % 8 else 0), start + count
+    else:
+        first, stride, end = h, P, tiles
+    L = first + j * stride
+    if L >= end:
+        return None
+    b, t = divmod(L, tiles_m * tiles_n)
+    if not grouped:
+        return b, t // tiles_n, t % tiles_n
+    band, inn = divmod(t, gm * tiles_n)
+    top = band * gm
+    height = min(tiles_m - top, gm)
+    return b, top + inn % height, inn // height
+
+
+@pytest.mark.parametrize("M,N,K,batch,flags,nsample", [
+    (1000, 3000, 96, 3, 0, None),                         # 8 x 24 tiles of 128, batch 3, bands of 8
+    (7680, 8192, 8192, 1, 0, None),                       # 30 x 32 tiles of 256, bands of 4: last band 2
+    (7936, 6144, 4096, 1, 0, None),                       # 31 x 24, bands of 4: last band 3
+    (2600, 4096, 128, 3, 0, None),                        # 21 x 32 tiles of 128 x 3, bands of 16: last band 5
+    (2000, 9000, 1024, 1, asl.AS_FLAG_TILE_128, None),    # 16 x 71
+    (2048, 2048, 128, 7, asl.AS_FLAG_NO_XCD_SPLIT, None),
+    (3000, 3000, 1024, 2, asl.AS_FLAG_NO_GROUPING, None),
+    (1000000, 999936, 1024, 1, 0, 4000),                  # 3907 x 3906 tiles: a divisor near 2^24, last band 3
+    (1000000, 2000, 512, 700, asl.AS_FLAG_TILE_128, 4000),  # 7813 x 16 x 700 tiles: dividends near 2^26
+])
+def test_tile_map_equals_the_plain_division_definition(M, N, K, batch, flags, nsample):
+    # The kernels map a logical tile to its coordinates with multiply-high
+    # division by divisors prepared on the host; gemm_plan_tile_of evaluates
+    # that same map.  Compare it with the definition written with plain
+    # integer division, for the plan's group size (one of 1, 2, 4, ..., 64).
+    import random
+    p = asl.gemm_create(M, N, K, batch, (K, 1, M * K), (N, 1, K * N), (N, 1, M * N), flags=flags)
+    tm, tn, _, wg, grid = asl.gemm_plan_info(p)
+    assert asl.gemm_plan_split_k(p)[0] == 1
+    tiles_m, tiles_n = -(-M // tm), -(-N // tn)
+    rng = random.Random(M ^ N ^ batch)
+    slots = range(wg) if nsample is None else sorted({0, wg - 1, *(rng.randrange(wg) for _ in range(nsample))})
+    got = {h: asl.gemm_plan_tile_of(p, h) for h in slots}
+    asl.gemm_destroy(p)
+    grouped = not flags & asl.AS_FLAG_NO_GROUPING
+    xcd_split = grouped and not flags & asl.AS_FLAG_NO_XCD_SPLIT
+    matches = [gm for gm in (1, 2, 4, 8, 16, 32, 64) if gm <= tiles_m and all(
+        _slot_model(h, grid, wg, tiles_m, tiles_n, gm, grouped, xcd_split) == got[h] for h in slots)]
+    assert matches, (M, N, K, batch, flags)
 
 
 def _wave_panels(p, wg, cus_per_xcd=32):
