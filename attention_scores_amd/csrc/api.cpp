@@ -314,6 +314,7 @@ asl::GemmDesc split_launch_desc(const asl::GemmDesc& d) {
     e.c_row = d.ws_ld;
     e.c_batch = d.M * d.ws_ld;
     e.c_bf16 = false;
+    e.c_keep = true;   // the reduction reads the partial sums next
     e.tiles = d.tiles * d.splits;
     e.splits = 1;
     return e;

@@ -65,6 +65,16 @@ struct KArgs {
     int32_t rotate;       // tile row tm starts its K loop at stage tm mod ktiles
     TileMap map;          // logical tile -> (batch, tile row, tile column)
     DivU31 kdiv;          // division by ktiles
+    int32_t c_keep;       // C is read again right away (a split product's partial sums): the
+                          // general kernel stores it with ordinary stores, so its lines stay in
+                          // L2 and the MALL; otherwise (and in the short-product kernel)
+                          // non-temporal stores
+};
+
+// A compile-time flag passed as a value (to generic lambdas).
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
 };
 
 // Per-lane source offsets of a wave's stage loads.  For the last, partial K
@@ -319,7 +329,11 @@ __device__ __forceinline__ void read_back_map(int l, int& rl, int& cp, int& s) {
 // 16-byte pieces: WTN*4-byte (fp32) or WTN*2-byte (bf16, rounded to nearest
 // even right before its store) runs, whole 128-byte lines for WTN >= 64.
 // The stores are non-temporal: C is written once and not re-read, so it
-// should not push A and B out of L2.
+// should not push A and B out of L2.  KEEP (fp32 only): C is a split
+// product's partial sums, which the reduction reads next; ordinary stores
+// leave them in L2 and the MALL for it.  (A run-time choice between the two
+// store forms does not work: the compiler merges the two stores into one
+// and drops the non-temporal hint.)
 //
 // EDGE (a tile that extends past C): only rows < m_lim and columns < n_lim
 // of the block (counted from r0, c0) are stored; a 16-byte piece that
@@ -367,7 +381,7 @@ __device__ __forceinline__ void epilogue_stage(const typename Mfma<MI>::Acc (&ac
     }
 }
 
-template <int MI, int WTM, int WTN, int ROWS, bool OUT_BF16, bool EDGE = false>
+template <int MI, int WTM, int WTN, int ROWS, bool OUT_BF16, bool EDGE = false, bool KEEP = false>
 __device__ __forceinline__ void epilogue(const typename Mfma<MI>::Acc (&acc)[WTM / MI][WTN / MI], char* region,
                                          void* Cv, int64_t c_off, int64_t r0, int64_t c0, int64_t ldc, int lane,
                                          int64_t m_lim = 0, int64_t n_lim = 0) {
@@ -424,7 +438,8 @@ __device__ __forceinline__ void epilogue(const typename Mfma<MI>::Acc (&acc)[WTM
                 __builtin_nontemporal_store(__builtin_bit_cast(i16x8, o), (i16x8*)((__bf16*)Cv + gi));
             } else {
                 const f32x4 v = *(const lds_f32x4_t*)(lds_void_t*)(region + rd_a + qoff);
-                __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
+                if constexpr (KEEP) *(f32x4*)((float*)Cv + gi) = v;
+                else __builtin_nontemporal_store(v, (f32x4*)((float*)Cv + gi));
             }
         }
         wave_lds_order();                            // the next chunk overwrites what was just read
@@ -701,12 +716,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
         // the tile loop, where it would stay live in registers throughout.
         int el = lane;
         if constexpr (RAGGED) asm volatile("" : "+v"(el));
-        if (RAGGED && !full)
-            epilogue<MI, WTM, WTN, ER, OUT_BF16, RAGGED>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim, n_lim);
-        else if (last)
-            epilogue<MI, WTM, WTN, 32, OUT_BF16>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
-        else
-            epilogue<MI, WTM, WTN, ER, OUT_BF16>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+        auto store = [&](auto keep) {
+            constexpr bool K = decltype(keep)::value;
+            if (RAGGED && !full)
+                epilogue<MI, WTM, WTN, ER, OUT_BF16, RAGGED, K>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el, m_lim,
+                                                                n_lim);
+            else if (last)
+                epilogue<MI, WTM, WTN, 32, OUT_BF16, false, K>(acc, smem + w * Epi32::kBytes, a.C, bb * a.c_bs, r0, c0,
+                                                               a.c_ld, el);
+            else
+                epilogue<MI, WTM, WTN, ER, OUT_BF16, false, K>(acc, epi, a.C, bb * a.c_bs, r0, c0, a.c_ld, el);
+        };
+        if constexpr (OUT_BF16) store(Flag<false>{});
+        else if (a.c_keep) store(Flag<true>{});
+        else store(Flag<false>{});
         prev_full = full;
     }
 }
@@ -986,6 +1009,7 @@ int launch_gemm(const GemmDesc& d, const void* A, const void* B, void* C, void* 
     k.rotate = d.rotate_k ? 1 : 0;
     k.map = TileMap::of(d.tiles_m, d.tiles_n, d.group_m, d.grouped);
     k.kdiv = DivU31::of((uint32_t)((d.K + kBK - 1) / kBK));
+    k.c_keep = d.c_keep ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
     if (d.tile == 256) return launch_tile<256>(d, k, s);
     if (d.tile == 64) return launch_tile<64>(d, k, s);

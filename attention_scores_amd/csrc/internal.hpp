@@ -18,6 +18,7 @@ struct GemmDesc {
     bool a_kmajor;                   // A[i, k..k+7] contiguous
     bool b_kmajor;                   // B[k..k+7, j] contiguous
     bool c_bf16;                     // output rounded to bf16 (else fp32)
+    bool c_keep;                     // output read again right away (split-K partial sums): cached stores
     int tile;                        // 256 or 128 (square output tile)
     int group_m;                     // rows of tiles per group in the grouped order
     bool grouped;                    // band order of group_m tile rows (false: row-major, the identity)

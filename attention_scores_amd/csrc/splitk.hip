@@ -8,48 +8,58 @@
 #include <mutex>
 
 #include "internal.hpp"
+#include "schedule.hpp"
 #include "tile.hpp"
 
 namespace asl {
 namespace kern {
 
 // Split-K reduction: C[i][j] = ws[0][i][j] + ws[1][i][j] + ... in chunk
-// order, rounded to C's type.  A thread takes 4 consecutive columns of a
-// row (one 16-byte load per chunk: ws rows are a multiple of 4 floats); the
+// order, rounded to C's type.  Thread t takes the 4 consecutive columns of
+// group t mod `groups` of row t div `groups` (one 16-byte load per chunk: ws
+// rows are a multiple of 4 floats; the division by the launch constant is
+// a multiply-high, DivU31), with two chunks' loads in flight at a time; the
 // last group of a row stores only its columns below N.  Memory-bound: 4
 // bytes read per chunk and element, 2 or 4 written.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws, void* __restrict__ C,
-                                                            int32_t N, int32_t groups, int32_t total, int64_t ws_ld,
-                                                            int64_t ws_bs, int64_t c_ld, int32_t splits) {
-    for (int32_t t = blockIdx.x * 256 + threadIdx.x; t < total; t += gridDim.x * 256) {
-        const int32_t i = t / groups, j = (t - i * groups) * 4;
-        const float* p = ws + (int64_t)i * ws_ld + j;
-        f32x4 acc = __builtin_nontemporal_load((const f32x4*)p);
-        for (int32_t c = 1; c < splits; ++c) {
-            const f32x4 v = __builtin_nontemporal_load((const f32x4*)(p + c * ws_bs));
+                                                            int32_t N, DivU31 rows, int32_t groups, int32_t total,
+                                                            int64_t ws_ld, int64_t ws_bs, int64_t c_ld, int32_t splits) {
+    const int32_t t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int32_t i = (int32_t)rows.div((uint32_t)t), j = (t - i * groups) * 4;
+    const float* p = ws + (int64_t)i * ws_ld + j;
+    f32x4 acc = __builtin_nontemporal_load((const f32x4*)p);
+    int32_t c = 1;
+    for (; c + 2 < splits + 1; c += 2) {
+        const f32x4 v0 = __builtin_nontemporal_load((const f32x4*)(p + c * ws_bs));
+        const f32x4 v1 = __builtin_nontemporal_load((const f32x4*)(p + (c + 1) * ws_bs));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += v[e];
-        }
-        const int64_t o = (int64_t)i * c_ld + j;
-        if (j + 4 <= N) {
-            if constexpr (OUT_BF16) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                bf16x4 y;
+        for (int e = 0; e < 4; ++e) acc[e] = (acc[e] + v0[e]) + v1[e];
+    }
+    if (c < splits) {
+        const f32x4 v = __builtin_nontemporal_load((const f32x4*)(p + c * ws_bs));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = (__bf16)acc[e];
-                *((bf16x4*)((__bf16*)C + o)) = y;
-            } else {
-                *((f32x4*)((float*)C + o)) = acc;
-            }
+        for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    }
+    const int64_t o = (int64_t)i * c_ld + j;
+    if (j + 4 <= N) {
+        if constexpr (OUT_BF16) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (__bf16)acc[e];
+            *((bf16x4*)((__bf16*)C + o)) = y;
         } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (j + e < N) {
-                    if constexpr (OUT_BF16) ((__bf16*)C)[o + e] = (__bf16)acc[e];
-                    else ((float*)C)[o + e] = acc[e];
-                }
+            *((f32x4*)((float*)C + o)) = acc;
         }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e < N) {
+                if constexpr (OUT_BF16) ((__bf16*)C)[o + e] = (__bf16)acc[e];
+                else ((float*)C)[o + e] = acc[e];
+            }
     }
 }
 
@@ -89,15 +99,18 @@ int scratch_address(void** out) {
 
 int launch_splitk_reduce(const GemmDesc& d, const void* ws, void* C, void* stream) {
     const int64_t groups = d.ws_ld / 4, total = d.M * groups;   // < 2^31: split plans are small grids
-    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    const DivU31 rows = DivU31::of((uint32_t)groups);
     hipStream_t s = (hipStream_t)stream;
     const float* w = (const float*)ws;
     if (d.c_bf16)
-        kern::splitk_reduce_kernel<true><<<blocks, 256, 0, s>>>(w, C, (int32_t)d.N, (int32_t)groups, (int32_t)total,
-                                                                d.ws_ld, d.M * d.ws_ld, d.c_row, d.splits);
+        kern::splitk_reduce_kernel<true><<<blocks, 256, 0, s>>>(w, C, (int32_t)d.N, rows, (int32_t)groups,
+                                                                (int32_t)total, d.ws_ld, d.M * d.ws_ld, d.c_row,
+                                                                d.splits);
     else
-        kern::splitk_reduce_kernel<false><<<blocks, 256, 0, s>>>(w, C, (int32_t)d.N, (int32_t)groups, (int32_t)total,
-                                                                 d.ws_ld, d.M * d.ws_ld, d.c_row, d.splits);
+        kern::splitk_reduce_kernel<false><<<blocks, 256, 0, s>>>(w, C, (int32_t)d.N, rows, (int32_t)groups,
+                                                                 (int32_t)total, d.ws_ld, d.M * d.ws_ld, d.c_row,
+                                                                 d.splits);
     return (int)hipGetLastError();
 }
 
