@@ -108,12 +108,12 @@ struct StageLoads {
     uint32_t klim;
     bool live;         // the stage exists (false past the workgroup's last tile: nothing is requested)
 
-    __device__ void setup(const char* dst, int w, const uint16_t* a_src, const uint16_t* b_src, int a_bytes,
-                          int b_bytes, int klim_, bool live_) {
+    __device__ void setup(const char* dst_a, const char* dst_b, int w, const uint16_t* a_src, const uint16_t* b_src,
+                          int a_bytes, int b_bytes, int klim_, bool live_) {
         ra = make_rsrc(a_src, a_bytes);
         rb = make_rsrc(b_src, b_bytes);
-        sa = lds_u32(dst + w * OpA::kLoadsPerWave * 1024);
-        sb = lds_u32(dst + OpA::kBytes + w * OpB::kLoadsPerWave * 1024);
+        sa = lds_u32(dst_a + w * OpA::kLoadsPerWave * 1024);
+        sb = lds_u32(dst_b + w * OpB::kLoadsPerWave * 1024);
         if constexpr (RAGGED) klim = (uint32_t)__builtin_amdgcn_readfirstlane(klim_);
         live = live_;
     }
@@ -242,12 +242,14 @@ struct Frags16 {
 // go out at the last MFMA of every group of kEvery: all in the first MFMAs
 // (5 % slower at 8192^3: the burst competes with the fragment reads) or at
 // the first of each group (0.3 % slower) measured worse.
-template <class OpA, class OpB, int TM, int TN, int P, bool LOADS, bool RAGGED, bool NT_A>
-__device__ __forceinline__ void substep16(f32x4 (&acc)[TM][TN], Frags16<TM, TN>& f, const char* rd, int j, int m0,
-                                          int n0, int lane, const StageLoads<OpA, OpB, RAGGED, NT_A>& ld,
+template <class OpA, class OpB, int TM, int TN, int P, bool LOADS, bool RAGGED, bool NT_A, bool B_FIRST = false>
+__device__ __forceinline__ void substep16(f32x4 (&acc)[TM][TN], Frags16<TM, TN>& f, const char* rd, const char* rdb,
+                                          int j, int m0, int n0, int lane,
+                                          const StageLoads<OpA, OpB, RAGGED, NT_A>& ld,
                                           const LaneOffsets<OpA, OpB>& off) {
     constexpr int kMfma = TM * TN;
     constexpr int kLoads = StageLoads<OpA, OpB, RAGGED, NT_A>::kCount;
+    constexpr int kLA = OpA::kLoadsPerWave, kLB = OpB::kLoadsPerWave;
     static_assert(TN <= TM && TN >= 3, "B units ride on the first MFMA of a row, A on the third");
     static_assert(kLoads <= kMfma, "at most one load per MFMA");
     constexpr int kEvery = kMfma / kLoads;
@@ -257,9 +259,12 @@ __device__ __forceinline__ void substep16(f32x4 (&acc)[TM][TN], Frags16<TM, TN>&
         const int mi = t / TN, ni = t % TN;
         acc[mi][ni] = Mfma<16>::run(f.a[mi], f.b[P][ni], acc[mi][ni]);
         if constexpr (LOADS) {
-            if (t % kEvery == kEvery - 1) ld.issue(t / kEvery, off);
+            if (t % kEvery == kEvery - 1) {
+                const int q = t / kEvery;   // B_FIRST: the B loads, then the A loads
+                ld.issue(B_FIRST ? (q < kLB ? kLA + q : q - kLB) : q, off);
+            }
         }
-        if (ni == 0 && mi < TN) f.b[1 - P][mi] = OpB::frag16(rd + OpA::kBytes, n0 + 16 * mi, j, lane);
+        if (ni == 0 && mi < TN) f.b[1 - P][mi] = OpB::frag16(rdb, n0 + 16 * mi, j, lane);
         if (ni == 2 && mi > 0) f.a[mi - 1] = OpA::frag16(rd, m0 + 16 * (mi - 1), j, lane);
         if (mi == TM - 2 && ni == TN - 1) last = OpA::frag16(rd, m0 + 16 * (TM - 1), j, lane);
         __builtin_amdgcn_sched_barrier(0);
@@ -563,12 +568,22 @@ struct StageCursor {
 // NT_A (an A that streams from HBM, e.g. one tile column): A's loads carry
 // the non-temporal hint, so its lines leave L2 first and B stays resident.
 //
+// SA = 3 (split ring; streaming A, one tile-aligned 256x256 tile per
+// workgroup): A and B get rings of their own, A three stages deep and B two,
+// which fill the 160 KiB of LDS (no room for a between-tiles epilogue
+// region, and none is needed).  Step g requests B(g+2), then A(g+3), so the
+// sync's wait for stage g+1 (its B was requested before A(g+2)) leaves A's
+// next stage in flight: while the MFMAs of a step run, two stages of A are
+// on their way from HBM instead of one, and B, which comes from L2, keeps
+// its one-step lead.  The MFMA order is that of the two-stage ring, so C is
+// bitwise the same.
+//
 // RAGGED: M or N is not a multiple of TILE or K not of BK.  The stage
 // resources then cover exactly the valid bytes, the last partial K stage
 // masks its K-contiguous chunks, and edge tiles use the predicated epilogue;
 // otherwise none of that code is compiled in.
 template <int TILE, int BK, int S, int WGM, int WGN, int MI, bool A_K, bool B_K, bool OUT_BF16, bool RAGGED,
-          bool NT_A>
+          bool NT_A, int SA = 0>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int NW = WGM * WGN;        // waves, WGM along M by WGN along N
     constexpr int WTM = TILE / WGM;      // wave tile rows
@@ -582,8 +597,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     using OpB = OperandTile<TILE, B_K, BK, NW, MI == 16>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int L = OpA::kLoadsPerWave + OpB::kLoadsPerWave;   // loads per wave per stage
+    constexpr int LA = OpA::kLoadsPerWave;
     static_assert(L * (S - 1) < 64, "vmcnt holds at most 63");
-    constexpr int kWaitStage = L * (S - 2);                       // loads issued after the awaited stage's
+    // SA > S: A has a ring of its own, SA deep, B one of S (split ring).
+    constexpr int kSA = SA ? SA : S;
+    constexpr bool kSplit = kSA != S;
+    static_assert(!kSplit || (S == 2 && kSA == 3 && MI == 16 && !RAGGED && NT_A),
+                  "the split ring is built for streaming A on tile-aligned 16x16x32 products");
+    constexpr int kRing = kSplit ? kSA * OpA::kBytes + S * OpB::kBytes : S * kStage;
+    // loads issued after the awaited stage's (split ring: B goes first, so
+    // only the next A stage is still on its way)
+    constexpr int kWaitStage = kSplit ? LA : L * (S - 2);
     // Rows per chunk of a tile followed by another: 8, or 16 where 8 rows
     // of a narrow bf16 block are fewer than one 16-byte piece per lane.
     constexpr int ER = 8 * WTN / (OUT_BF16 ? 8 : 4) >= 64 ? 8 : 16;
@@ -591,21 +615,30 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     constexpr int kWaitAfterEpi = kWaitStage + kEpiStores < 63 ? kWaitStage + kEpiStores : 63;
     using Epi8 = EpiRegion<WTN, ER>;
     using Epi32 = EpiRegion<WTN, 32>;
-    static_assert(NW * Epi32::kBytes <= S * kStage, "last-tile epilogue must fit in the ring");
-    __shared__ __attribute__((aligned(1024))) char smem[S * kStage + NW * Epi8::kBytes];
+    static_assert(NW * Epi32::kBytes <= kRing, "last-tile epilogue must fit in the ring");
+    // The split ring leaves no room for the between-tiles region: it runs
+    // one tile per workgroup, so every tile is a last tile.
+    __shared__ __attribute__((aligned(1024))) char smem[kSplit ? kRing : S * kStage + NW * Epi8::kBytes];
+    auto abuf = [&](int i) __attribute__((always_inline)) {
+        return kSplit ? smem + i * OpA::kBytes : smem + i * kStage;
+    };
+    auto bbuf = [&](int i) __attribute__((always_inline)) {
+        return kSplit ? smem + kSA * OpA::kBytes + i * OpB::kBytes : smem + i * kStage + OpA::kBytes;
+    };
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = w / WGN, wn = w % WGN;
     const int m0 = wm * WTM, n0 = wn * WTN;
-    char* const epi = smem + S * kStage + w * Epi8::kBytes;
+    char* const epi = kSplit ? smem : smem + S * kStage + w * Epi8::kBytes;
 
     // The logical tiles this workgroup visits: first, first + stride, ... < end.
     int first, stride, end;
     tile_walk<int>(blockIdx.x, gridDim.x, a.tiles, a.xcd_split != 0, first, stride, end);
     if (first >= end) return;
 
-    StageCursor<TILE, BK, A_K, B_K, RAGGED> cur_ld(a, first, stride, end);
+    StageCursor<TILE, BK, A_K, B_K, RAGGED> cur_ld(a, first, stride, end);   // split ring: A's stages
+    StageCursor<TILE, BK, A_K, B_K, RAGGED> cur_b(a, first, stride, end);    // split ring: B's stages
     LaneOffsets<OpA, OpB> off;
 #pragma unroll
     for (int i = 0; i < OpA::kLoadsPerWave; ++i) off.a[i] = OpA::src_offset(w, i, lane, a.a_ld);
@@ -623,17 +656,39 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
     // 64 tile, whose short products end with S-1 such steps); the two-stage
     // kernels keep one constant wait and a branch-free main loop.
     bool tail = false;                            // a stage past the last one was skipped
+    if constexpr (kSplit) {
+        // B(s) then A(s) for s < S, then A(s) for S <= s < SA: the order of
+        // the main loop, where waiting for a stage's B leaves only the next
+        // A stage in flight.  Stage 0 has landed once the loads after A(0)
+        // are all that is left.
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const bool lv = S == 2 || cur_ld.live();
-        tail |= !lv;
-        ld.setup(smem + s * kStage, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim(), lv);
+        for (int s = 0; s < kSA; ++s) {
+            ld.setup(abuf(s), bbuf(s < S ? s : 0), w, cur_ld.pa, cur_b.pb, cur_ld.a_bytes(), cur_b.b_bytes(), BK,
+                     true);
+            if (s < S) {
 #pragma unroll
-        for (int i = 0; i < L; ++i) ld.issue(i, off);
-        cur_ld.advance();
+                for (int i = LA; i < L; ++i) ld.issue(i, off);
+                cur_b.advance();
+            }
+#pragma unroll
+            for (int i = 0; i < LA; ++i) ld.issue(i, off);
+            cur_ld.advance();
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1) + LA * (kSA - S), 0));
+    } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const bool lv = S == 2 || cur_ld.live();
+            tail |= !lv;
+            ld.setup(abuf(s), bbuf(s), w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim(),
+                     lv);
+#pragma unroll
+            for (int i = 0; i < L; ++i) ld.issue(i, off);
+            cur_ld.advance();
+        }
+        if (tail) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
     }
-    if (tail) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(L * (S - 1), 0));
     asm volatile("s_barrier" ::: "memory");
 
     Frags<TM, TN> f[2];
@@ -645,10 +700,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
 #pragma unroll
         for (int u = 0; u < TM; ++u) f16.a[u] = OpA::frag16(smem, m0 + 16 * u, 0, lane);
 #pragma unroll
-        for (int u = 0; u < TN; ++u) f16.b[0][u] = OpB::frag16(smem + OpA::kBytes, n0 + 16 * u, 0, lane);
+        for (int u = 0; u < TN; ++u) f16.b[0][u] = OpB::frag16(bbuf(0), n0 + 16 * u, 0, lane);
     }
 
-    int cur = 0;                                  // buffer of the current stage
+    int cur = 0;                                  // buffer of the current stage (split ring: its B)
+    int cura = 0;                                 // split ring: A buffer of the current stage
     bool prev_full = true;                        // the previous tile stored every piece
     for (int t = first; t < end; t += stride) {
         typename Mfma<MI>::Acc acc[TM][TN];
@@ -660,13 +716,16 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
         for (int kt = 0; kt < KT; ++kt) {
             char* st = smem + cur * kStage;
             const int nxt = (cur + 1 == S) ? 0 : cur + 1;
+            const int nxta = (cura + 1 == kSA) ? 0 : cura + 1;   // split ring only
+            char* const sta = kSplit ? abuf(cura) : st;
+            char* const stb = kSplit ? bbuf(cur) : st + OpA::kBytes;
             if constexpr (MI == 32) {
 #pragma unroll
                 for (int j = 0; j + 1 < NS; ++j)
                     substep<OpA, OpB, MI, TM, TN, false, RAGGED, NT_A>(acc, f[j & 1], f[(j + 1) & 1], st, j + 1, m0, n0,
                                                                      lane, ld, off);
             } else {
-                substep16<OpA, OpB, TM, TN, 0, false, RAGGED, NT_A>(acc, f16, st, 1, m0, n0, lane, ld, off);
+                substep16<OpA, OpB, TM, TN, 0, false, RAGGED, NT_A>(acc, f16, sta, stb, 1, m0, n0, lane, ld, off);
             }
             // the next stage landed everywhere; nobody reads buffer `cur` any more
             __builtin_amdgcn_sched_barrier(0);
@@ -685,16 +744,27 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             const bool lv = S == 2 || cur_ld.live();
             tail |= !lv;
-            ld.setup(st, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim(), lv);
+            if constexpr (kSplit)
+                ld.setup(sta, stb, w, cur_ld.pa, cur_b.pb, cur_ld.a_bytes(), cur_b.b_bytes(), BK, true);
+            else
+                ld.setup(sta, stb, w, cur_ld.pa, cur_ld.pb, cur_ld.a_bytes(), cur_ld.b_bytes(), cur_ld.klim(), lv);
             if constexpr (MI == 32)
                 substep<OpA, OpB, MI, TM, TN, true, RAGGED, NT_A>(acc, f[(NS - 1) & 1], f[0], smem + nxt * kStage, 0, m0,
                                                                 n0, lane, ld, off);
+            else if constexpr (kSplit)
+                substep16<OpA, OpB, TM, TN, 1, true, RAGGED, NT_A, true>(acc, f16, abuf(nxta), bbuf(nxt), 0, m0, n0,
+                                                                         lane, ld, off);
             else
-                substep16<OpA, OpB, TM, TN, 1, true, RAGGED, NT_A>(acc, f16, smem + nxt * kStage, 0, m0, n0, lane, ld,
-                                                                 off);
+                substep16<OpA, OpB, TM, TN, 1, true, RAGGED, NT_A>(acc, f16, smem + nxt * kStage,
+                                                                 smem + nxt * kStage + OpA::kBytes, 0, m0, n0, lane,
+                                                                 ld, off);
             __builtin_amdgcn_sched_barrier(0);
             cur_ld.advance();
             cur = nxt;
+            if constexpr (kSplit) {
+                cur_b.advance();
+                cura = nxta;
+            }
         }
 
         int bb, tm, tn;
@@ -702,7 +772,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(KArgs a) {
         const int64_t r0 = (int64_t)tm * TILE + m0, c0 = (int64_t)tn * TILE + n0;
         const bool full = !RAGGED || (((int64_t)tm + 1) * TILE <= a.M && ((int64_t)tn + 1) * TILE <= a.N);
         const int64_t m_lim = a.M - r0, n_lim = a.N - c0;   // rows / columns of the wave's block inside C
-        const bool last = t + stride >= end;
+        const bool last = kSplit || t + stride >= end;
         if (last) {
             // Last tile: only loads past the end (two-stage ring: they fetch
             // nothing but still complete into LDS) can be outstanding.  Once
@@ -822,7 +892,8 @@ __device__ __forceinline__ void short64_tile(const KArgs& a, char* smem, int w, 
             off.bkc[p] = (uint32_t)OpB::inner_of(lw, p << OpB::kGroupBit, lane);
         }
         StageLoads<OpA, OpB, RAGGED, NT_A> ld;
-        ld.setup(smem, lw, cur.tile_a(), cur.tile_b(), cur.tile_a_bytes(), cur.tile_b_bytes(), BK, true);
+        ld.setup(smem, smem + OpA::kBytes, lw, cur.tile_a(), cur.tile_b(), cur.tile_a_bytes(), cur.tile_b_bytes(), BK,
+                 true);
         const uint32_t astep = (uint32_t)(cur.a_step * 2), bstep = (uint32_t)(cur.b_step * 2);
         const int ks0 = cur.ks;
         auto issue_stage = [&](int s) __attribute__((always_inline)) {
@@ -935,6 +1006,15 @@ void launch_nt(const GemmDesc& d, const KArgs& k, hipStream_t s) {
         if (short64_fits(d, k)) {
             if (ragged) gemm_short64_kernel<A_K, B_K, OUT_BF16, true, NT_A><<<grid, dim3(512), 0, s>>>(k);
             else gemm_short64_kernel<A_K, B_K, OUT_BF16, false, NT_A><<<grid, dim3(512), 0, s>>>(k);
+            return;
+        }
+    }
+    // Streaming A with one tile-aligned 256x256 tile per workgroup: the split
+    // ring (A three stages deep).
+    if constexpr (TILE == 256 && NT_A) {
+        if (!ragged && d.grid >= d.tiles) {
+            gemm_kernel<TILE, kBK, S, WF::M, WF::N, WF::MI, A_K, B_K, OUT_BF16, false, NT_A, 3>
+                <<<grid, dim3(64 * WF::M * WF::N), 0, s>>>(k);
             return;
         }
     }

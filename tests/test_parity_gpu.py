@@ -754,6 +754,58 @@ def test_rotated_k_random_data_within_tolerance_and_deterministic():
     assert not torch.equal(runs["default"], runs["unrotated"])
 
 
+# ------------------------------------------ deeper A ring (streaming A) --
+# With A streaming (one 256-wide tile column, tile-aligned) and one tile per
+# workgroup, the kernel gives A a ring of three stages and B one of two.  Its
+# MFMA order is the two-stage ring's, which runs when A's loads are ordinary
+# (AS_FLAG_NO_NT_A).
+
+_T256 = asl.AS_FLAG_TILE_256
+DEEP_A = [  # (M, N, K, flags)
+    (65536, 256, 1024, 0),                               # 256 tiles: the resident grid, one tile each
+    (8192, 256, 4096, _T256 | asl.AS_FLAG_NO_SPLIT_K),   # 32 tiles of 64 stages
+    (4096, 256, 8192, _T256),                            # 16 tiles: split into K chunks, each on the deep ring
+    (2048, 256, 64, _T256 | asl.AS_FLAG_NO_SPLIT_K),     # one stage: every later request fetches nothing
+]
+
+
+@pytest.mark.parametrize("M,N,K,flags", DEEP_A)
+@pytest.mark.parametrize("a_k", [True, False])
+def test_deep_a_ring_bitwise_equals_two_stage_ring(M, N, K, flags, a_k):
+    _say("deep A ring M=%d N=%d K=%d flags=0x%x a_k=%s" % (M, N, K, flags, a_k))
+    A = draw((1, M, K) if a_k else (1, K, M), "normal", 0, 1, 6100 + K)
+    B = draw((1, K, N), "normal", 0, 1, 6200 + K)
+    sa = (K, 1, M * K) if a_k else (1, M, M * K)
+    sb = (N, 1, K * N)
+    p = asl.gemm_create(M, N, K, 1, sa, sb, (N, 1, M * N), flags=flags)
+    tile, _, _, tiles, grid = asl.gemm_plan_info(p)
+    splits = asl.gemm_plan_split_k(p)[0]
+    asl.gemm_destroy(p)
+    assert tile == 256 and (splits == 1 or K // splits % 64 == 0)
+    assert grid >= tiles * splits        # one tile (or K chunk of one) per workgroup
+    deep = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, flags)
+    two = _run_gemm(A, B, M, N, K, 1, sa, sb, torch.float32, flags | asl.AS_FLAG_NO_NT_A)
+    assert torch.equal(deep.view(torch.int32), two.view(torch.int32))
+    assert torch.isfinite(deep).all()
+
+
+DEEP_A_INT = [  # (M, N, K, a_k, b_k)
+    (2048, 256, 512, True, False),
+    (1024, 256, 64, False, False),
+    (1536, 256, 1024, True, True),
+    (4096, 256, 4096, False, True),               # split into K chunks
+]
+
+
+@pytest.mark.parametrize("M,N,K,a_k,b_k", DEEP_A_INT)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_deep_a_ring_integer_bit_exact(M, N, K, a_k, b_k, out):
+    """Integer data through the deep A ring (padded NaN storage, sentinel C):
+    the oracle's result bit for bit, nothing stored outside C."""
+    _say("deep A ring integer M=%d N=%d K=%d a_k=%s b_k=%s out=%s" % (M, N, K, a_k, b_k, out))
+    _ragged(M, N, K, 1, a_k, b_k, out, _T256, 6300 + M + K)
+
+
 # --------------------------------------------------- randomized shape sweep --
 
 def _random_cases(n, seed):
