@@ -766,6 +766,8 @@ DEEP_A = [  # (M, N, K, flags)
     (8192, 256, 4096, _T256 | asl.AS_FLAG_NO_SPLIT_K),   # 32 tiles of 64 stages
     (4096, 256, 8192, _T256),                            # 16 tiles: split into K chunks, each on the deep ring
     (2048, 256, 64, _T256 | asl.AS_FLAG_NO_SPLIT_K),     # one stage: every later request fetches nothing
+    (16384, 256, 2048, _T256 | asl.AS_FLAG_NO_ROTATE_K),  # every tile walks K from stage 0
+    (1024, 256, 192, _T256 | asl.AS_FLAG_NO_SPLIT_K),    # three stages: the ring's depth exactly
 ]
 
 
