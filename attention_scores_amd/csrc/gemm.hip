@@ -16,8 +16,9 @@
 //
 // Data path of one K step (BK = 64):
 //   global -> LDS   buffer_load_dwordx4 ... lds (no registers in between),
-//                   double-buffered; the next step's tile is requested while
-//                   the current one is multiplied.  LDS keeps each operand in
+//                   double-buffered (A triple-buffered when it streams and
+//                   every workgroup has one tile); the next step's tile is
+//                   requested while the current one is multiplied.  LDS keeps each operand in
 //                   its global orientation, 16-byte chunks XOR-swizzled so
 //                   that the fragment reads below are bank-conflict free
 //                   (one swizzle per MFMA shape, tile.hpp).
