@@ -18,10 +18,10 @@
 //   global -> LDS   buffer_load_dwordx4 ... lds (no registers in between),
 //                   double-buffered (A triple-buffered when it streams and
 //                   every workgroup has one tile); the next step's tile is
-//                   requested while the current one is multiplied.  LDS keeps each operand in
-//                   its global orientation, 16-byte chunks XOR-swizzled so
-//                   that the fragment reads below are bank-conflict free
-//                   (one swizzle per MFMA shape, tile.hpp).
+//                   requested while the current one is multiplied.  LDS
+//                   keeps each operand in its global orientation, 16-byte
+//                   chunks XOR-swizzled so that the fragment reads below are
+//                   bank-conflict free (one swizzle per MFMA shape, tile.hpp).
 //   LDS -> VGPR     K-contiguous operands: ds_read_b128 (8 k values of one
 //                   row per lane); MN-contiguous operands: two
 //                   ds_read_b64_tr_b16, which transpose 4x16 blocks on the way
