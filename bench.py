@@ -256,8 +256,8 @@ def time_workload(w, steps, warmup, flags=0):
     return wall_ms, ev_ms, info, steps, warmup
 
 
-# The oracle's threads: the GPU machine gives one GPU's job a 16-core share of its
-# host, whatever the machine reports in all (both counts are recorded).
+# The oracle's threads: a one-GPU job gets a 16-core share of its host,
+# whatever the machine reports in all (both counts are recorded).
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 

@@ -170,7 +170,7 @@ def test_padded_output_leaves_the_rest_untouched():
     assert np.all(np.isnan(raw[mask]))
 
 
-# Oracle threads: the GPU machine's share of its host is 16 cores.
+# Oracle threads: a one-GPU job's share of its host is 16 cores.
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 

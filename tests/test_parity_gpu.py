@@ -34,7 +34,7 @@ def _say(msg):
     print("[case] " + msg, flush=True)
 
 
-# Oracle threads: the GPU machine's share of its host is 16 cores, whatever the
+# Oracle threads: a one-GPU job's share of its host is 16 cores, whatever the
 # machine reports in all.
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
